@@ -1,0 +1,32 @@
+"""Closed-form storage cost of the encoded cache (test infrastructure only).
+
+QVG explainer, "Sommario tecnico" 4 and the title: the method reports the
+compression of the KV cache at 2 bits per code.  With the readings of this
+oracle (per-group fp16 scale and zero per stage, one cluster id per token,
+one codebook snapshot per head per encode call) the stored bits per cached
+element are
+
+    S*b                         codes
+  + S*2*16/G                    fp16 (sigma, z) per group per stage
+  + 8*id_bytes/d                one id per token, shared by its d channels
+  + 8*cb_bytes*C/n_call         the call's codebook, amortised over its tokens
+
+with id_bytes = 1 for C <= 256, else 2, and cb_bytes the cache dtype's size.
+"""
+from fractions import Fraction
+
+
+def bits_per_element(n_stages, bits, group, head_dim, n_clusters, cb_bytes, n_call,
+                     with_ids=True):
+    """Exact bits per element as a Fraction."""
+    id_bytes = 1 if n_clusters <= 256 else 2
+    total = Fraction(n_stages * bits) + Fraction(n_stages * 32, group)
+    if with_ids:
+        total += Fraction(8 * id_bytes, head_dim)
+        total += Fraction(8 * cb_bytes * n_clusters, n_call)
+    return total
+
+
+def compression_ratio(input_bytes, *args, **kw):
+    """Ratio of the input's bits per element to the stored bits per element."""
+    return Fraction(8 * input_bytes) / bits_per_element(*args, **kw)
