@@ -1,0 +1,163 @@
+"""Benchmark of the hot path on one MI355X: encode + reconstruct + fused attention.
+
+One step = one pass of the whole path over one Wan2.1-1.3B-shaped layer
+(K and V bf16 [12 heads, 32760 tokens, d=128], C=256 clusters, 5 k-means
+iterations, 2-stage INT2 with group 32):
+  qkv_rewind to 0 (state reset, a one-thread kernel), qkv_encode_chunk of all
+  32760 tokens (k-means + PRQ + packing, K and V), qkv_reconstruct of K and V
+  (bf16 out), qkv_attend of a 4680-token bf16 query chunk over the packed
+  cache.
+Inputs are seeded synthetic tensors already resident in HBM.  Each library
+call is also bracketed by HIP events on the stream it is launched on.
+
+Prints ONE JSON line (see the repository's design notes for every field).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def cpu_baseline(cfgs, k_dev, v_dev, q_dev):
+    """The oracle, as it stands, on a bounded sample: head 0 of K and V (1/12 of
+    the layer): full k-means + PRQ encode, reconstruction, and attention of all
+    4680 queries of that head.  Scaled to the same GB/s unit as the GPU line."""
+    import numpy as np
+    import torch
+    from oracle import attend as o_attend
+    from oracle import stream as o_stream
+
+    threads = torch.get_num_threads()
+    k = k_dev[:1].float().cpu().numpy()
+    v = v_dev[:1].float().cpu().numpy()
+    q = q_dev[:1].float().cpu().numpy()
+    t = time.perf_counter()
+    xs = []
+    for x in (k, v):
+        s = o_stream.Stream(1, cfgs.head_dim, cfgs.n_clusters, cfgs.iters, cfgs.n_stages, cfgs.bits,
+                            cfgs.group, "bf16")
+        s.encode(x)
+        xs.append(s.xhat())
+    o_attend.attend(q, xs[0], xs[1])
+    dt = time.perf_counter() - t
+    sample_bytes = 2 * k.shape[1] * k.shape[2] * 2     # bf16 K+V of one head
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": round(sample_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": cores,
+            "blas_threads": threads, "kind": "oracle", "seconds": round(dt, 2),
+            "sample": "head 0 of K and V (1/12 of the layer): full encode (5 k-means iterations + "
+                      "2 PRQ stages), reconstruction, attention of all 4680 queries of that head"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; the path shards by heads/layers "
+                          "with no exchange (see the design notes), but no multi-GPU run exists"}))
+        sys.exit(2)
+    import torch
+    import kv_cache_quantization_head_amd as qkv
+    import synth
+
+    dev = torch.device("cuda:0")
+    cfgs = synth.WAN_LAYER
+    H, T, d, Tq = cfgs.n_heads, cfgs.tokens, cfgs.head_dim, cfgs.q_tokens
+    cfg = qkv.config(1, H, d, cfgs.n_clusters, cfgs.n_stages, cfgs.bits, cfgs.group,
+                     kmeans_iters=cfgs.iters, max_tokens=T, max_chunks=1, kv_dtype=qkv.QKV_BF16,
+                     max_query_tokens=Tq)
+    codec = qkv.Codec(cfg, device=dev)
+    k = synth.kv_tokens(cfgs, 0, 0, 0, T, device=dev)
+    v = synth.kv_tokens(cfgs, 0, 1, 0, T, device=dev)
+    q = synth.queries(cfgs, 0, Tq, device=dev)
+    rec = torch.empty((2, 1, H, T, d), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((H, Tq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((H, Tq), dtype=torch.float32, device=dev)
+
+    ev = {name: [] for name in ("encode", "reconstruct", "attend")}
+
+    def step(record):
+        codec.rewind(0, 1, 0)
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        if record: marks[0].record()
+        codec.encode_chunk(k, v)
+        if record: marks[1].record()
+        codec.reconstruct(0, 1, 0, 0, T, out=rec[0])
+        codec.reconstruct(0, 1, 1, 0, T, out=rec[1])
+        if record: marks[2].record()
+        codec.attend(0, q, out=out, lse=lse)
+        if record:
+            marks[3].record()
+            ev["encode"].append((marks[0], marks[1]))
+            ev["reconstruct"].append((marks[1], marks[2]))
+            ev["attend"].append((marks[2], marks[3]))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"# timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    def avg_ms(name):
+        xs = [a.elapsed_time(b) for a, b in ev[name]]
+        return sum(xs) / len(xs)
+
+    ms = {n: avg_ms(n) for n in ev}
+    ms_step = wall * 1e3 / args.steps
+    n_el = 2 * H * T * d                                   # K + V elements
+    kv_bytes = n_el * 2
+    S, b, G = cfgs.n_stages, cfgs.bits, cfgs.group
+    packed_bytes = n_el * (S * b / 8 + S * 4 / G) + 2 * H * T  # codes + meta + ids
+    att_flops = 4.0 * H * Tq * T * d
+    att_tflops = att_flops / (ms["attend"] * 1e-3) / 1e12
+    codebook_bytes = 2 * H * cfgs.n_clusters * d * 2
+    recon_gbs = (packed_bytes + codebook_bytes + n_el * 2) / (ms["reconstruct"] * 1e-3) / 1e9
+    encode_gbs = (kv_bytes + packed_bytes) / (ms["encode"] * 1e-3) / 1e9
+    result = {
+        "metric": "KV quantize+pack GB/s and fused dequant-attention tokens/s; % of HBM/MFMA peak",
+        "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 3),
+        "unit": "GB/s (bf16 K+V cache bytes through encode + reconstruct + attend per step)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded prototype/drift/outlier generator)",
+        "config": {"workload": "wan_layer: K,V bf16 [12, 32760, 128], C=256, 5 iters, 2-stage INT2 "
+                               "G=32; 4680 bf16 queries", "heads": H, "tokens": T, "head_dim": d,
+                   "clusters": cfgs.n_clusters, "stages": S, "bits": b, "group": G, "q_tokens": Tq},
+        "calls_ms": {n: round(x, 4) for n, x in ms.items()},
+        "encode_GBps": round(encode_gbs, 2),
+        "reconstruct_GBps": round(recon_gbs, 2),
+        "attend_q_tokens_per_s": round(Tq / (ms["attend"] * 1e-3), 1),
+        "attend_TFLOPs": round(att_tflops, 2),
+        "roofline": {"kernel": "qkv_attend (k_attend + split merge)", "bound": "mfma",
+                     "achieved": round(att_tflops, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(att_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfgs, k, v, q)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,248 @@
+// C-ABI entry points of the qkv library (see include/qkv.h).  Each call
+// validates its arguments on the host (plan.cpp), then enqueues the kernels
+// of kernels.hip on the caller's stream and updates the host bookkeeping.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <new>
+#include <string>
+
+#include "device.h"
+#include "launch.h"
+#include "plan.h"
+
+using namespace qkv;
+
+static int hip_status(qkv_ctx *ctx) {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) return QKV_OK;
+  ctx->last_hip_error = int(e);
+  ctx->last_error = std::string("HIP error: ") + hipGetErrorString(e);
+  return QKV_E_HIP;
+}
+
+static uint8_t *scratch(qkv_ctx *ctx, uint64_t off) { return ctx->arena + ctx->plan.scratch_off + off; }
+
+extern "C" int qkv_init(const qkv_config *cfg, void *d_arena, size_t arena_bytes,
+                        const void *d_predictor, qkv_ctx **out) {
+  if (!out) return QKV_E_INVAL;
+  *out = nullptr;
+  Plan p;
+  const int rc = make_plan(cfg, &p);
+  if (rc != QKV_OK) return rc;
+  if (!d_arena) return QKV_E_INVAL;
+  if (reinterpret_cast<uintptr_t>(d_arena) % kAlign) return QKV_E_ARENA;
+  if (arena_bytes < p.total_bytes) return QKV_E_ARENA;
+  if (p.cfg.xlayer && !d_predictor) return QKV_E_INVAL;
+  qkv_ctx *ctx = new (std::nothrow) qkv_ctx;
+  if (!ctx) return QKV_E_INVAL;
+  ctx->plan = p;
+  ctx->arena = static_cast<uint8_t *>(d_arena);
+  ctx->arena_bytes = arena_bytes;
+  ctx->predictor = static_cast<const uint8_t *>(d_predictor);
+  ctx->layers.resize(size_t(p.cfg.n_layers));
+  *out = ctx;
+  return QKV_OK;
+}
+
+// SAS + PRQ for the 2*n_layers streams of `a` (k-means loop, then codes).
+static void enqueue_sas(const EncodeArgs &a, int streams, int iters, hipStream_t st) {
+  launch_header(a, streams, st);
+  launch_init(a, streams, st);
+  for (int it = 0; it < iters; ++it) {
+    launch_assign(a, streams, st);
+    launch_update(a, streams, st);
+  }
+  launch_assign(a, streams, st);
+  launch_quantize(a, streams, st);
+}
+
+extern "C" int qkv_encode_chunk(qkv_ctx *ctx, int32_t layer0, int32_t n_layers, const void *d_k,
+                                const void *d_v, int64_t n, void *stream) {
+  const int rc = check_encode(ctx, layer0, n_layers, d_k, d_v, n);
+  if (rc != QKV_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Plan &p = ctx->plan;
+  const qkv_config &c = p.cfg;
+  const int64_t t0 = ctx->layers[layer0].n_tokens;
+  const int slot = int(ctx->layers[layer0].starts.size());
+
+  EncodeArgs a{};
+  a.L = dev_layout(p);
+  a.arena = ctx->arena;
+  a.n = int32_t(n);
+  a.t0 = int32_t(t0);
+  a.slot = slot;
+  a.prev_slot = slot - 1;
+  const uint64_t layer_bytes = uint64_t(c.n_heads) * uint64_t(n) * c.head_dim * p.kv_elem_bytes;
+  const uint8_t *kin = static_cast<const uint8_t *>(d_k);
+  const uint8_t *vin = static_cast<const uint8_t *>(d_v);
+
+  (void)hipGetLastError();
+  if (!c.xlayer) {
+    a.layer0 = layer0;
+    a.k_in = kin;
+    a.v_in = vin;
+    enqueue_sas(a, 2 * n_layers, c.kmeans_iters, st);
+  } else {
+    const uint64_t HD = uint64_t(c.n_heads) * c.head_dim;
+    const uint64_t kv_stride = HD * c.head_dim + 2 * HD * uint64_t(c.xlayer_rank);
+    uint16_t *chain = reinterpret_cast<uint16_t *>(scratch(ctx, p.xl_chain_off));
+    float *pred = reinterpret_cast<float *>(scratch(ctx, p.xl_pred_off));
+    float *proj = reinterpret_cast<float *>(scratch(ctx, p.xl_proj_off));
+    for (int l = layer0; l < layer0 + n_layers; ++l) {
+      a.layer0 = l;
+      a.k_in = kin + uint64_t(l - layer0) * layer_bytes;
+      a.v_in = vin + uint64_t(l - layer0) * layer_bytes;
+      a.chain = chain;
+      if (l == 0) {
+        a.pred = nullptr;
+        enqueue_sas(a, 2, c.kmeans_iters, st);
+      } else {
+        XlArgs x{};
+        x.H = c.n_heads; x.D = c.head_dim; x.r = c.xlayer_rank; x.n = int32_t(n);
+        x.chain = chain;
+        x.weights = reinterpret_cast<const uint16_t *>(ctx->predictor) + uint64_t(l - 1) * 2 * kv_stride;
+        x.kv_weight_stride = kv_stride;
+        x.proj = proj;
+        x.pred = pred;
+        launch_xl_predict(x, 0, 2, st);
+        a.pred = pred;
+        launch_header(a, 2, st);
+        launch_quantize(a, 2, st);
+      }
+    }
+  }
+  const int hs = hip_status(ctx);
+  if (hs != QKV_OK) return hs;
+  for (int l = layer0; l < layer0 + n_layers; ++l) {
+    ctx->layers[l].starts.push_back(t0);
+    ctx->layers[l].n_tokens = t0 + n;
+  }
+  if (c.xlayer) {
+    ctx->chain_layer = layer0 + n_layers - 1;
+    ctx->chain_t0 = t0;
+    ctx->chain_n = n;
+  }
+  return QKV_OK;
+}
+
+extern "C" int qkv_attend(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t n_q, int32_t q_dtype,
+                          void *d_out, int32_t out_dtype, float *d_lse, void *stream) {
+  const int rc = check_attend(ctx, layer, d_q, n_q, q_dtype, d_out, out_dtype);
+  if (rc != QKV_OK) return rc;
+  if (n_q == 0) return QKV_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Plan &p = ctx->plan;
+  const int64_t n_keys = ctx->layers[layer].n_tokens;
+  int splits = attention_splits(p, n_keys, n_q);
+  int64_t split_len = (n_keys + splits - 1) / splits;
+  split_len = (split_len + 63) / 64 * 64;
+  splits = int((n_keys + split_len - 1) / split_len);
+
+  AttnArgs a{};
+  a.L = dev_layout(p);
+  a.stream_k = ctx->arena + stream_offset(p, layer, 0);
+  a.stream_v = ctx->arena + stream_offset(p, layer, 1);
+  a.q = d_q;
+  a.q_bf16 = q_dtype == QKV_BF16;
+  a.n_q = int32_t(n_q);
+  a.n_keys = int32_t(n_keys);
+  a.split_len = int32_t(split_len);
+  a.n_splits = splits;
+  a.out = d_out;
+  a.out_bf16 = out_dtype == QKV_BF16;
+  a.lse = d_lse;
+  a.part_o = reinterpret_cast<float *>(scratch(ctx, p.attn_part_o_off));
+  a.part_lse = reinterpret_cast<float *>(scratch(ctx, p.attn_part_lse_off));
+  (void)hipGetLastError();
+  launch_attend(a, st);
+  ctx->chain_layer = -1;  // scratch reused
+  return hip_status(ctx);
+}
+
+extern "C" int qkv_reconstruct(qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int32_t kv, int64_t t0,
+                               int64_t t1, void *d_out, int32_t out_dtype, void *stream) {
+  const int rc = check_reconstruct(ctx, layer0, n_layers, kv, t0, t1, d_out, out_dtype);
+  if (rc != QKV_OK) return rc;
+  if (t1 == t0) return QKV_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Plan &p = ctx->plan;
+  const qkv_config &c = p.cfg;
+  ReconArgs r{};
+  r.L = dev_layout(p);
+  r.arena = ctx->arena;
+  r.kv = kv;
+  r.out_bf16 = out_dtype == QKV_BF16;
+  (void)hipGetLastError();
+  if (!c.xlayer) {
+    r.layer0 = layer0;
+    r.t0 = int32_t(t0);
+    r.n = int32_t(t1 - t0);
+    r.out = d_out;
+    launch_reconstruct(r, n_layers, t1 - t0, 0, st);
+    return hip_status(ctx);
+  }
+  // cross-layer: layer l >= 1 needs the bf16 reconstruction of layer l-1
+  const int last = layer0 + n_layers - 1;
+  const int64_t M = c.max_chunk_tokens;
+  const uint64_t HD = uint64_t(c.n_heads) * c.head_dim;
+  const uint64_t kv_stride = HD * c.head_dim + 2 * HD * uint64_t(c.xlayer_rank);
+  const uint64_t out_eb = out_dtype == QKV_BF16 ? 2 : 4;
+  uint16_t *chain = reinterpret_cast<uint16_t *>(scratch(ctx, p.xl_chain_off));
+  float *pred = reinterpret_cast<float *>(scratch(ctx, p.xl_pred_off));
+  float *proj = reinterpret_cast<float *>(scratch(ctx, p.xl_proj_off));
+  for (int64_t ts = t0; ts < t1; ts += M) {
+    const int64_t ns = std::min(t1, ts + M) - ts;
+    for (int l = 0; l <= last; ++l) {
+      r.layer0 = l;
+      r.t0 = int32_t(ts);
+      r.n = int32_t(ns);
+      r.out = l >= layer0 ? static_cast<uint8_t *>(d_out) + uint64_t(l - layer0) * HD * uint64_t(t1 - t0) * out_eb
+                          : nullptr;
+      r.pred = l >= 1 ? pred + uint64_t(kv) * HD * ns : nullptr;
+      r.chain = l < last ? chain + uint64_t(kv) * HD * ns : nullptr;
+      launch_reconstruct(r, 1, t1 - t0, int32_t(ts - t0), st);
+      if (l < last) {
+        XlArgs x{};
+        x.H = c.n_heads; x.D = c.head_dim; x.r = c.xlayer_rank; x.n = int32_t(ns);
+        x.chain = chain;
+        x.weights = reinterpret_cast<const uint16_t *>(ctx->predictor) + uint64_t(l) * 2 * kv_stride;
+        x.kv_weight_stride = kv_stride;
+        x.proj = proj;
+        x.pred = pred;
+        launch_xl_predict(x, kv, 1, st);
+      }
+    }
+  }
+  ctx->chain_layer = -1;
+  return hip_status(ctx);
+}
+
+extern "C" int qkv_rewind(qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int64_t n_tokens, void *stream) {
+  const int rc = check_rewind(ctx, layer0, n_layers, n_tokens);
+  if (rc != QKV_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const DevLayout L = dev_layout(ctx->plan);
+  bool launched = false;
+  for (int l = layer0; l < layer0 + n_layers; ++l) {
+    const LayerState &ls = ctx->layers[l];
+    if (n_tokens == ls.n_tokens) continue;
+    int kept = 0;
+    while (kept < int(ls.starts.size()) && ls.starts[kept] < n_tokens) ++kept;
+    if (!launched) (void)hipGetLastError();
+    launched = true;
+    launch_set_header(ctx->arena, L, l, 1, kept, int(n_tokens), st);
+  }
+  if (launched) {
+    const int hs = hip_status(ctx);
+    if (hs != QKV_OK) return hs;
+  }
+  for (int l = layer0; l < layer0 + n_layers; ++l) {
+    LayerState &ls = ctx->layers[l];
+    while (!ls.starts.empty() && ls.starts.back() >= n_tokens) ls.starts.pop_back();
+    ls.n_tokens = n_tokens;
+  }
+  ctx->chain_layer = -1;
+  return QKV_OK;
+}

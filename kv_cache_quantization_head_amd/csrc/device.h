@@ -1,0 +1,91 @@
+// Shared device-side definitions of the qkv kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace qkv {
+
+// Layout of one (layer, K|V) stream passed by value to kernels.
+struct DevLayout {
+  uint64_t stream_bytes, header_off;
+  uint64_t codes_off, codes_stage, codes_head, codes_token;
+  uint64_t meta_off, meta_stage, meta_head, meta_token;
+  uint64_t ids_off, ids_head;
+  uint64_t cb_off, cb_chunk, cb_head, cb_row;
+  uint64_t cn_off, cn_chunk, cn_head;
+  int32_t H, D, C, S, bits, G, id_bytes, kv_bf16;
+};
+
+inline DevLayout dev_layout(const Plan &p) {
+  DevLayout d{};
+  const StreamLayout &s = p.s;
+  d.stream_bytes = s.bytes;
+  d.header_off = s.header_off;
+  d.codes_off = s.codes_off; d.codes_stage = s.codes_stage; d.codes_head = s.codes_head;
+  d.codes_token = s.codes_token;
+  d.meta_off = s.meta_off; d.meta_stage = s.meta_stage; d.meta_head = s.meta_head;
+  d.meta_token = s.meta_token;
+  d.ids_off = s.ids_off; d.ids_head = s.ids_head;
+  d.cb_off = s.cb_off; d.cb_chunk = s.cb_chunk; d.cb_head = s.cb_head; d.cb_row = s.cb_row;
+  d.cn_off = s.cn_off; d.cn_chunk = s.cn_chunk; d.cn_head = s.cn_head;
+  d.H = p.cfg.n_heads; d.D = p.cfg.head_dim; d.C = p.cfg.n_clusters; d.S = p.cfg.n_stages;
+  d.bits = p.cfg.bits; d.G = p.cfg.group_size; d.id_bytes = int32_t(s.id_bytes);
+  d.kv_bf16 = p.cfg.kv_dtype == QKV_BF16;
+  return d;
+}
+
+// Arguments of the encode kernels.  Streams of one launch are the 2*n_layers
+// (layer, K|V) pairs starting at layer0 (blockIdx.z = 2*layer_rel + kv) unless
+// `single_kv_layer` >= 0 (cross-layer mode: one layer, blockIdx.z = kv).
+struct EncodeArgs {
+  DevLayout L;
+  uint8_t *arena;
+  const uint8_t *k_in, *v_in;   // [n_layers][H][n][D] cache dtype
+  int32_t layer0;
+  int32_t n;                    // tokens of this call
+  int32_t t0;                   // first token of the chunk in every stream
+  int32_t slot;                 // snapshot slot of this chunk
+  int32_t prev_slot;            // warm-start slot, -1 for strided init
+  // cross-layer coding: base = pred instead of the centroid, reconstruction
+  // written to chain (both [2][H][n][D], f32 / bf16)
+  const float *pred;
+  uint16_t *chain;
+};
+
+struct ReconArgs {
+  DevLayout L;
+  const uint8_t *arena;
+  int32_t layer0, kv;
+  int32_t t0, n;                // tokens [t0, t0+n) of each layer
+  void *out;                    // [n_layers][H][n][D], or null
+  int32_t out_bf16;
+  const float *pred;            // cross-layer base [H][n][D] for this kv, or null
+  uint16_t *chain;              // bf16 copy of the output [H][n][D], or null
+};
+
+struct AttnArgs {
+  DevLayout L;
+  const uint8_t *stream_k, *stream_v;   // stream bases of the layer
+  const void *q;                        // [H][n_q][D]
+  int32_t q_bf16;
+  int32_t n_q, n_keys, split_len, n_splits;
+  void *out;                            // final [H][n_q][D] when n_splits == 1
+  int32_t out_bf16;
+  float *lse;                           // final [H][n_q] or null
+  float *part_o;                        // [splits][H][n_q][D] when n_splits > 1
+  float *part_lse;                      // [splits][H][n_q]
+};
+
+struct XlArgs {
+  int32_t H, D, r, n;
+  const uint16_t *chain;       // [2][H][n][D] bf16 reconstruction of the source layer
+  const uint16_t *weights;     // predictor block of the source layer: per kv B, U, V
+  uint64_t kv_weight_stride;   // elements between the K and V blocks
+  float *proj;                 // [2][n][r] bf16-rounded projections (as f32)
+  float *pred;                 // [2][H][n][D]
+};
+
+}  // namespace qkv

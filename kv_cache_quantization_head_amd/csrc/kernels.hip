@@ -1,0 +1,872 @@
+// HIP kernels of the qkv library for gfx950 (CDNA4, wave64).
+//
+//   k_header      chunk table of every stream touched by an encode call
+//   k_init        initial codebook of a call: previous snapshot (centroid
+//                 caching) or strided tokens
+//   k_assign      nearest centroid per token: fp32 scores screen the
+//                 candidates under a proven error bound; near ties are decided
+//                 by the exact fp64 distance, channels summed in order
+//   k_update      fp64 member sums in token order -> mean -> one rounding
+//   k_quantize    centroid (or prediction) subtraction + S PRQ stages + packing
+//   k_reconstruct unpack + dequantize + add base, fp32 or bf16 out
+//   k_attend      split-KV attention reading the packed cache: tiles are
+//                 rebuilt in bf16 in LDS and fed to bf16 MFMA (16x16x32)
+//   k_attend_merge  LSE merge of the split partials
+//   k_xl_project, k_xl_predict  cross-layer block-diagonal + low-rank
+//                 prediction in fp64 with a fixed summation order
+//
+// Every elementwise codec operation is IEEE fp32 with no contraction (the
+// library is compiled with -ffp-contract=off; fused multiply-adds are
+// written as fmaf where the definition has one).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "device.h"
+#include "launch.h"
+
+namespace qkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  __bf16 h = (__bf16)f;  // round to nearest even (v_cvt_pk_bf16_f32)
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// Round an fp64 value once to bf16 (nearest even): scale the significand to
+// 8 bits by a power of two, round to an integer, scale back; all exact in fp64.
+__device__ __forceinline__ uint16_t f64_to_bf16_bits(double v) {
+  if (v == 0.0) return signbit(v) ? 0x8000u : 0u;
+  int e = ilogb(v);
+  e = e < -126 ? -126 : e;
+  const double r = ldexp(rint(ldexp(v, 7 - e)), e - 7);
+  const float f = (float)r;  // exact, or overflow to infinity
+  return (uint16_t)(__float_as_uint(f) >> 16);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load_elem(const uint8_t *base, uint64_t idx) {
+  if constexpr (BF16) return bf16_to_f32(((const uint16_t *)base)[idx]);
+  else return ((const float *)base)[idx];
+}
+
+__device__ __forceinline__ uint8_t *stream_ptr(uint8_t *arena, const DevLayout &L, int layer, int kv) {
+  return arena + (uint64_t(layer) * 2 + uint64_t(kv)) * L.stream_bytes;
+}
+__device__ __forceinline__ const uint8_t *stream_ptr(const uint8_t *arena, const DevLayout &L,
+                                                     int layer, int kv) {
+  return arena + (uint64_t(layer) * 2 + uint64_t(kv)) * L.stream_bytes;
+}
+
+__device__ __forceinline__ int load_id(const uint8_t *ids, int id_bytes, int64_t t) {
+  return id_bytes == 1 ? int(ids[t]) : int(((const uint16_t *)ids)[t]);
+}
+
+// Chunk (snapshot slot) of token t: the last chunk whose first token is <= t.
+__device__ __forceinline__ int chunk_of(const StreamHeader *hdr, int t) {
+  int lo = 0, hi = hdr->n_chunks - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (hdr->start[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------- encode kernels
+
+// blockIdx.x = stream of the call (2*layer_rel + kv)
+__global__ void k_header(EncodeArgs a) {
+  if (threadIdx.x != 0) return;
+  const int z = blockIdx.x;
+  uint8_t *st = stream_ptr(a.arena, a.L, a.layer0 + (z >> 1), z & 1);
+  StreamHeader *hdr = (StreamHeader *)(st + a.L.header_off);
+  hdr->start[a.slot] = a.t0;
+  hdr->start[a.slot + 1] = a.t0 + a.n;
+  hdr->n_chunks = a.slot + 1;
+  hdr->n_tokens = a.t0 + a.n;
+}
+
+// blockIdx.x = head, blockIdx.y = stream of the call
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_init(EncodeArgs a) {
+  constexpr int EB = BF16 ? 2 : 4;
+  const DevLayout &L = a.L;
+  const int h = blockIdx.x, z = blockIdx.y, lrel = z >> 1, kv = z & 1;
+  uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, kv);
+  const uint8_t *x = (kv ? a.v_in : a.k_in) + (uint64_t(lrel) * L.H + h) * uint64_t(a.n) * D * EB;
+  uint8_t *cb = st + L.cb_off + uint64_t(a.slot) * L.cb_chunk + uint64_t(h) * L.cb_head;
+  float *cn = (float *)(st + L.cn_off + uint64_t(a.slot) * L.cn_chunk + uint64_t(h) * L.cn_head);
+  if (a.prev_slot >= 0) {
+    const uint32_t *src =
+        (const uint32_t *)(st + L.cb_off + uint64_t(a.prev_slot) * L.cb_chunk + uint64_t(h) * L.cb_head);
+    const float *pcn =
+        (const float *)(st + L.cn_off + uint64_t(a.prev_slot) * L.cn_chunk + uint64_t(h) * L.cn_head);
+    uint32_t *dst = (uint32_t *)cb;
+    const int words = L.C * D * EB / 4;
+    for (int i = threadIdx.x; i < words; i += blockDim.x) dst[i] = src[i];
+    for (int k = threadIdx.x; k < L.C; k += blockDim.x) cn[k] = pcn[k];
+    return;
+  }
+  for (int k = threadIdx.x; k < L.C; k += blockDim.x) {
+    const int64_t row = (int64_t(k) * a.n) / L.C;
+    const uint8_t *src = x + uint64_t(row) * D * EB;
+    uint8_t *dst = cb + uint64_t(k) * D * EB;
+    double acc = 0.0;
+    for (int j = 0; j < D; ++j) {
+      float v;
+      if constexpr (BF16) {
+        const uint16_t b = ((const uint16_t *)src)[j];
+        ((uint16_t *)dst)[j] = b;
+        v = bf16_to_f32(b);
+      } else {
+        v = ((const float *)src)[j];
+        ((float *)dst)[j] = v;
+      }
+      acc = acc + double(v) * double(v);
+    }
+    cn[k] = float(acc);
+  }
+}
+
+// One thread per token.  blockIdx.x = token tile of 256, y = head, z = stream.
+//
+// Screening: s_k = ||c_k||^2 - 2 x.c_k in fp32 (FMA chain over D channels).
+// Its error is below (D+4) 2^-24 (||x||^2 + ||c_k||^2) (dot-product bound
+// gamma_D sum|x_j c_j| <= gamma_D (||x||^2+||c||^2)/2, doubled, plus the
+// rounding of ||c||^2 and of the subtraction).  E below doubles that again.
+// If the two best scores differ by more than 2E, the best one is the exact
+// minimiser of the distance with a gap of more than E, far above fp64
+// rounding; otherwise the whole wave recomputes D(t, k) for every k in fp64,
+// channel by channel, and takes the lowest index among equal minima.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_assign(EncodeArgs a) {
+  constexpr int EB = BF16 ? 2 : 4;
+  constexpr int TK = 64;
+  __shared__ float cs[TK][D];
+  __shared__ float cns[TK];
+  const DevLayout &L = a.L;
+  const int h = blockIdx.y, z = blockIdx.z, lrel = z >> 1, kv = z & 1;
+  uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, kv);
+  const uint8_t *x = (kv ? a.v_in : a.k_in) + (uint64_t(lrel) * L.H + h) * uint64_t(a.n) * D * EB;
+  const uint8_t *cb = st + L.cb_off + uint64_t(a.slot) * L.cb_chunk + uint64_t(h) * L.cb_head;
+  const float *cn = (const float *)(st + L.cn_off + uint64_t(a.slot) * L.cn_chunk + uint64_t(h) * L.cn_head);
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const bool valid = t < a.n;
+
+  float xr[D];
+  float xn = 0.0f;
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    xr[j] = valid ? load_elem<BF16>(x + uint64_t(t) * D * EB, j) : 0.0f;
+    xn = fmaf(xr[j], xr[j], xn);
+  }
+  float s1 = INFINITY, s2 = INFINITY, cmax = 0.0f;
+  int k1 = 0;
+  for (int k0 = 0; k0 < L.C; k0 += TK) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < TK * D; i += blockDim.x) {
+      const int kk = i / D, j = i % D, k = k0 + kk;
+      cs[kk][j] = k < L.C ? load_elem<BF16>(cb + uint64_t(k) * D * EB, j) : 0.0f;
+    }
+    if (threadIdx.x < TK) cns[threadIdx.x] = k0 + int(threadIdx.x) < L.C ? cn[k0 + threadIdx.x] : 0.0f;
+    __syncthreads();
+    const int kmax = min(TK, L.C - k0);
+    for (int kk = 0; kk < kmax; ++kk) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int j = 0; j < D; ++j) dot = fmaf(xr[j], cs[kk][j], dot);
+      const float s = cns[kk] - 2.0f * dot;
+      cmax = fmaxf(cmax, cns[kk]);
+      if (s < s1) {
+        s2 = s1; s1 = s; k1 = k0 + kk;
+      } else if (s < s2) {
+        s2 = s;
+      }
+    }
+  }
+  const float E = float(D + 8) * 0x1p-23f * (xn + cmax);
+  const bool flag = valid && !(s2 - s1 > 2.0f * E);
+
+  const int lane = threadIdx.x & 63;
+  uint64_t fm = __ballot(flag);
+  while (fm) {
+    const int src = __ffsll((unsigned long long)fm) - 1;
+    fm &= fm - 1;
+    const int tf = blockIdx.x * blockDim.x + (threadIdx.x & ~63) + src;
+    const uint8_t *xrow = x + uint64_t(tf) * D * EB;
+    double best = INFINITY;
+    int bk = 0x7fffffff;
+    for (int k = lane; k < L.C; k += 64) {
+      const uint8_t *crow = cb + uint64_t(k) * D * EB;
+      double dd = 0.0;
+      for (int j = 0; j < D; ++j) {
+        const double diff = double(load_elem<BF16>(xrow, j)) - double(load_elem<BF16>(crow, j));
+        dd = dd + diff * diff;
+      }
+      if (dd < best) { best = dd; bk = k; }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ob = __shfl_xor(best, off);
+      const int ok = __shfl_xor(bk, off);
+      if (ob < best || (ob == best && ok < bk)) { best = ob; bk = ok; }
+    }
+    if (lane == src) k1 = bk;
+  }
+  if (valid) {
+    uint8_t *ids = st + L.ids_off + uint64_t(h) * L.ids_head;
+    const int64_t tt = int64_t(a.t0) + t;
+    if (L.id_bytes == 1) ids[tt] = uint8_t(k1);
+    else ((uint16_t *)ids)[tt] = uint16_t(k1);
+  }
+}
+
+// One wave per 4 clusters; blockIdx.x = group of 16 clusters, y = head, z = stream.
+// Each wave scans the call's ids in token order and adds the member rows in
+// fp64 (lane = D/64 channels), so every centroid sum is the sequential sum in
+// token order.  Empty clusters keep their centroid.
+template <int D, bool BF16>
+__device__ __forceinline__ void finalize_centroid(uint8_t *cb, float *cn, int k, int C, int cnt,
+                                                  const double *acc, int lane) {
+  constexpr int CPL = D / 64;
+  if (k >= C || cnt == 0) return;
+  double nrm = 0.0;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const double mean = acc[c] / double(cnt);
+    const int j = lane * CPL + c;
+    float v;
+    if constexpr (BF16) {
+      const uint16_t b = f64_to_bf16_bits(mean);
+      ((uint16_t *)cb)[uint64_t(k) * D + j] = b;
+      v = bf16_to_f32(b);
+    } else {
+      v = float(mean);
+      ((float *)cb)[uint64_t(k) * D + j] = v;
+    }
+    nrm = nrm + double(v) * double(v);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) nrm += __shfl_xor(nrm, off);
+  if (lane == 0) cn[k] = float(nrm);
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_update(EncodeArgs a) {
+  constexpr int EB = BF16 ? 2 : 4;
+  constexpr int CPL = D / 64;
+  const DevLayout &L = a.L;
+  const int h = blockIdx.y, z = blockIdx.z, lrel = z >> 1, kv = z & 1;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kb = blockIdx.x * 16 + wave * 4;
+  if (kb >= L.C) return;  // whole wave exits together
+  uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, kv);
+  const uint8_t *x = (kv ? a.v_in : a.k_in) + (uint64_t(lrel) * L.H + h) * uint64_t(a.n) * D * EB;
+  const uint8_t *ids = st + L.ids_off + uint64_t(h) * L.ids_head + uint64_t(a.t0) * L.id_bytes;
+  uint8_t *cb = st + L.cb_off + uint64_t(a.slot) * L.cb_chunk + uint64_t(h) * L.cb_head;
+  float *cn = (float *)(st + L.cn_off + uint64_t(a.slot) * L.cn_chunk + uint64_t(h) * L.cn_head);
+
+  double acc0[CPL], acc1[CPL], acc2[CPL], acc3[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc0[c] = acc1[c] = acc2[c] = acc3[c] = 0.0;
+  int n0 = 0, n1 = 0, n2 = 0, n3 = 0;
+  for (int base = 0; base < a.n; base += 64) {
+    const int t = base + lane;
+    const int myid = t < a.n ? load_id(ids, L.id_bytes, t) : -1;
+    const uint64_t m0 = __ballot(myid == kb), m1 = __ballot(myid == kb + 1);
+    const uint64_t m2 = __ballot(myid == kb + 2), m3 = __ballot(myid == kb + 3);
+    uint64_t all = m0 | m1 | m2 | m3;
+    while (all) {
+      const int b = __ffsll((unsigned long long)all) - 1;
+      all &= all - 1;
+      const uint64_t bit = uint64_t(1) << b;
+      const uint8_t *row = x + uint64_t(base + b) * D * EB;
+      double v[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) v[c] = double(load_elem<BF16>(row, lane * CPL + c));
+      if (m0 & bit) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc0[c] = acc0[c] + v[c];
+        ++n0;
+      } else if (m1 & bit) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc1[c] = acc1[c] + v[c];
+        ++n1;
+      } else if (m2 & bit) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc2[c] = acc2[c] + v[c];
+        ++n2;
+      } else {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc3[c] = acc3[c] + v[c];
+        ++n3;
+      }
+    }
+  }
+  finalize_centroid<D, BF16>(cb, cn, kb + 0, L.C, n0, acc0, lane);
+  finalize_centroid<D, BF16>(cb, cn, kb + 1, L.C, n1, acc1, lane);
+  finalize_centroid<D, BF16>(cb, cn, kb + 2, L.C, n2, acc2, lane);
+  finalize_centroid<D, BF16>(cb, cn, kb + 3, L.C, n3, acc3, lane);
+}
+
+// One thread per (token, group).  blockIdx.x = tile of 256 (token, group)
+// items, y = head, z = stream.  Base = centroid of the token's cluster, or the
+// cross-layer prediction when a.pred is set (then the reconstruction is also
+// written to a.chain in bf16).
+template <int D, int G, int BITS, bool BF16>
+__global__ __launch_bounds__(256) void k_quantize(EncodeArgs a) {
+  constexpr int EB = BF16 ? 2 : 4;
+  constexpr int NG = D / G;
+  constexpr int WORDS = G * BITS / 32;
+  constexpr float LEVELS = float((1 << BITS) - 1);
+  const DevLayout &L = a.L;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int t = idx / NG, g = idx % NG;
+  if (t >= a.n) return;
+  const int h = blockIdx.y, z = blockIdx.z, lrel = z >> 1, kv = z & 1;
+  uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, kv);
+  const uint8_t *xrow =
+      (kv ? a.v_in : a.k_in) + ((uint64_t(lrel) * L.H + h) * uint64_t(a.n) + t) * D * EB;
+  const int64_t tt = int64_t(a.t0) + t;
+
+  float r[G], xh[G];
+  if (a.pred) {
+    const float *p = a.pred + ((uint64_t(kv) * L.H + h) * uint64_t(a.n) + t) * D + g * G;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      xh[j] = p[j];
+      r[j] = load_elem<BF16>(xrow, g * G + j) - p[j];
+    }
+  } else {
+    const uint8_t *ids = st + L.ids_off + uint64_t(h) * L.ids_head;
+    const int id = load_id(ids, L.id_bytes, tt);
+    const uint8_t *crow = st + L.cb_off + uint64_t(a.slot) * L.cb_chunk + uint64_t(h) * L.cb_head +
+                          uint64_t(id) * D * EB;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float c = load_elem<BF16>(crow, g * G + j);
+      xh[j] = c;
+      r[j] = load_elem<BF16>(xrow, g * G + j) - c;
+    }
+  }
+  for (int s = 0; s < L.S; ++s) {
+    float mn = r[0], mx = r[0];
+#pragma unroll
+    for (int j = 1; j < G; ++j) {
+      mn = fminf(mn, r[j]);
+      mx = fmaxf(mx, r[j]);
+    }
+    const uint16_t zb = f32_to_f16_bits(mn);
+    const float zf = f16_bits_to_f32(zb);
+    const uint16_t sb = f32_to_f16_bits((mx - zf) / LEVELS);
+    const float sf = f16_bits_to_f32(sb);
+    const bool live = sf != 0.0f;
+    const float inv = live ? 1.0f / sf : 0.0f;
+    uint32_t w[WORDS];
+#pragma unroll
+    for (int i = 0; i < WORDS; ++i) w[i] = 0;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      float q = 0.0f;
+      if (live) q = fminf(fmaxf(rintf((r[j] - zf) * inv), 0.0f), LEVELS);
+      w[(j * BITS) / 32] |= uint32_t(q) << ((j * BITS) % 32);
+      const float rh = fmaf(q, sf, zf);
+      r[j] = r[j] - rh;
+      xh[j] = xh[j] + rh;
+    }
+    uint8_t *cp = st + L.codes_off + uint64_t(s) * L.codes_stage + uint64_t(h) * L.codes_head +
+                  uint64_t(tt) * L.codes_token + uint64_t(g) * (G * BITS / 8);
+    if constexpr (WORDS == 2) {
+      *(uint2 *)cp = make_uint2(w[0], w[1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < WORDS; i += 4) *(uint4 *)(cp + 4 * i) = make_uint4(w[i], w[i + 1], w[i + 2], w[i + 3]);
+    }
+    uint32_t *mp = (uint32_t *)(st + L.meta_off + uint64_t(s) * L.meta_stage + uint64_t(h) * L.meta_head +
+                                uint64_t(tt) * L.meta_token) + g;
+    *mp = uint32_t(sb) | (uint32_t(zb) << 16);
+  }
+  if (a.chain) {
+    uint16_t *cp = a.chain + ((uint64_t(kv) * L.H + h) * uint64_t(a.n) + t) * D + g * G;
+#pragma unroll
+    for (int j = 0; j < G; ++j) cp[j] = f32_to_bf16_bits(xh[j]);
+  }
+}
+
+// ----------------------------------------------------------------- decode
+
+// Rebuild one group (G channels) of token tt of head h in fp32:
+// xhat = fl32(...fl32(base + rhat_1)... + rhat_S).  xh holds the base on entry.
+template <int D, int G, int BITS>
+__device__ __forceinline__ void add_stages(const uint8_t *st, const DevLayout &L, int h, int64_t tt,
+                                           int g, float *xh) {
+  constexpr int WORDS = G * BITS / 32;
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  for (int s = 0; s < L.S; ++s) {
+    const uint8_t *cp = st + L.codes_off + uint64_t(s) * L.codes_stage + uint64_t(h) * L.codes_head +
+                        uint64_t(tt) * L.codes_token + uint64_t(g) * (G * BITS / 8);
+    uint32_t w[WORDS];
+    if constexpr (WORDS == 2) {
+      const uint2 v = *(const uint2 *)cp;
+      w[0] = v.x; w[1] = v.y;
+    } else {
+#pragma unroll
+      for (int i = 0; i < WORDS; i += 4) {
+        const uint4 v = *(const uint4 *)(cp + 4 * i);
+        w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
+      }
+    }
+    const uint32_t m = *((const uint32_t *)(st + L.meta_off + uint64_t(s) * L.meta_stage +
+                                            uint64_t(h) * L.meta_head + uint64_t(tt) * L.meta_token) + g);
+    const float sf = f16_bits_to_f32(uint16_t(m & 0xffffu));
+    const float zf = f16_bits_to_f32(uint16_t(m >> 16));
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float q = float((w[(j * BITS) / 32] >> ((j * BITS) % 32)) & MASK);
+      xh[j] = xh[j] + fmaf(q, sf, zf);
+    }
+  }
+}
+
+// Centroid base of token tt (snapshot of its chunk).
+template <int D, int G, bool CB_BF16>
+__device__ __forceinline__ void centroid_base(const uint8_t *st, const DevLayout &L, int h, int tt, int g,
+                                              float *xh) {
+  constexpr int EB = CB_BF16 ? 2 : 4;
+  const StreamHeader *hdr = (const StreamHeader *)(st + L.header_off);
+  const int slot = chunk_of(hdr, tt);
+  const int id = load_id(st + L.ids_off + uint64_t(h) * L.ids_head, L.id_bytes, tt);
+  const uint8_t *crow = st + L.cb_off + uint64_t(slot) * L.cb_chunk + uint64_t(h) * L.cb_head +
+                        uint64_t(id) * D * EB + uint64_t(g) * G * EB;
+#pragma unroll
+  for (int j = 0; j < G; ++j) xh[j] = load_elem<CB_BF16>(crow, j);
+}
+
+// One thread per (token, group).  blockIdx.x = item tile, y = head, z = layer.
+template <int D, int G, int BITS, bool CB_BF16>
+__global__ __launch_bounds__(256) void k_reconstruct(ReconArgs a, int64_t out_tokens, int32_t out_t_off) {
+  constexpr int NG = D / G;
+  const DevLayout &L = a.L;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int t = idx / NG, g = idx % NG;
+  if (t >= a.n) return;
+  const int h = blockIdx.y, lrel = blockIdx.z;
+  const uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, a.kv);
+  const int tt = a.t0 + t;
+  float xh[G];
+  if (a.pred) {
+    const float *p = a.pred + (uint64_t(h) * a.n + t) * D + g * G;
+#pragma unroll
+    for (int j = 0; j < G; ++j) xh[j] = p[j];
+  } else {
+    centroid_base<D, G, CB_BF16>(st, L, h, tt, g, xh);
+  }
+  add_stages<D, G, BITS>(st, L, h, tt, g, xh);
+  if (a.out) {
+    const uint64_t o = ((uint64_t(lrel) * L.H + h) * uint64_t(out_tokens) + out_t_off + t) * D + g * G;
+    if (a.out_bf16) {
+      uint16_t *op = (uint16_t *)a.out + o;
+#pragma unroll
+      for (int j = 0; j < G; ++j) op[j] = f32_to_bf16_bits(xh[j]);
+    } else {
+      float *op = (float *)a.out + o;
+#pragma unroll
+      for (int j = 0; j < G; j += 4) *(float4 *)(op + j) = make_float4(xh[j], xh[j + 1], xh[j + 2], xh[j + 3]);
+    }
+  }
+  if (a.chain) {
+    uint16_t *cp = a.chain + (uint64_t(h) * a.n + t) * D + g * G;
+#pragma unroll
+    for (int j = 0; j < G; ++j) cp[j] = f32_to_bf16_bits(xh[j]);
+  }
+}
+
+// -------------------------------------------------------------- attention
+//
+// Block = 4 waves = 128 queries of one head (32 per wave, two 16-column MFMA
+// blocks); grid = (query blocks, heads, KV splits).  Per 64-key tile the
+// block rebuilds K and V in bf16 into LDS (K as [key][d], V transposed as
+// [d][key]), then each wave computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16
+// (so each lane's accumulator column is one query), runs the online softmax
+// in fp32 with exp2, and accumulates O^T += V^T P^T with the probabilities
+// rounded to bf16.  The key order inside one 32-key MFMA step is permuted
+// identically in both operands so that P^T comes straight from the S^T
+// accumulator registers.
+constexpr int ATT_BQ = 128;
+constexpr int ATT_BK = 64;
+
+template <int D, int G, int BITS, bool CB_BF16>
+__global__ __launch_bounds__(256) void k_attend(AttnArgs a) {
+  constexpr int NG = D / G;
+  constexpr int KP = D + 8;          // Ks row pitch (elements)
+  constexpr int VP = ATT_BK + 8;     // Vt row pitch (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[ATT_BK * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
+  const DevLayout &L = a.L;
+  const int h = blockIdx.y, split = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const float sc = 1.4426950408889634f / sqrtf(float(D));   // log2(e)/sqrt(d)
+
+  // query fragments (B operand of S^T = K Q^T): lane holds Q[q][32*step + 8*g4 .. +8]
+  bf16x8 qf[2][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int q = blockIdx.x * ATT_BQ + wave * 32 + qb * 16 + c16;
+#pragma unroll
+    for (int step = 0; step < D / 32; ++step) {
+      bf16x8 v;
+      if (q < a.n_q) {
+        const uint64_t off = (uint64_t(h) * a.n_q + q) * D + step * 32 + g4 * 8;
+        if (a.q_bf16) {
+          v = *(const bf16x8 *)((const uint16_t *)a.q + off);
+        } else {
+          const float *qp = (const float *)a.q + off;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)qp[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+      }
+      qf[qb][step] = v;
+    }
+  }
+
+  floatx4 o[D / 16][2];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) o[db][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+  const int ks = split * a.split_len;
+  const int ke = min(a.n_keys, ks + a.split_len);
+  for (int kt0 = ks; kt0 < ke; kt0 += ATT_BK) {
+    __syncthreads();
+    // rebuild the K and V tile in bf16
+    for (int it = threadIdx.x; it < ATT_BK * NG; it += blockDim.x) {
+      const int key = it / NG, g = it % NG;
+      const int tt = kt0 + key;
+      float xk[G], xv[G];
+      if (tt < ke) {
+        centroid_base<D, G, CB_BF16>(a.stream_k, L, h, tt, g, xk);
+        add_stages<D, G, BITS>(a.stream_k, L, h, tt, g, xk);
+        centroid_base<D, G, CB_BF16>(a.stream_v, L, h, tt, g, xv);
+        add_stages<D, G, BITS>(a.stream_v, L, h, tt, g, xv);
+      } else {
+#pragma unroll
+        for (int j = 0; j < G; ++j) xk[j] = xv[j] = 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < G; j += 2) {
+        const uint32_t pk = uint32_t(f32_to_bf16_bits(xk[j])) | (uint32_t(f32_to_bf16_bits(xk[j + 1])) << 16);
+        *(uint32_t *)&Ks[key * KP + g * G + j] = pk;
+      }
+#pragma unroll
+      for (int j = 0; j < G; ++j) Vt[(g * G + j) * VP + key] = f32_to_bf16_bits(xv[j]);
+    }
+    __syncthreads();
+
+    // S^T blocks: s[kb][qb], rows = keys 16kb + 4g4 + r, column = query c16
+    floatx4 s[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int step = 0; step < D / 32; ++step) {
+        const bf16x8 ka = *(const bf16x8 *)&Ks[(kb * 16 + c16) * KP + step * 32 + g4 * 8];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qb][step], s[kb][qb], 0, 0, 0);
+      }
+    }
+    // online softmax per query column
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float tmax = -INFINITY;
+      float sv[4][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kt0 + kb * 16 + g4 * 4 + r;
+          const float v = key < ke ? s[kb][qb][r] * sc : -INFINITY;
+          sv[kb][r] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mnew = fmaxf(m_run[qb], tmax);
+      const float alpha = exp2f(m_run[qb] - mnew);
+      float rs = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = exp2f(sv[kb][r] - mnew);
+          sv[kb][r] = p;
+          rs += p;
+        }
+      rs += __shfl_xor(rs, 16);
+      rs += __shfl_xor(rs, 32);
+      l_run[qb] = l_run[qb] * alpha + rs;
+      m_run[qb] = mnew;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) o[db][qb] *= alpha;
+#pragma unroll
+      for (int st2 = 0; st2 < 2; ++st2) {
+        bf16x8 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = (__bf16)sv[2 * st2][r];
+          v[4 + r] = (__bf16)sv[2 * st2 + 1][r];
+        }
+        pb[qb][st2] = v;
+      }
+    }
+    // O^T += V^T P^T; A = V^T rows d, key slots (32*st2 + 4*g4 + 0..3, 32*st2 + 16 + 4*g4 + 0..3)
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+#pragma unroll
+      for (int st2 = 0; st2 < 2; ++st2) {
+        const uint16_t *vr = &Vt[(db * 16 + c16) * VP + st2 * 32 + g4 * 4];
+        const bf16x4 lo = *(const bf16x4 *)vr;
+        const bf16x4 hi = *(const bf16x4 *)(vr + 16);
+        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qb][st2], o[db][qb], 0, 0, 0);
+      }
+    }
+  }
+
+  // write: lane holds O[q][16db + 4g4 + r]
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int q = blockIdx.x * ATT_BQ + wave * 32 + qb * 16 + c16;
+    if (q >= a.n_q) continue;
+    const bool empty = l_run[qb] == 0.0f;
+    const float inv_l = empty ? 0.0f : 1.0f / l_run[qb];
+    const float lse = empty ? -INFINITY : (m_run[qb] + log2f(l_run[qb])) * 0.6931471805599453f;
+    if (a.n_splits == 1) {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const uint64_t off = (uint64_t(h) * a.n_q + q) * D + db * 16 + g4 * 4;
+        const floatx4 v = o[db][qb] * inv_l;
+        if (a.out_bf16) {
+          uint16_t *op = (uint16_t *)a.out + off;
+          const uint32_t p0 = uint32_t(f32_to_bf16_bits(v[0])) | (uint32_t(f32_to_bf16_bits(v[1])) << 16);
+          const uint32_t p1 = uint32_t(f32_to_bf16_bits(v[2])) | (uint32_t(f32_to_bf16_bits(v[3])) << 16);
+          *(uint2 *)op = make_uint2(p0, p1);
+        } else {
+          *(float4 *)((float *)a.out + off) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+      if (a.lse && g4 == 0) a.lse[uint64_t(h) * a.n_q + q] = lse;
+    } else {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const uint64_t off = ((uint64_t(split) * L.H + h) * a.n_q + q) * D + db * 16 + g4 * 4;
+        const floatx4 v = o[db][qb] * inv_l;
+        *(float4 *)(a.part_o + off) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      if (g4 == 0) a.part_lse[(uint64_t(split) * L.H + h) * a.n_q + q] = lse;
+    }
+  }
+}
+
+// Merge split partials: O = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - max).
+// One thread per (query, channel); blockIdx.y = head.
+__global__ __launch_bounds__(256) void k_attend_merge(AttnArgs a) {
+  const int D = a.L.D;
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= int64_t(a.n_q) * D) return;
+  const int q = int(idx / D), dd = int(idx % D), h = blockIdx.y;
+  float mx = -INFINITY;
+  for (int s = 0; s < a.n_splits; ++s)
+    mx = fmaxf(mx, a.part_lse[(uint64_t(s) * a.L.H + h) * a.n_q + q]);
+  float wsum = 0.0f, acc = 0.0f;
+  for (int s = 0; s < a.n_splits; ++s) {
+    const float ls = a.part_lse[(uint64_t(s) * a.L.H + h) * a.n_q + q];
+    if (ls == -INFINITY) continue;
+    const float w = expf(ls - mx);
+    wsum += w;
+    acc = fmaf(w, a.part_o[((uint64_t(s) * a.L.H + h) * a.n_q + q) * D + dd], acc);
+  }
+  const float v = acc / wsum;
+  const uint64_t off = (uint64_t(h) * a.n_q + q) * D + dd;
+  if (a.out_bf16) ((uint16_t *)a.out)[off] = f32_to_bf16_bits(v);
+  else ((float *)a.out)[off] = v;
+  if (a.lse && dd == 0) a.lse[uint64_t(h) * a.n_q + q] = mx + logf(wsum);
+}
+
+// ------------------------------------------------------------ cross layer
+
+// p[t][k] = sum over m = 0..H*D-1 of V[m][k] * y[t][m] in fp64 (order m),
+// rounded once to bf16.  blockIdx.x = token tile, y = kv index (kv0 + y).
+__global__ __launch_bounds__(256) void k_xl_project(XlArgs a, int kv0) {
+  int rp = 1;
+  while (rp < a.r) rp <<= 1;
+  const int tpb = 256 / rp;
+  const int t = blockIdx.x * tpb + int(threadIdx.x) / rp;
+  const int k = int(threadIdx.x) % rp;
+  const int kv = kv0 + blockIdx.y;
+  if (t >= a.n || k >= a.r) return;
+  const uint64_t HD = uint64_t(a.H) * a.D;
+  const uint16_t *Vw = a.weights + uint64_t(kv) * a.kv_weight_stride + HD * a.D + HD * a.r;
+  const uint16_t *y = a.chain + uint64_t(kv) * HD * a.n;
+  double acc = 0.0;
+  for (int hh = 0; hh < a.H; ++hh) {
+    const uint16_t *yr = y + (uint64_t(hh) * a.n + t) * a.D;
+    for (int j = 0; j < a.D; ++j) {
+      const uint64_t m = uint64_t(hh) * a.D + j;
+      acc = acc + double(bf16_to_f32(yr[j])) * double(bf16_to_f32(Vw[m * a.r + k]));
+    }
+  }
+  a.proj[(uint64_t(kv) * a.n + t) * a.r + k] = bf16_to_f32(f64_to_bf16_bits(acc));
+}
+
+// pred[h][t][i] = sum_j B_h[i][j] y_h[t][j] (order j) then + sum_k U[h*D+i][k] w[t][k]
+// (order k), fp64, rounded once to fp32.  One thread per (t, i); y = head, z = kv.
+__global__ __launch_bounds__(256) void k_xl_predict(XlArgs a, int kv0) {
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= int64_t(a.n) * a.D) return;
+  const int t = int(idx / a.D), i = int(idx % a.D);
+  const int h = blockIdx.y, kv = kv0 + blockIdx.z;
+  const uint64_t HD = uint64_t(a.H) * a.D;
+  const uint16_t *W = a.weights + uint64_t(kv) * a.kv_weight_stride;
+  const uint16_t *B = W + uint64_t(h) * a.D * a.D + uint64_t(i) * a.D;
+  const uint16_t *U = W + HD * a.D + (uint64_t(h) * a.D + i) * a.r;
+  const uint16_t *y = a.chain + (uint64_t(kv) * HD * a.n) + (uint64_t(h) * a.n + t) * a.D;
+  const float *w = a.proj + (uint64_t(kv) * a.n + t) * a.r;
+  double acc = 0.0;
+  for (int j = 0; j < a.D; ++j) acc = acc + double(bf16_to_f32(B[j])) * double(bf16_to_f32(y[j]));
+  for (int k = 0; k < a.r; ++k) acc = acc + double(bf16_to_f32(U[k])) * double(w[k]);
+  a.pred[(uint64_t(kv) * HD * a.n) + (uint64_t(h) * a.n + t) * a.D + i] = float(acc);
+}
+
+// chunk table after a rewind: blockIdx.x = stream of the range
+__global__ void k_set_header(uint8_t *arena, DevLayout L, int layer0, int n_chunks, int n_tokens) {
+  if (threadIdx.x != 0) return;
+  const int z = blockIdx.x;
+  StreamHeader *hdr = (StreamHeader *)(stream_ptr(arena, L, layer0 + (z >> 1), z & 1) + L.header_off);
+  hdr->n_chunks = n_chunks;
+  hdr->n_tokens = n_tokens;
+}
+
+// ---------------------------------------------------------------- launchers
+
+static inline unsigned cdiv(int64_t a, int64_t b) { return unsigned((a + b - 1) / b); }
+
+#define QKV_DISPATCH_D_BF16(D_, BF_, FN, ...)                           \
+  do {                                                                  \
+    if (D_ == 64 && BF_) FN<64, true>(__VA_ARGS__);                     \
+    else if (D_ == 64) FN<64, false>(__VA_ARGS__);                      \
+    else if (BF_) FN<128, true>(__VA_ARGS__);                           \
+    else FN<128, false>(__VA_ARGS__);                                   \
+  } while (0)
+
+template <int D, bool BF>
+static void launch_init_t(const EncodeArgs &a, int streams, hipStream_t st) {
+  hipLaunchKernelGGL((k_init<D, BF>), dim3(a.L.H, streams), dim3(256), 0, st, a);
+}
+template <int D, bool BF>
+static void launch_assign_t(const EncodeArgs &a, int streams, hipStream_t st) {
+  hipLaunchKernelGGL((k_assign<D, BF>), dim3(cdiv(a.n, 256), a.L.H, streams), dim3(256), 0, st, a);
+}
+template <int D, bool BF>
+static void launch_update_t(const EncodeArgs &a, int streams, hipStream_t st) {
+  hipLaunchKernelGGL((k_update<D, BF>), dim3(cdiv(a.L.C, 16), a.L.H, streams), dim3(256), 0, st, a);
+}
+
+template <int D, int G, int BITS, bool BF>
+static void launch_quantize_t(const EncodeArgs &a, int streams, hipStream_t st) {
+  const int64_t items = int64_t(a.n) * (D / G);
+  hipLaunchKernelGGL((k_quantize<D, G, BITS, BF>), dim3(cdiv(items, 256), a.L.H, streams), dim3(256), 0,
+                     st, a);
+}
+
+template <int D, int G, int BITS, bool BF>
+static void launch_recon_t(const ReconArgs &a, int n_layers, int64_t out_tokens, int out_t_off,
+                           hipStream_t st) {
+  const int64_t items = int64_t(a.n) * (D / G);
+  hipLaunchKernelGGL((k_reconstruct<D, G, BITS, BF>), dim3(cdiv(items, 256), a.L.H, n_layers), dim3(256),
+                     0, st, a, out_tokens, out_t_off);
+}
+
+template <int D, int G, int BITS, bool BF>
+static void launch_attend_t(const AttnArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL((k_attend<D, G, BITS, BF>), dim3(cdiv(a.n_q, ATT_BQ), a.L.H, a.n_splits), dim3(256),
+                     0, st, a);
+}
+
+// (D, G, BITS, BF) dispatch for the codec-shaped kernels
+#define QKV_DISPATCH_CODEC(L_, FN, ...)                                                   \
+  do {                                                                                    \
+    const int D_ = (L_).D, G_ = (L_).G, B_ = (L_).bits;                                   \
+    const bool BF_ = (L_).kv_bf16 != 0;                                                   \
+    if (D_ == 64 && G_ == 32 && B_ == 2) { if (BF_) FN<64, 32, 2, true>(__VA_ARGS__); else FN<64, 32, 2, false>(__VA_ARGS__); } \
+    else if (D_ == 64 && G_ == 32) { if (BF_) FN<64, 32, 4, true>(__VA_ARGS__); else FN<64, 32, 4, false>(__VA_ARGS__); }      \
+    else if (D_ == 64 && B_ == 2) { if (BF_) FN<64, 64, 2, true>(__VA_ARGS__); else FN<64, 64, 2, false>(__VA_ARGS__); }       \
+    else if (D_ == 64) { if (BF_) FN<64, 64, 4, true>(__VA_ARGS__); else FN<64, 64, 4, false>(__VA_ARGS__); }                  \
+    else if (G_ == 32 && B_ == 2) { if (BF_) FN<128, 32, 2, true>(__VA_ARGS__); else FN<128, 32, 2, false>(__VA_ARGS__); }     \
+    else if (G_ == 32) { if (BF_) FN<128, 32, 4, true>(__VA_ARGS__); else FN<128, 32, 4, false>(__VA_ARGS__); }                \
+    else if (B_ == 2) { if (BF_) FN<128, 64, 2, true>(__VA_ARGS__); else FN<128, 64, 2, false>(__VA_ARGS__); }                 \
+    else { if (BF_) FN<128, 64, 4, true>(__VA_ARGS__); else FN<128, 64, 4, false>(__VA_ARGS__); }                              \
+  } while (0)
+
+void launch_header(const EncodeArgs &a, int streams, hipStream_t st) {
+  hipLaunchKernelGGL(k_header, dim3(streams), dim3(64), 0, st, a);
+}
+void launch_init(const EncodeArgs &a, int streams, hipStream_t st) {
+  QKV_DISPATCH_D_BF16(a.L.D, a.L.kv_bf16, launch_init_t, a, streams, st);
+}
+void launch_assign(const EncodeArgs &a, int streams, hipStream_t st) {
+  QKV_DISPATCH_D_BF16(a.L.D, a.L.kv_bf16, launch_assign_t, a, streams, st);
+}
+void launch_update(const EncodeArgs &a, int streams, hipStream_t st) {
+  QKV_DISPATCH_D_BF16(a.L.D, a.L.kv_bf16, launch_update_t, a, streams, st);
+}
+void launch_quantize(const EncodeArgs &a, int streams, hipStream_t st) {
+  QKV_DISPATCH_CODEC(a.L, launch_quantize_t, a, streams, st);
+}
+void launch_reconstruct(const ReconArgs &a, int n_layers, int64_t out_tokens, int out_t_off, hipStream_t st) {
+  QKV_DISPATCH_CODEC(a.L, launch_recon_t, a, n_layers, out_tokens, out_t_off, st);
+}
+void launch_attend(const AttnArgs &a, hipStream_t st) {
+  QKV_DISPATCH_CODEC(a.L, launch_attend_t, a, st);
+  if (a.n_splits > 1)
+    hipLaunchKernelGGL(k_attend_merge, dim3(cdiv(int64_t(a.n_q) * a.L.D, 256), a.L.H), dim3(256), 0, st, a);
+}
+void launch_xl_predict(const XlArgs &a, int kv0, int n_kv, hipStream_t st) {
+  int rp = 1;
+  while (rp < a.r) rp <<= 1;
+  const int tpb = 256 / rp;
+  hipLaunchKernelGGL(k_xl_project, dim3(cdiv(a.n, tpb), n_kv), dim3(256), 0, st, a, kv0);
+  hipLaunchKernelGGL(k_xl_predict, dim3(cdiv(int64_t(a.n) * a.D, 256), a.H, n_kv), dim3(256), 0, st, a, kv0);
+}
+void launch_set_header(uint8_t *arena, const DevLayout &L, int layer0, int n_layers, int n_chunks,
+                       int n_tokens, hipStream_t st) {
+  hipLaunchKernelGGL(k_set_header, dim3(2 * n_layers), dim3(64), 0, st, arena, L, layer0, n_chunks, n_tokens);
+}
+
+}  // namespace qkv

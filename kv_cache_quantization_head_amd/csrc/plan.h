@@ -1,0 +1,97 @@
+// Host-side plan of the qkv library: configuration checks, arena layout and
+// per-layer stream state.  Contains no HIP code so that it can be compiled and
+// tested on a machine without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/qkv.h"
+
+namespace qkv {
+
+constexpr int kMaxChunks = 256;      // snapshot slots per stream (header size)
+constexpr int kMaxSplits = 8;        // split-KV partitions of one attention call
+constexpr uint64_t kAlign = 256;
+
+inline uint64_t align_up(uint64_t v, uint64_t a = kAlign) { return (v + a - 1) / a * a; }
+
+// Device-side header at the start of every (layer, K|V) stream region.
+// start[c] is the first token of chunk c; entries at or beyond n_chunks are
+// not read by any kernel.
+struct StreamHeader {
+  int32_t n_chunks;
+  int32_t n_tokens;
+  int32_t start[kMaxChunks + 1];
+};
+
+// Byte offsets and strides of one stream, relative to the stream's base.
+struct StreamLayout {
+  uint64_t header_off;
+  uint64_t codes_off, codes_stage, codes_head, codes_token;
+  uint64_t meta_off, meta_stage, meta_head, meta_token;
+  uint64_t ids_off, ids_head, id_bytes;
+  uint64_t cb_off, cb_chunk, cb_head, cb_row;
+  uint64_t cn_off, cn_chunk, cn_head;
+  uint64_t bytes;      // whole stream, aligned
+};
+
+struct Plan {
+  qkv_config cfg;
+  StreamLayout s;
+  uint64_t streams_bytes;     // 2 * L * s.bytes
+  // scratch, shared by the calls of one context (they are ordered on the device)
+  uint64_t scratch_off, scratch_bytes;
+  uint64_t attn_part_o_off, attn_part_lse_off;     // relative to scratch
+  uint64_t xl_pred_off, xl_chain_off, xl_proj_off; // relative to scratch
+  uint64_t total_bytes;
+  int kv_elem_bytes;
+};
+
+// Returns QKV_OK and fills plan, or a negative status.
+int make_plan(const qkv_config *cfg, Plan *plan);
+
+struct LayerState {
+  int64_t n_tokens = 0;
+  std::vector<int64_t> starts;   // first token of each chunk
+};
+
+}  // namespace qkv
+
+struct qkv_ctx {
+  qkv::Plan plan;
+  uint8_t *arena = nullptr;
+  uint64_t arena_bytes = 0;
+  const uint8_t *predictor = nullptr;
+  std::vector<qkv::LayerState> layers;
+  // cross-layer chain: bf16 reconstruction of layer `chain_layer` for tokens
+  // [chain_t0, chain_t0 + chain_n) is held in scratch after an encode call
+  int32_t chain_layer = -1;
+  int64_t chain_t0 = 0, chain_n = 0;
+  int last_hip_error = 0;
+  std::string last_error;
+};
+
+namespace qkv {
+
+// Validation of each entry point's arguments against the context state.
+// These run before anything is enqueued and never touch device memory.
+int check_encode(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, const void *k,
+                 const void *v, int64_t n);
+int check_attend(const qkv_ctx *ctx, int32_t layer, const void *q, int64_t n_q, int32_t q_dtype,
+                 const void *out, int32_t out_dtype);
+int check_reconstruct(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int32_t kv, int64_t t0,
+                      int64_t t1, const void *out, int32_t out_dtype);
+int check_rewind(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int64_t n_tokens);
+
+// Number of KV splits used by an attention call over n_keys keys.
+int attention_splits(const Plan &p, int64_t n_keys, int64_t n_q);
+
+// Byte offset of stream (layer, kv) from the arena base.
+inline uint64_t stream_offset(const Plan &p, int layer, int kv) {
+  return (uint64_t(layer) * 2 + uint64_t(kv)) * p.s.bytes;
+}
+
+}  // namespace qkv

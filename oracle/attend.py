@@ -18,21 +18,28 @@ import numpy as np
 from .numerics import round_to_bf16
 
 
-def attend(q, khat, vhat):
+def attend(q, khat, vhat, rows=256):
     """q [H, Tq, d]; khat, vhat [H, Tk, d] (fp32 reconstructions).
 
-    Returns O [H, Tq, d] float64 and LSE [H, Tq] float64.
+    Returns O [H, Tq, d] float64 and LSE [H, Tq] float64.  Query rows are
+    independent; they are processed ``rows`` at a time only to bound memory.
     """
     qb = round_to_bf16(q).astype(np.float64)
     kb = round_to_bf16(khat).astype(np.float64)
     vb = round_to_bf16(vhat).astype(np.float64)
-    d = q.shape[-1]
-    logits = np.matmul(qb, np.swapaxes(kb, -1, -2)) / np.sqrt(np.float64(d))
-    m = logits.max(axis=-1, keepdims=True)
-    p = np.exp(logits - m)
-    denom = p.sum(axis=-1, keepdims=True)
-    out = np.matmul(p, vb) / denom
-    lse = (m + np.log(denom))[..., 0]
+    H, Tq, d = q.shape
+    scale = np.sqrt(np.float64(d))
+    out = np.empty((H, Tq, vb.shape[-1]), dtype=np.float64)
+    lse = np.empty((H, Tq), dtype=np.float64)
+    for h in range(H):
+        kt = np.ascontiguousarray(kb[h].T)
+        for r0 in range(0, Tq, rows):
+            logits = (qb[h, r0:r0 + rows] @ kt) / scale
+            m = logits.max(axis=-1, keepdims=True)
+            p = np.exp(logits - m)
+            denom = p.sum(axis=-1, keepdims=True)
+            out[h, r0:r0 + rows] = (p @ vb[h]) / denom
+            lse[h, r0:r0 + rows] = (m + np.log(denom))[:, 0]
     return out, lse
 
 

@@ -1,0 +1,173 @@
+"""GPU parity: the HIP library, called through the C-ABI, against the oracle.
+
+Bar: cluster ids, codebook snapshots, packed codes and (sigma, z) are
+bit-exact; fp32 reconstruction is bit-exact (bf16 output = nearest-even
+rounding of it); attention output within 2e-2 * max(1, |O_ref|) and the same
+for LSE.  Inputs are the seeded synthetic caches of `synth`.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from parity_util import (assert_stream_equal, attention_tolerance_check, bf16_of, f32_bits,
+                         make_codec, o_attend, oracle_stream)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _encode_and_oracle(cfgs, n_list, dtype, heads=None, layer=0, codec=None, max_q=256):
+    """Encode chunks of the seeded stream; returns codec, (oracle K, oracle V), inputs."""
+    H, d = cfgs.n_heads, cfgs.head_dim
+    total = sum(n_list)
+    if codec is None:
+        codec = make_codec(H, d, cfgs.n_clusters, cfgs.n_stages, cfgs.bits, cfgs.group, iters=cfgs.iters,
+                           max_tokens=total, max_chunks=len(n_list), dtype=dtype, max_q=max_q)
+    hs = list(range(H)) if heads is None else heads
+    ost = [oracle_stream(len(hs), d, cfgs.n_clusters, cfgs.iters, cfgs.n_stages, cfgs.bits, cfgs.group,
+                         dtype) for _ in range(2)]
+    xs = [[], []]
+    t0 = 0
+    for n in n_list:
+        k = synth.kv_tokens(cfgs, layer, 0, t0, n)
+        v = synth.kv_tokens(cfgs, layer, 1, t0, n)
+        codec.encode_chunk(k.to(DEV), v.to(DEV))
+        for kv, x in ((0, k), (1, v)):
+            xn = x.float().numpy()[hs]
+            ost[kv].encode(xn)
+            xs[kv].append(xn)
+        t0 += n
+    torch.cuda.synchronize()
+    return codec, ost, [np.concatenate(x, axis=1) for x in xs]
+
+
+def test_tiny_full():
+    cfgs = synth.TINY
+    _say("tiny: encode 2x4096 fp32")
+    codec, ost, _ = _encode_and_oracle(cfgs, [4096], "f32")
+    for kv in (0, 1):
+        assert_stream_equal(codec, 0, kv, ost[kv])
+        rec = codec.reconstruct(0, 1, kv, 0, 4096)[0].cpu().numpy()
+        np.testing.assert_array_equal(f32_bits(rec), f32_bits(ost[kv].xhat()))
+        recb = codec.reconstruct(0, 1, kv, 0, 4096, out_dtype=torch.bfloat16)[0].float().cpu().numpy()
+        np.testing.assert_array_equal(f32_bits(recb), f32_bits(bf16_of(ost[kv].xhat())))
+    q = synth.queries(cfgs, 0, 256)
+    out, lse = codec.attend(0, q.to(DEV))
+    o_ref, lse_ref = o_attend.attend(q.numpy(), ost[0].xhat(), ost[1].xhat())
+    err = attention_tolerance_check(out.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+    _say(f"tiny attention max abs err {err:.3e}")
+
+
+EDGE = [
+    # name, overrides, chunk sizes, dtype
+    ("T_below_C_bf16", dict(n_heads=2, head_dim=128, n_clusters=256, group=32, tokens=100), [100], "bf16"),
+    ("int4_g64_ragged", dict(n_heads=3, head_dim=128, n_clusters=7, n_stages=1, bits=4, group=64,
+                             tokens=1000), [1000], "bf16"),
+    ("single_cluster_3stage_f32", dict(n_heads=2, head_dim=128, n_clusters=1, n_stages=3, group=32,
+                                       tokens=333), [333], "f32"),
+    ("u16_ids_4stage_d64", dict(n_heads=2, head_dim=64, n_clusters=300, n_stages=4, group=32,
+                                tokens=777), [777], "bf16"),
+    ("three_chunks_warm", dict(n_heads=2, head_dim=128, n_clusters=32, group=32, tokens=1531),
+     [1000, 530, 1], "bf16"),
+    ("no_iterations", dict(n_heads=2, head_dim=64, n_clusters=16, iters=0, group=64, tokens=500),
+     [500], "f32"),
+]
+
+
+@pytest.mark.parametrize("name,over,chunks,dtype", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(name, over, chunks, dtype):
+    base = synth.WAN_LAYER if dtype == "bf16" else synth.scaled(synth.TINY, per_token_labels=False,
+                                                                 drift=0.02)
+    cfgs = synth.scaled(base, **over)
+    _say(f"edge {name}: chunks {chunks}")
+    codec, ost, _ = _encode_and_oracle(cfgs, chunks, dtype, max_q=300)
+    total = sum(chunks)
+    assert codec.chunk_starts(0) == list(np.cumsum([0] + chunks[:-1]))
+    for kv in (0, 1):
+        assert_stream_equal(codec, 0, kv, ost[kv])
+        # a ragged window across chunk boundaries
+        t0, t1 = (total // 3, total - 1) if total > 3 else (0, total)
+        rec = codec.reconstruct(0, 1, kv, t0, t1)[0].cpu().numpy()
+        np.testing.assert_array_equal(f32_bits(rec), f32_bits(ost[kv].xhat()[:, t0:t1]))
+    q = synth.queries(synth.scaled(cfgs, q_dtype=dtype), 0, 77)
+    out, lse = codec.attend(0, q.to(DEV), out_dtype=torch.bfloat16)
+    o_ref, lse_ref = o_attend.attend(q.float().numpy(), ost[0].xhat(), ost[1].xhat())
+    attention_tolerance_check(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+
+
+def test_rewind_and_reencode():
+    cfgs = synth.scaled(synth.WAN_LAYER, n_heads=2, n_clusters=16, tokens=3000)
+    codec = make_codec(2, 128, 16, 2, 2, 32, max_tokens=3000, max_chunks=4)
+    k = synth.kv_tokens(cfgs, 0, 0, 0, 3000)
+    v = synth.kv_tokens(cfgs, 0, 1, 0, 3000)
+    codec.encode_chunk(k[:, :1000].to(DEV), v[:, :1000].to(DEV))
+    codec.encode_chunk(k[:, 1000:2000].to(DEV), v[:, 1000:2000].to(DEV))
+    codec.rewind(0, 1, 1000)
+    assert codec.chunk_starts(0) == [0]
+    codec.encode_chunk(k[:, 1000:2700].to(DEV), v[:, 1000:2700].to(DEV))
+    torch.cuda.synchronize()
+    for kv, x in ((0, k), (1, v)):
+        o = oracle_stream(2, 128, 16, 5, 2, 2, 32, "bf16")
+        o.encode(x[:, :1000].float().numpy())
+        o.encode(x[:, 1000:2700].float().numpy())
+        assert_stream_equal(codec, 0, kv, o)
+
+
+def test_multi_layer_call_matches_per_layer_oracle():
+    cfgs = synth.scaled(synth.WHOLE_CACHE, n_layers=3, n_heads=2, n_clusters=32, tokens=1200)
+    codec = make_codec(2, 128, 32, 2, 2, 32, max_tokens=1200, max_chunks=2, n_layers=3)
+    ks = torch.stack([synth.kv_tokens(cfgs, l, 0, 0, 700) for l in range(3)])
+    vs = torch.stack([synth.kv_tokens(cfgs, l, 1, 0, 700) for l in range(3)])
+    codec.encode_chunk(ks.to(DEV), vs.to(DEV))              # one call, three layers
+    ks2 = torch.stack([synth.kv_tokens(cfgs, l, 0, 700, 500) for l in range(3)])
+    vs2 = torch.stack([synth.kv_tokens(cfgs, l, 1, 700, 500) for l in range(3)])
+    codec.encode_chunk(ks2.to(DEV), vs2.to(DEV))
+    torch.cuda.synchronize()
+    rec = codec.reconstruct(0, 3, 1, 0, 1200).cpu().numpy()
+    for l in range(3):
+        for kv, (a, b) in ((0, (ks, ks2)), (1, (vs, vs2))):
+            o = oracle_stream(2, 128, 32, 5, 2, 2, 32, "bf16")
+            o.encode(a[l].float().numpy())
+            o.encode(b[l].float().numpy())
+            assert_stream_equal(codec, l, kv, o)
+            if kv == 1:
+                np.testing.assert_array_equal(f32_bits(rec[l]), f32_bits(o.xhat()))
+
+
+def test_wan_layer_full_size_sampled_heads():
+    """Full Wan-layer shape (12 heads x 32760 tokens, C=256); the oracle runs heads 0 and 7."""
+    cfgs = synth.WAN_LAYER
+    heads = [0, 7]
+    _say("wan layer: encode 12x32760x128 bf16 (K and V)")
+    codec, ost, _ = _encode_and_oracle(cfgs, [32760], "bf16", heads=heads, max_q=4680)
+    for kv in (0, 1):
+        assert_stream_equal(codec, 0, kv, ost[kv], heads=heads)
+        for oi, h in enumerate(heads):
+            rec = codec.reconstruct(0, 1, kv, 0, 32760)[0, h].cpu().numpy()
+            np.testing.assert_array_equal(f32_bits(rec), f32_bits(ost[kv].xhat()[oi]))
+    q = synth.queries(cfgs, 0, 4680)
+    out, lse = codec.attend(0, q.to(DEV))
+    sample = np.arange(0, 4680, 73)
+    o_ref, lse_ref = o_attend.attend(q.float().numpy()[heads][:, sample], ost[0].xhat(), ost[1].xhat())
+    err = attention_tolerance_check(out.cpu().numpy()[heads][:, sample], lse.cpu().numpy()[heads][:, sample],
+                                    o_ref, lse_ref)
+    _say(f"wan layer attention (sampled) max abs err {err:.3e}")
+
+
+def test_encode_is_deterministic():
+    cfgs = synth.scaled(synth.WAN_LAYER, n_heads=4, tokens=6000)
+    arenas = []
+    for _ in range(2):
+        codec = make_codec(4, 128, 256, 2, 2, 32, max_tokens=6000, max_chunks=1, max_q=0)
+        codec.arena.zero_()      # bytes the encoder never writes must not differ either
+        k = synth.kv_tokens(cfgs, 0, 0, 0, 6000).to(DEV)
+        v = synth.kv_tokens(cfgs, 0, 1, 0, 6000).to(DEV)
+        codec.encode_chunk(k, v)
+        torch.cuda.synchronize()
+        arenas.append(codec.arena.cpu())
+    assert torch.equal(arenas[0], arenas[1])

@@ -1,0 +1,60 @@
+"""GPU parity of the cross-layer residual mode (Coral-KV block-DPLR predictor).
+
+Layer 0 is coded with SAS + PRQ; each layer l >= 1 is coded as the residual
+against the prediction from the bf16 reconstruction of layer l-1.  Codes,
+(sigma, z) and the fp32 reconstruction of every layer must be bit-exact
+against the oracle chain.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import stream as o_stream
+from oracle import xlayer as o_xlayer
+from parity_util import assert_stream_equal, f32_bits, make_codec, oracle_stream
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _predictor_blob(cfgs, n_layers, rank):
+    parts = []
+    for l in range(n_layers - 1):
+        for kv in (0, 1):
+            B, U, V = synth.predictor(cfgs, l, kv, rank=rank)
+            parts += [B.reshape(-1), U.reshape(-1), V.reshape(-1)]
+    return torch.cat(parts)
+
+
+@pytest.mark.parametrize("G,S,bits", [(64, 2, 2), (64, 1, 4), (32, 2, 2)])
+def test_cross_layer_chain(G, S, bits):
+    L, H, n, r, C = 3, 4, 300, 8, 16
+    cfgs = synth.scaled(synth.WIDE_HEAD, n_layers=L, n_heads=H, tokens=n, n_clusters=C,
+                        n_stages=S, bits=bits, group=G, xlayer_rank=r)
+    blob = _predictor_blob(cfgs, L, r)
+    codec = make_codec(H, 128, C, S, bits, G, max_tokens=n, max_chunks=1, n_layers=L, max_q=0,
+                       xlayer=1, rank=r, predictor=blob.to(DEV))
+    xs = {kv: torch.stack([synth.kv_tokens(cfgs, l, kv, 0, n) for l in range(L)]) for kv in (0, 1)}
+    print(f"xlayer G={G} S={S} b={bits}: encode {L} layers", flush=True)
+    codec.encode_chunk(xs[0].to(DEV), xs[1].to(DEV))
+    torch.cuda.synchronize()
+    for kv in (0, 1):
+        rec = codec.reconstruct(0, L, kv, 0, n).cpu().numpy()
+        o0 = oracle_stream(H, 128, C, 5, S, bits, G, "bf16")
+        o0.encode(xs[kv][0].float().numpy())
+        assert_stream_equal(codec, 0, kv, o0)
+        np.testing.assert_array_equal(f32_bits(rec[0]), f32_bits(o0.xhat()))
+        prev = o0.xhat()
+        for l in range(1, L):
+            B, U, V = synth.predictor(cfgs, l - 1, kv, rank=r)
+            pred = o_xlayer.predict(prev, B.float().numpy(), U.float().numpy(), V.float().numpy())
+            ol = oracle_stream(H, 128, C, 5, S, bits, G, "bf16")
+            ol.encode_residual(xs[kv][l].float().numpy(), pred)
+            assert_stream_equal(codec, l, kv, ol, check_ids=False)
+            np.testing.assert_array_equal(f32_bits(rec[l]), f32_bits(ol.xhat()),
+                                          err_msg=f"layer {l} kv {kv}")
+            prev = ol.xhat()
+        # a later window through the chain: layers 1..2 only, tokens [50, 250)
+        part = codec.reconstruct(1, 2, kv, 50, 250).cpu().numpy()
+        np.testing.assert_array_equal(f32_bits(part), f32_bits(rec[1:, :, 50:250]))
