@@ -237,6 +237,175 @@ __global__ __launch_bounds__(256) void k_assign(EncodeArgs a) {
   }
 }
 
+// MFMA screening for bf16 caches with C <= 512.  blockIdx.x = group of
+// token tiles, y = head, z = stream; 4 waves, each owning 64 tokens of a
+// 256-token tile (four 16-token MFMA column blocks).
+//
+// The head's codebook (bf16, rows padded to the 16-row MFMA block) and
+// -||c||^2/2 are staged in LDS once per block.  For a 16-cluster block the
+// accumulator starts at -(||c||^2 + ||x||^2)/2 and v_mfma_f32_16x16x32_bf16
+// adds x.c, so acc = -D/2 (D the squared distance).  Each lane owns one token
+// column and four cluster rows; the fp32 bits of acc with the low 9 bits
+// replaced by the cluster index form a key whose unsigned order is the order
+// of D (acc <= 0 up to rounding), ties to the lowest index, and a running
+// (min, second min) of the keys is kept with v_min / v_med3.  The screening
+// error (MFMA accumulation over D+1 terms, rounding of the start value, the
+// 9 dropped bits) is below E; a token whose two best keys are within 2E goes
+// to the exact fp64 decision shared with k_assign.
+template <int D>
+__global__ __launch_bounds__(256) void k_assign_mfma(EncodeArgs a, int tiles_per_block) {
+  constexpr int KP = D + 8;                 // LDS row pitch (bf16 elements)
+  constexpr int STEPS = D / 32;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  const DevLayout &L = a.L;
+  const int C16 = (L.C + 15) & ~15;
+  uint16_t *cbs = (uint16_t *)smem;                          // [C16][KP]
+  float *cnh = (float *)(smem + size_t(C16) * KP * 2);       // [C16]
+  __shared__ uint32_t cmax_bits;
+
+  const int h = blockIdx.y, z = blockIdx.z, lrel = z >> 1, kv = z & 1;
+  uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, kv);
+  const uint16_t *x = (const uint16_t *)((kv ? a.v_in : a.k_in)) + (uint64_t(lrel) * L.H + h) * uint64_t(a.n) * D;
+  const uint16_t *cb = (const uint16_t *)(st + L.cb_off + uint64_t(a.slot) * L.cb_chunk + uint64_t(h) * L.cb_head);
+  const float *cn = (const float *)(st + L.cn_off + uint64_t(a.slot) * L.cn_chunk + uint64_t(h) * L.cn_head);
+  uint8_t *ids = st + L.ids_off + uint64_t(h) * L.ids_head;
+
+  if (threadIdx.x == 0) cmax_bits = 0;
+  __syncthreads();
+  for (int i = threadIdx.x; i < C16 * (D / 8); i += blockDim.x) {
+    const int k = i / (D / 8), c8 = i % (D / 8);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (k < L.C) v = *(const uint4 *)(cb + uint64_t(k) * D + c8 * 8);
+    *(uint4 *)(cbs + k * KP + c8 * 8) = v;
+  }
+  for (int k = threadIdx.x; k < C16; k += blockDim.x) {
+    const float c = k < L.C ? cn[k] : 0.0f;
+    cnh[k] = k < L.C ? -0.5f * c : -INFINITY;
+    if (k < L.C) atomicMax(&cmax_bits, __float_as_uint(c));
+  }
+  __syncthreads();
+  const float cmax = __uint_as_float(cmax_bits);
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const int n_tiles = (a.n + 255) / 256;
+  for (int tile = blockIdx.x * tiles_per_block; tile < min(n_tiles, (blockIdx.x + 1) * tiles_per_block); ++tile) {
+    const int tb = tile * 256 + wave * 64;
+    bf16x8 xf[4][STEPS];
+    float xnh[4], xn[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int t = tb + nt * 16 + c16;
+      float ss = 0.0f;
+#pragma unroll
+      for (int step = 0; step < STEPS; ++step) {
+        bf16x8 v;
+        if (t < a.n) {
+          v = *(const bf16x8 *)(x + uint64_t(t) * D + step * 32 + g4 * 8);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+        }
+        xf[nt][step] = v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float f = (float)v[e];
+          ss = fmaf(f, f, ss);
+        }
+      }
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      xn[nt] = ss;
+      xnh[nt] = -0.5f * ss;
+    }
+    uint32_t m1[4], m2[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) m1[nt] = m2[nt] = 0xffffffffu;
+    for (int k0 = 0; k0 < C16; k0 += 16) {
+      bf16x8 ca[STEPS];
+#pragma unroll
+      for (int step = 0; step < STEPS; ++step)
+        ca[step] = *(const bf16x8 *)(cbs + (k0 + c16) * KP + step * 32 + g4 * 8);
+      const float4 ch = *(const float4 *)(cnh + k0 + g4 * 4);
+      const uint32_t kidx = uint32_t(k0 + g4 * 4);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        floatx4 acc = {ch.x + xnh[nt], ch.y + xnh[nt], ch.z + xnh[nt], ch.w + xnh[nt]};
+#pragma unroll
+        for (int step = 0; step < STEPS; ++step)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[step], xf[nt][step], acc, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t key = (__float_as_uint(acc[r]) & ~0x1ffu) | (kidx + r);
+          const uint32_t lo = min(m1[nt], key);
+          const uint32_t mid = max(m1[nt], min(m2[nt], key));
+          m1[nt] = lo;
+          m2[nt] = mid;
+        }
+      }
+    }
+    // merge the four lanes that share a token column
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+#pragma unroll
+      for (int off = 16; off <= 32; off <<= 1) {
+        const uint32_t o1 = __shfl_xor(m1[nt], off), o2 = __shfl_xor(m2[nt], off);
+        const uint32_t n2 = min(max(m1[nt], o1), min(m2[nt], o2));
+        m1[nt] = min(m1[nt], o1);
+        m2[nt] = n2;
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int t = tb + nt * 16 + c16;
+      const bool valid = t < a.n;
+      const float d1 = -2.0f * __uint_as_float(m1[nt] & ~0x1ffu);
+      const float d2 = m2[nt] == 0xffffffffu ? INFINITY : -2.0f * __uint_as_float(m2[nt] & ~0x1ffu);
+      const float E = float(D + 16) * 0x1p-22f * (xn[nt] + cmax) + 0x1p-12f * (fabsf(d1) + fabsf(d2));
+      const bool flag = valid && g4 == 0 && !(d2 - d1 > 2.0f * E);
+      int k1 = int(m1[nt] & 0x1ffu);
+      uint64_t fm = __ballot(flag);
+      while (fm) {
+        const int src = __ffsll((unsigned long long)fm) - 1;
+        fm &= fm - 1;
+        const int tf = tb + nt * 16 + (src & 15);
+        const uint16_t *xrow = x + uint64_t(tf) * D;
+        double best = INFINITY;
+        int bk = 0x7fffffff;
+        for (int k = lane; k < L.C; k += 64) {
+          const uint16_t *crow = cbs + k * KP;      // codebook row in LDS
+          double dd = 0.0;
+          for (int j8 = 0; j8 < D / 8; ++j8) {
+            const uint4 xv = *(const uint4 *)(xrow + j8 * 8);
+            const uint4 cv = *(const uint4 *)(crow + j8 * 8);
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, cw[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t xb = (xw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+              const uint32_t cbb = (cw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+              const double diff = double(bf16_to_f32(xb)) - double(bf16_to_f32(cbb));
+              dd = dd + diff * diff;
+            }
+          }
+          if (dd < best) { best = dd; bk = k; }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          const double ob = __shfl_xor(best, off);
+          const int ok = __shfl_xor(bk, off);
+          if (ob < best || (ob == best && ok < bk)) { best = ob; bk = ok; }
+        }
+        if (lane == src) k1 = bk;
+      }
+      if (valid && g4 == 0) {
+        const int64_t tt = int64_t(a.t0) + t;
+        if (L.id_bytes == 1) ids[tt] = uint8_t(k1);
+        else ((uint16_t *)ids)[tt] = uint16_t(k1);
+      }
+    }
+  }
+}
+
 // One wave per 4 clusters; blockIdx.x = group of 16 clusters, y = head, z = stream.
 // Each wave scans the call's ids in token order and adds the member rows in
 // fp64 (lane = D/64 channels), so every centroid sum is the sequential sum in
@@ -267,62 +436,99 @@ __device__ __forceinline__ void finalize_centroid(uint8_t *cb, float *cn, int k,
   if (lane == 0) cn[k] = float(nrm);
 }
 
+// Block = 16 waves, one cluster each (blockIdx.x = group of 16 clusters,
+// y = head, z = stream).  The block stages a segment of the call's ids in LDS;
+// each wave scans it in token order, appending its cluster's member token
+// indices to a list in LDS; a full list (or the end of the ids) is drained by
+// summing the listed rows in list order with UPD_UNROLL row loads in flight,
+// so every centroid sum is the sequential fp64 sum in token order.
+constexpr int UPD_SEG = 16384;      // ids staged per pass
+constexpr int UPD_CAP = 512;        // list entries per cluster
+constexpr int UPD_UNROLL = 32;
+
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void k_update(EncodeArgs a) {
+__device__ __forceinline__ void drain_list(const uint8_t *x, const int32_t *list, int count, double *acc,
+                                           int lane) {
   constexpr int EB = BF16 ? 2 : 4;
   constexpr int CPL = D / 64;
+  for (int i = 0; i < count; i += UPD_UNROLL) {
+    float v[UPD_UNROLL][CPL];
+#pragma unroll
+    for (int e = 0; e < UPD_UNROLL; ++e) {
+      const int row = list[min(i + e, count - 1)];   // tail: reload the last row, not added
+      const uint8_t *rp = x + uint64_t(row) * D * EB;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) v[e][c] = load_elem<BF16>(rp, lane * CPL + c);
+    }
+#pragma unroll
+    for (int e = 0; e < UPD_UNROLL; ++e) {
+      if (i + e < count) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) acc[c] = acc[c] + double(v[e][c]);
+      }
+    }
+  }
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(1024) void k_update(EncodeArgs a) {
+  constexpr int EB = BF16 ? 2 : 4;
+  constexpr int CPL = D / 64;
+  __shared__ __attribute__((aligned(16))) uint8_t sid_raw[UPD_SEG * 2];
+  __shared__ int32_t lists[16][UPD_CAP];
   const DevLayout &L = a.L;
   const int h = blockIdx.y, z = blockIdx.z, lrel = z >> 1, kv = z & 1;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int kb = blockIdx.x * 16 + wave * 4;
-  if (kb >= L.C) return;  // whole wave exits together
+  const int k = blockIdx.x * 16 + wave;
   uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, kv);
   const uint8_t *x = (kv ? a.v_in : a.k_in) + (uint64_t(lrel) * L.H + h) * uint64_t(a.n) * D * EB;
   const uint8_t *ids = st + L.ids_off + uint64_t(h) * L.ids_head + uint64_t(a.t0) * L.id_bytes;
   uint8_t *cb = st + L.cb_off + uint64_t(a.slot) * L.cb_chunk + uint64_t(h) * L.cb_head;
   float *cn = (float *)(st + L.cn_off + uint64_t(a.slot) * L.cn_chunk + uint64_t(h) * L.cn_head);
 
-  double acc0[CPL], acc1[CPL], acc2[CPL], acc3[CPL];
+  double acc[CPL];
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) acc0[c] = acc1[c] = acc2[c] = acc3[c] = 0.0;
-  int n0 = 0, n1 = 0, n2 = 0, n3 = 0;
-  for (int base = 0; base < a.n; base += 64) {
-    const int t = base + lane;
-    const int myid = t < a.n ? load_id(ids, L.id_bytes, t) : -1;
-    const uint64_t m0 = __ballot(myid == kb), m1 = __ballot(myid == kb + 1);
-    const uint64_t m2 = __ballot(myid == kb + 2), m3 = __ballot(myid == kb + 3);
-    uint64_t all = m0 | m1 | m2 | m3;
-    while (all) {
-      const int b = __ffsll((unsigned long long)all) - 1;
-      all &= all - 1;
-      const uint64_t bit = uint64_t(1) << b;
-      const uint8_t *row = x + uint64_t(base + b) * D * EB;
-      double v[CPL];
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) v[c] = double(load_elem<BF16>(row, lane * CPL + c));
-      if (m0 & bit) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) acc0[c] = acc0[c] + v[c];
-        ++n0;
-      } else if (m1 & bit) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) acc1[c] = acc1[c] + v[c];
-        ++n1;
-      } else if (m2 & bit) {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) acc2[c] = acc2[c] + v[c];
-        ++n2;
-      } else {
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) acc3[c] = acc3[c] + v[c];
-        ++n3;
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.0;
+  int cnt = 0, fill = 0;              // wave-uniform
+  int32_t *list = &lists[wave][0];
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+
+  for (int seg0 = 0; seg0 < a.n; seg0 += UPD_SEG) {
+    const int segn = min(UPD_SEG, a.n - seg0);
+    __syncthreads();
+    // stage the segment's ids (bytes; ids start on any byte, so copy bytewise
+    // when unaligned, else 16 bytes at a time)
+    const int nbytes = segn * L.id_bytes;
+    const uint8_t *src = ids + uint64_t(seg0) * L.id_bytes;
+    if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+      for (int i = threadIdx.x; i < nbytes / 16; i += blockDim.x)
+        *(uint4 *)(sid_raw + 16 * i) = *(const uint4 *)(src + 16 * i);
+      for (int i = (nbytes / 16) * 16 + threadIdx.x; i < nbytes; i += blockDim.x) sid_raw[i] = src[i];
+    } else {
+      for (int i = threadIdx.x; i < nbytes; i += blockDim.x) sid_raw[i] = src[i];
+    }
+    __syncthreads();
+    if (k < L.C) {
+      for (int w0 = 0; w0 < segn; w0 += 64) {
+        const int t = w0 + lane;
+        int myid = -1;
+        if (t < segn) myid = L.id_bytes == 1 ? int(sid_raw[t]) : int(((const uint16_t *)sid_raw)[t]);
+        const uint64_t m = __ballot(myid == k);
+        if (m == 0) continue;
+        const int nm = __popcll(m);
+        if (fill + nm > UPD_CAP) {
+          drain_list<D, BF16>(x, list, fill, acc, lane);
+          fill = 0;
+        }
+        if ((m >> lane) & 1) list[fill + __popcll(m & below)] = seg0 + t;
+        fill += nm;
+        cnt += nm;
       }
     }
   }
-  finalize_centroid<D, BF16>(cb, cn, kb + 0, L.C, n0, acc0, lane);
-  finalize_centroid<D, BF16>(cb, cn, kb + 1, L.C, n1, acc1, lane);
-  finalize_centroid<D, BF16>(cb, cn, kb + 2, L.C, n2, acc2, lane);
-  finalize_centroid<D, BF16>(cb, cn, kb + 3, L.C, n3, acc3, lane);
+  if (k >= L.C) return;
+  if (fill) drain_list<D, BF16>(x, list, fill, acc, lane);
+  finalize_centroid<D, BF16>(cb, cn, k, L.C, cnt, acc, lane);
 }
 
 // One thread per (token, group).  blockIdx.x = tile of 256 (token, group)
@@ -694,6 +900,313 @@ __global__ __launch_bounds__(256) void k_attend(AttnArgs a) {
   }
 }
 
+// Attention, version used by qkv_attend: block = 8 waves (two per SIMD, so
+// one wave's MFMA overlaps the other's softmax/dequant VALU work) = 256
+// queries of one head, 32 per wave; grid = (query blocks, heads, KV splits).
+// Tiles of 64 keys are rebuilt in bf16 into a double-buffered LDS tile (K as
+// [key][d], V transposed as [d][key]): one (tensor, key, group) item per
+// thread.  Loads are software-pipelined: the cluster ids of tile i+2 and the
+// packed data (codes, scale/zero, centroid rows) of tile i+1 are in flight
+// while tile i is multiplied.  The chunk table is cached in LDS.
+constexpr int AT_WAVES = 8;
+constexpr int AT_BQ = 32 * AT_WAVES;
+constexpr int AT_BK = 64;
+
+template <int WORDS, int CV, int SMAX>
+struct TileRegs {                 // packed inputs of one (tensor, key, group) item
+  uint32_t codes[SMAX][WORDS];    // S stages of G codes
+  uint32_t meta[SMAX];            // (sigma, z) fp16 pairs
+  uint4 cent[CV];                 // the centroid slice: G values of the cache dtype
+};
+
+__device__ __forceinline__ int chunk_of_lds(const int32_t *starts, int n_chunks, int t) {
+  int lo = 0, hi = n_chunks - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (starts[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int D, int G, int BITS, bool CB_BF16>
+__global__ __launch_bounds__(512, 1) void k_attend2(AttnArgs a) {
+  constexpr int NG = D / G;
+  constexpr int NI = AT_BK * NG;           // items per tensor per tile
+  constexpr int KP = D + 8;
+  constexpr int VP = AT_BK + 8;
+  constexpr int WORDS = G * BITS / 32;
+  constexpr int EB = CB_BF16 ? 2 : 4;
+  constexpr int CV = G * EB / 16;          // uint4 per centroid slice
+  constexpr int SMAX = 4;
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  static_assert(2 * NI <= 512, "one item per thread");
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][AT_BK * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VP];
+  __shared__ int32_t starts_s[kMaxChunks + 1];
+  __shared__ int32_t nch_s;
+
+  const DevLayout &L = a.L;
+  const int h = blockIdx.y, split = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const float sc = 1.4426950408889634f / sqrtf(float(D));
+
+  // my item: tensor (0 = K, 1 = V), key within the tile, group
+  const bool has_item = tid < 2 * NI;
+  const int it_kv = tid / NI, it_rem = tid % NI;
+  const int it_key = it_rem / NG, it_g = it_rem % NG;
+  const uint8_t *st = it_kv ? a.stream_v : a.stream_k;
+  const uint8_t *idp = st + L.ids_off + uint64_t(h) * L.ids_head;
+
+  if (tid == 0) nch_s = ((const StreamHeader *)(a.stream_k + L.header_off))->n_chunks;
+  __syncthreads();
+  for (int i = tid; i < nch_s; i += blockDim.x)
+    starts_s[i] = ((const StreamHeader *)(a.stream_k + L.header_off))->start[i];
+
+  const int ks = split * a.split_len;
+  const int ke = min(a.n_keys, ks + a.split_len);
+  const int n_tiles = ke > ks ? (ke - ks + AT_BK - 1) / AT_BK : 0;
+
+  // queries
+  bf16x8 qf[2][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int q = blockIdx.x * AT_BQ + wave * 32 + qb * 16 + c16;
+#pragma unroll
+    for (int step = 0; step < D / 32; ++step) {
+      bf16x8 v;
+      if (q < a.n_q) {
+        const uint64_t off = (uint64_t(h) * a.n_q + q) * D + step * 32 + g4 * 8;
+        if (a.q_bf16) {
+          v = *(const bf16x8 *)((const uint16_t *)a.q + off);
+        } else {
+          const float *qp = (const float *)a.q + off;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)qp[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+      }
+      qf[qb][step] = v;
+    }
+  }
+  floatx4 o[D / 16][2];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) o[db][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+  // ---- software pipeline over tiles
+  auto load_id = [&](int tile) -> int {
+    const int t = ks + tile * AT_BK + it_key;
+    if (!has_item || tile >= n_tiles || t >= ke) return -1;
+    return L.id_bytes == 1 ? int(idp[t]) : int(((const uint16_t *)idp)[t]);
+  };
+  TileRegs<WORDS, CV, SMAX> R;
+  auto load_data = [&](int tile, int id) {
+    const int t = ks + tile * AT_BK + it_key;
+    if (id < 0) return;
+    const int slot = chunk_of_lds(starts_s, nch_s, t);
+    const uint8_t *crow = st + L.cb_off + uint64_t(slot) * L.cb_chunk + uint64_t(h) * L.cb_head +
+                          uint64_t(id) * D * EB + uint64_t(it_g) * G * EB;
+#pragma unroll
+    for (int i = 0; i < CV; ++i) R.cent[i] = *(const uint4 *)(crow + 16 * i);
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) {
+      if (s < L.S) {
+        const uint8_t *cp = st + L.codes_off + uint64_t(s) * L.codes_stage + uint64_t(h) * L.codes_head +
+                            uint64_t(t) * L.codes_token + uint64_t(it_g) * (G * BITS / 8);
+        if constexpr (WORDS == 2) {
+          const uint2 v = *(const uint2 *)cp;
+          R.codes[s][0] = v.x; R.codes[s][1] = v.y;
+        } else {
+#pragma unroll
+          for (int w = 0; w < WORDS; w += 4) {
+            const uint4 v = *(const uint4 *)(cp + 4 * w);
+            R.codes[s][w] = v.x; R.codes[s][w + 1] = v.y; R.codes[s][w + 2] = v.z; R.codes[s][w + 3] = v.w;
+          }
+        }
+        R.meta[s] = *((const uint32_t *)(st + L.meta_off + uint64_t(s) * L.meta_stage +
+                                         uint64_t(h) * L.meta_head + uint64_t(t) * L.meta_token) + it_g);
+      }
+    }
+  };
+  auto dequant_store = [&](int buf, int id) {
+    if (!has_item) return;
+    float xh[G];
+    if (id >= 0) {
+#pragma unroll
+      for (int i = 0; i < CV; ++i) {
+        const uint32_t w4[4] = {R.cent[i].x, R.cent[i].y, R.cent[i].z, R.cent[i].w};
+        if constexpr (CB_BF16) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xh[i * 8 + e] = bf16_to_f32((w4[e >> 1] >> (16 * (e & 1))) & 0xffffu);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xh[i * 4 + e] = __uint_as_float(w4[e]);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < SMAX; ++s) {
+        if (s < L.S) {
+          const float sf = f16_bits_to_f32(uint16_t(R.meta[s] & 0xffffu));
+          const float zf = f16_bits_to_f32(uint16_t(R.meta[s] >> 16));
+#pragma unroll
+          for (int j = 0; j < G; ++j) {
+            const float q = float((R.codes[s][(j * BITS) / 32] >> ((j * BITS) % 32)) & MASK);
+            xh[j] = xh[j] + fmaf(q, sf, zf);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < G; ++j) xh[j] = 0.0f;
+    }
+    if (it_kv == 0) {
+      uint16_t *dst = &Ks[buf][it_key * KP + it_g * G];
+#pragma unroll
+      for (int j = 0; j < G; j += 8) {
+        uint4 v;
+        v.x = uint32_t(f32_to_bf16_bits(xh[j])) | (uint32_t(f32_to_bf16_bits(xh[j + 1])) << 16);
+        v.y = uint32_t(f32_to_bf16_bits(xh[j + 2])) | (uint32_t(f32_to_bf16_bits(xh[j + 3])) << 16);
+        v.z = uint32_t(f32_to_bf16_bits(xh[j + 4])) | (uint32_t(f32_to_bf16_bits(xh[j + 5])) << 16);
+        v.w = uint32_t(f32_to_bf16_bits(xh[j + 6])) | (uint32_t(f32_to_bf16_bits(xh[j + 7])) << 16);
+        *(uint4 *)(dst + j) = v;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < G; ++j) Vt[buf][(it_g * G + j) * VP + it_key] = f32_to_bf16_bits(xh[j]);
+    }
+  };
+
+  __syncthreads();  // chunk table in LDS
+  int id_cur = load_id(0);
+  int id_next = load_id(1);
+  load_data(0, id_cur);
+  dequant_store(0, id_cur);
+  __syncthreads();
+
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int buf = tile & 1;
+    const int kt0 = ks + tile * AT_BK;
+    // prefetch: data of tile+1, ids of tile+2
+    load_data(tile + 1, id_next);
+    const int id_after = load_id(tile + 2);
+
+    floatx4 s[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int step = 0; step < D / 32; ++step) {
+        const bf16x8 ka = *(const bf16x8 *)&Ks[buf][(kb * 16 + c16) * KP + step * 32 + g4 * 8];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qb][step], s[kb][qb], 0, 0, 0);
+      }
+    }
+    const bool full = kt0 + AT_BK <= ke;
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float sv[4][4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = s[kb][qb][r] * sc;
+          if (!full && kt0 + kb * 16 + g4 * 4 + r >= ke) v = -INFINITY;
+          sv[kb][r] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mnew = fmaxf(m_run[qb], tmax);
+      const float alpha = exp2f(m_run[qb] - mnew);
+      float rs = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = exp2f(sv[kb][r] - mnew);
+          sv[kb][r] = p;
+          rs += p;
+        }
+      rs += __shfl_xor(rs, 16);
+      rs += __shfl_xor(rs, 32);
+      l_run[qb] = l_run[qb] * alpha + rs;
+      m_run[qb] = mnew;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) o[db][qb] *= alpha;
+#pragma unroll
+      for (int st2 = 0; st2 < 2; ++st2) {
+        bf16x8 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = (__bf16)sv[2 * st2][r];
+          v[4 + r] = (__bf16)sv[2 * st2 + 1][r];
+        }
+        pb[qb][st2] = v;
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+#pragma unroll
+      for (int st2 = 0; st2 < 2; ++st2) {
+        const uint16_t *vr = &Vt[buf][(db * 16 + c16) * VP + st2 * 32 + g4 * 4];
+        const bf16x4 lo = *(const bf16x4 *)vr;
+        const bf16x4 hi = *(const bf16x4 *)(vr + 16);
+        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qb][st2], o[db][qb], 0, 0, 0);
+      }
+    }
+    // rebuild tile+1 into the other buffer
+    if (tile + 1 < n_tiles) dequant_store(buf ^ 1, id_next);
+    id_next = id_after;
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int q = blockIdx.x * AT_BQ + wave * 32 + qb * 16 + c16;
+    if (q >= a.n_q) continue;
+    const bool empty = l_run[qb] == 0.0f;
+    const float inv_l = empty ? 0.0f : 1.0f / l_run[qb];
+    const float lse = empty ? -INFINITY : (m_run[qb] + log2f(l_run[qb])) * 0.6931471805599453f;
+    if (a.n_splits == 1) {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const uint64_t off = (uint64_t(h) * a.n_q + q) * D + db * 16 + g4 * 4;
+        const floatx4 v = o[db][qb] * inv_l;
+        if (a.out_bf16) {
+          uint16_t *op = (uint16_t *)a.out + off;
+          const uint32_t p0 = uint32_t(f32_to_bf16_bits(v[0])) | (uint32_t(f32_to_bf16_bits(v[1])) << 16);
+          const uint32_t p1 = uint32_t(f32_to_bf16_bits(v[2])) | (uint32_t(f32_to_bf16_bits(v[3])) << 16);
+          *(uint2 *)op = make_uint2(p0, p1);
+        } else {
+          *(float4 *)((float *)a.out + off) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+      if (a.lse && g4 == 0) a.lse[uint64_t(h) * a.n_q + q] = lse;
+    } else {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const uint64_t off = ((uint64_t(split) * L.H + h) * a.n_q + q) * D + db * 16 + g4 * 4;
+        const floatx4 v = o[db][qb] * inv_l;
+        *(float4 *)(a.part_o + off) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      if (g4 == 0) a.part_lse[(uint64_t(split) * L.H + h) * a.n_q + q] = lse;
+    }
+  }
+}
+
 // Merge split partials: O = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - max).
 // One thread per (query, channel); blockIdx.y = head.
 __global__ __launch_bounds__(256) void k_attend_merge(AttnArgs a) {
@@ -791,11 +1304,24 @@ static void launch_init_t(const EncodeArgs &a, int streams, hipStream_t st) {
 }
 template <int D, bool BF>
 static void launch_assign_t(const EncodeArgs &a, int streams, hipStream_t st) {
+  if (BF && a.L.C <= 512) {
+    // MFMA screening; about four 256-token tiles per block so that the
+    // codebook is staged in LDS once per 1024 tokens
+    const int n_tiles = int(cdiv(a.n, 256));
+    const int per_block = n_tiles >= 16 ? 4 : 1;
+    const int C16 = (a.L.C + 15) & ~15;
+    const size_t lds = size_t(C16) * (D + 8) * 2 + size_t(C16) * 4;
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_assign_mfma<D>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    hipLaunchKernelGGL((k_assign_mfma<D>), dim3(cdiv(n_tiles, per_block), a.L.H, streams), dim3(256), lds, st,
+                       a, per_block);
+    return;
+  }
   hipLaunchKernelGGL((k_assign<D, BF>), dim3(cdiv(a.n, 256), a.L.H, streams), dim3(256), 0, st, a);
 }
 template <int D, bool BF>
 static void launch_update_t(const EncodeArgs &a, int streams, hipStream_t st) {
-  hipLaunchKernelGGL((k_update<D, BF>), dim3(cdiv(a.L.C, 16), a.L.H, streams), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_update<D, BF>), dim3(cdiv(a.L.C, 16), a.L.H, streams), dim3(1024), 0, st, a);
 }
 
 template <int D, int G, int BITS, bool BF>
@@ -815,7 +1341,7 @@ static void launch_recon_t(const ReconArgs &a, int n_layers, int64_t out_tokens,
 
 template <int D, int G, int BITS, bool BF>
 static void launch_attend_t(const AttnArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((k_attend<D, G, BITS, BF>), dim3(cdiv(a.n_q, ATT_BQ), a.L.H, a.n_splits), dim3(256),
+  hipLaunchKernelGGL((k_attend2<D, G, BITS, BF>), dim3(cdiv(a.n_q, AT_BQ), a.L.H, a.n_splits), dim3(512),
                      0, st, a);
 }
 

@@ -161,11 +161,13 @@ int check_rewind(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int64_t n
 }
 
 int attention_splits(const Plan &p, int64_t n_keys, int64_t n_q) {
-  const int64_t q_blocks = (n_q + 127) / 128;
+  // blocks of 256 queries; aim for about two blocks per compute unit (256
+  // CUs) while keeping at least 8 key tiles of 64 per split
+  const int64_t q_blocks = (n_q + 255) / 256;
   const int64_t base = int64_t(p.cfg.n_heads) * q_blocks;
-  int64_t splits = (1024 + base - 1) / base;
+  int64_t splits = (512 + base - 1) / base;
   splits = std::min<int64_t>(splits, kMaxSplits);
-  splits = std::min<int64_t>(splits, (n_keys + 255) / 256);
+  splits = std::min<int64_t>(splits, (n_keys + 511) / 512);
   return int(std::max<int64_t>(splits, 1));
 }
 
