@@ -74,6 +74,9 @@ extern "C" int qkv_encode_chunk(qkv_ctx *ctx, int32_t layer0, int32_t n_layers, 
   a.t0 = int32_t(t0);
   a.slot = slot;
   a.prev_slot = slot - 1;
+  a.sort_perm = scratch(ctx, p.sort_perm_off);
+  a.sort_off = reinterpret_cast<uint16_t *>(scratch(ctx, p.sort_off_off));
+  a.sort_tiles = int32_t(p.sort_tiles);
   const uint64_t layer_bytes = uint64_t(c.n_heads) * uint64_t(n) * c.head_dim * p.kv_elem_bytes;
   const uint8_t *kin = static_cast<const uint8_t *>(d_k);
   const uint8_t *vin = static_cast<const uint8_t *>(d_v);

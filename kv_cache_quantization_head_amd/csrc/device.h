@@ -53,6 +53,10 @@ struct EncodeArgs {
   // written to chain (both [2][H][n][D], f32 / bf16)
   const float *pred;
   uint16_t *chain;
+  // k-means update: per-tile stable sort of the ids
+  uint8_t *sort_perm;           // [streams][H][tiles][256] u8 token offsets sorted by (id, t)
+  uint16_t *sort_off;           // [streams][H][tiles][C+1] start of each cluster in the tile
+  int32_t sort_tiles;           // tile stride of the two arrays
 };
 
 struct ReconArgs {

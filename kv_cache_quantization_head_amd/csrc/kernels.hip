@@ -318,9 +318,9 @@ __global__ __launch_bounds__(256) void k_assign_mfma(EncodeArgs a, int tiles_per
       xn[nt] = ss;
       xnh[nt] = -0.5f * ss;
     }
-    uint32_t m1[4], m2[4];
+    uint32_t m1[4], m2[4], m3[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) m1[nt] = m2[nt] = 0xffffffffu;
+    for (int nt = 0; nt < 4; ++nt) m1[nt] = m2[nt] = m3[nt] = 0xffffffffu;
     for (int k0 = 0; k0 < C16; k0 += 16) {
       bf16x8 ca[STEPS];
 #pragma unroll
@@ -337,34 +337,85 @@ __global__ __launch_bounds__(256) void k_assign_mfma(EncodeArgs a, int tiles_per
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const uint32_t key = (__float_as_uint(acc[r]) & ~0x1ffu) | (kidx + r);
-          const uint32_t lo = min(m1[nt], key);
-          const uint32_t mid = max(m1[nt], min(m2[nt], key));
-          m1[nt] = lo;
-          m2[nt] = mid;
+          const uint32_t n3 = max(m2[nt], min(m3[nt], key));
+          const uint32_t n2 = max(m1[nt], min(m2[nt], key));
+          m1[nt] = min(m1[nt], key);
+          m2[nt] = n2;
+          m3[nt] = n3;
         }
       }
     }
-    // merge the four lanes that share a token column
+    // merge the sorted triples of the four lanes that share a token column
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
 #pragma unroll
       for (int off = 16; off <= 32; off <<= 1) {
-        const uint32_t o1 = __shfl_xor(m1[nt], off), o2 = __shfl_xor(m2[nt], off);
-        const uint32_t n2 = min(max(m1[nt], o1), min(m2[nt], o2));
-        m1[nt] = min(m1[nt], o1);
-        m2[nt] = n2;
+        const uint32_t b1 = __shfl_xor(m1[nt], off), b2 = __shfl_xor(m2[nt], off), b3 = __shfl_xor(m3[nt], off);
+        const uint32_t r3 = min(min(m3[nt], b3), min(max(m2[nt], b1), max(m1[nt], b2)));
+        const uint32_t r2 = min(max(m1[nt], b1), min(m2[nt], b2));
+        m1[nt] = min(m1[nt], b1);
+        m2[nt] = r2;
+        m3[nt] = r3;
       }
     }
+    auto decode = [](uint32_t m) {
+      return m == 0xffffffffu ? INFINITY : -2.0f * __uint_as_float(m & ~0x1ffu);
+    };
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int t = tb + nt * 16 + c16;
-      const bool valid = t < a.n;
-      const float d1 = -2.0f * __uint_as_float(m1[nt] & ~0x1ffu);
-      const float d2 = m2[nt] == 0xffffffffu ? INFINITY : -2.0f * __uint_as_float(m2[nt] & ~0x1ffu);
-      const float E = float(D + 16) * 0x1p-22f * (xn[nt] + cmax) + 0x1p-12f * (fabsf(d1) + fabsf(d2));
-      const bool flag = valid && g4 == 0 && !(d2 - d1 > 2.0f * E);
-      int k1 = int(m1[nt] & 0x1ffu);
-      uint64_t fm = __ballot(flag);
+      const bool valid = t < a.n && g4 == 0;
+      const float d1 = decode(m1[nt]), d2 = decode(m2[nt]), d3 = decode(m3[nt]);
+      const float E = float(D + 16) * 0x1p-22f * (xn[nt] + cmax) +
+                      0x1p-12f * fmaxf(fabsf(d1), fmaxf(d2 == INFINITY ? 0.0f : fabsf(d2),
+                                                        d3 == INFINITY ? 0.0f : fabsf(d3)));
+      const int k1 = int(m1[nt] & 0x1ffu), k2 = int(m2[nt] & 0x1ffu);
+      // decided by the screen / exact check of the two best / exact check of all
+      const bool pair = valid && !(d2 - d1 > 2.0f * E) && (d3 - d1 > 2.0f * E);
+      const bool full = valid && !(d2 - d1 > 2.0f * E) && !(d3 - d1 > 2.0f * E);
+      int kbest = k1;
+      const uint64_t pm = __ballot(pair);
+      if (pm) {
+        // lane 2j / 2j+1 computes the exact distance of the j-th pair token to k1 / k2
+        const int np = __popcll(pm);
+        const int mine = pair ? __popcll(pm & ((uint64_t(1) << lane) - 1)) : -1;
+        int src_lane = -1;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const uint64_t has = __ballot(mine == j);
+          if (has && lane / 2 == j) src_lane = __ffsll((unsigned long long)has) - 1;
+        }
+        const int sl = lane < 2 * np ? src_lane : 0;
+        const int tok_c16 = __shfl(c16, sl);
+        // both shuffles run on every lane (a shuffle under a divergent select
+        // would read the select taken by the source lane)
+        const int s_k1 = __shfl(k1, sl), s_k2 = __shfl(k2, sl);
+        const int cand = (lane & 1) ? s_k2 : s_k1;
+        double dd = INFINITY;
+        if (lane < 2 * np) {
+          const uint16_t *xrow = x + uint64_t(tb + nt * 16 + tok_c16) * D;
+          const uint16_t *crow = cbs + cand * KP;
+          dd = 0.0;
+          for (int j8 = 0; j8 < D / 8; ++j8) {
+            const uint4 xv = *(const uint4 *)(xrow + j8 * 8);
+            const uint4 cv = *(const uint4 *)(crow + j8 * 8);
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, cw[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t xb = (xw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+              const uint32_t cbb = (cw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+              const double diff = double(bf16_to_f32(xb)) - double(bf16_to_f32(cbb));
+              dd = dd + diff * diff;
+            }
+          }
+        }
+        const double od = __shfl_xor(dd, 1);
+        const int oc = __shfl_xor(cand, 1);
+        const int win = (dd < od || (dd == od && cand < oc)) ? cand : oc;
+        const int got = __shfl(win, 2 * (mine < 0 ? 0 : mine));
+        if (pair) kbest = got;
+      }
+      uint64_t fm = __ballot(full);
       while (fm) {
         const int src = __ffsll((unsigned long long)fm) - 1;
         fm &= fm - 1;
@@ -395,12 +446,12 @@ __global__ __launch_bounds__(256) void k_assign_mfma(EncodeArgs a, int tiles_per
           const int ok = __shfl_xor(bk, off);
           if (ob < best || (ob == best && ok < bk)) { best = ob; bk = ok; }
         }
-        if (lane == src) k1 = bk;
+        if (lane == src) kbest = bk;
       }
-      if (valid && g4 == 0) {
+      if (valid) {
         const int64_t tt = int64_t(a.t0) + t;
-        if (L.id_bytes == 1) ids[tt] = uint8_t(k1);
-        else ((uint16_t *)ids)[tt] = uint16_t(k1);
+        if (L.id_bytes == 1) ids[tt] = uint8_t(kbest);
+        else ((uint16_t *)ids)[tt] = uint16_t(kbest);
       }
     }
   }
@@ -527,6 +578,110 @@ __global__ __launch_bounds__(1024) void k_update(EncodeArgs a) {
     }
   }
   if (k >= L.C) return;
+  if (fill) drain_list<D, BF16>(x, list, fill, acc, lane);
+  finalize_centroid<D, BF16>(cb, cn, k, L.C, cnt, acc, lane);
+}
+
+// Stable sort of one 256-token tile of a call's ids (blockIdx.x = tile,
+// y = head, z = stream): keys (id << 8 | offset) are bitonic-sorted in LDS;
+// the tile's permutation (offsets in (id, token) order) and, for every
+// cluster k in [0, C], the position of its first member are written out.
+__global__ __launch_bounds__(256) void k_tile_sort(EncodeArgs a) {
+  __shared__ uint32_t keys[256];
+  const DevLayout &L = a.L;
+  const int tile = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
+  const uint8_t *st = stream_ptr(a.arena, L, a.layer0 + (z >> 1), z & 1);
+  const uint8_t *ids = st + L.ids_off + uint64_t(h) * L.ids_head + uint64_t(a.t0) * L.id_bytes;
+  const int i = threadIdx.x;
+  const int t = tile * 256 + i;
+  keys[i] = t < a.n ? (uint32_t(load_id(ids, L.id_bytes, t)) << 8) | uint32_t(i) : 0xffffffffu;
+  __syncthreads();
+  for (int size = 2; size <= 256; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const int j = i ^ stride;
+      if (j > i) {
+        const uint32_t u = keys[i], v = keys[j];
+        const bool up = (i & size) == 0;
+        if ((u > v) == up) { keys[i] = v; keys[j] = u; }
+      }
+      __syncthreads();
+    }
+  }
+  const uint64_t unit = (uint64_t(z) * L.H + h) * uint64_t(a.sort_tiles) + tile;
+  a.sort_perm[unit * 256 + i] = uint8_t(keys[i] & 0xffu);
+  uint16_t *off = a.sort_off + unit * uint64_t(L.C + 1);
+  for (int k = i; k <= L.C; k += blockDim.x) {
+    const uint32_t target = uint32_t(k) << 8;
+    int lo = 0, hi = 256;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (keys[mid] < target) lo = mid + 1; else hi = mid;
+    }
+    off[k] = uint16_t(lo);
+  }
+}
+
+// k-means update from the tile sort: one wave per cluster (blockIdx.x = group
+// of 4 clusters, y = head, z = stream).  Lanes read the cluster's member range
+// of 64 tiles at a time; a wave prefix sum lays the members out in token order
+// (tiles ascending, offsets ascending inside a tile) in an LDS list, drained
+// with UPD_UNROLL row loads in flight: the sum is the sequential fp64 sum in
+// token order.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_update_sorted(EncodeArgs a) {
+  constexpr int EB = BF16 ? 2 : 4;
+  constexpr int CPL = D / 64;
+  __shared__ int32_t lists[4][UPD_CAP];
+  const DevLayout &L = a.L;
+  const int h = blockIdx.y, z = blockIdx.z, lrel = z >> 1, kv = z & 1;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int k = blockIdx.x * 4 + wave;
+  if (k >= L.C) return;  // whole wave; no block barrier below
+  uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, kv);
+  const uint8_t *x = (kv ? a.v_in : a.k_in) + (uint64_t(lrel) * L.H + h) * uint64_t(a.n) * D * EB;
+  uint8_t *cb = st + L.cb_off + uint64_t(a.slot) * L.cb_chunk + uint64_t(h) * L.cb_head;
+  float *cn = (float *)(st + L.cn_off + uint64_t(a.slot) * L.cn_chunk + uint64_t(h) * L.cn_head);
+  const uint64_t unit0 = (uint64_t(z) * L.H + h) * uint64_t(a.sort_tiles);
+  const uint8_t *perm = a.sort_perm + unit0 * 256;
+  const uint16_t *off = a.sort_off + unit0 * uint64_t(L.C + 1);
+  int32_t *list = &lists[wave][0];
+
+  double acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.0;
+  int cnt = 0, fill = 0;  // wave-uniform
+  const int n_tiles = (a.n + 255) / 256;
+  for (int tc = 0; tc < n_tiles; tc += 64) {
+    const int tile = tc + lane;
+    int beg = 0, num = 0;
+    if (tile < n_tiles) {
+      const uint16_t *o = off + uint64_t(tile) * (L.C + 1);
+      beg = o[k];
+      num = int(o[k + 1]) - beg;
+    }
+    int incl = num;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    const int total = __shfl(incl, 63);
+    const int excl = incl - num;
+    int done = 0;
+    while (done < total) {
+      if (fill == UPD_CAP) {
+        drain_list<D, BF16>(x, list, fill, acc, lane);
+        fill = 0;
+      }
+      const int take = min(UPD_CAP - fill, total - done);
+      const int e0 = max(0, done - excl), e1 = min(num, done + take - excl);
+      for (int e = e0; e < e1; ++e)
+        list[fill + excl + e - done] = tile * 256 + int(perm[uint64_t(tile) * 256 + beg + e]);
+      fill += take;
+      done += take;
+      cnt += take;
+    }
+  }
   if (fill) drain_list<D, BF16>(x, list, fill, acc, lane);
   finalize_centroid<D, BF16>(cb, cn, k, L.C, cnt, acc, lane);
 }
@@ -1321,6 +1476,11 @@ static void launch_assign_t(const EncodeArgs &a, int streams, hipStream_t st) {
 }
 template <int D, bool BF>
 static void launch_update_t(const EncodeArgs &a, int streams, hipStream_t st) {
+  if (a.L.C <= kSortMaxClusters) {
+    hipLaunchKernelGGL(k_tile_sort, dim3(cdiv(a.n, 256), a.L.H, streams), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_update_sorted<D, BF>), dim3(cdiv(a.L.C, 4), a.L.H, streams), dim3(256), 0, st, a);
+    return;
+  }
   hipLaunchKernelGGL((k_update<D, BF>), dim3(cdiv(a.L.C, 16), a.L.H, streams), dim3(1024), 0, st, a);
 }
 

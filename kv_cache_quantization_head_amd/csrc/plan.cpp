@@ -87,7 +87,16 @@ int make_plan(const qkv_config *cfg, Plan *plan) {
     p.xl_proj_off = align_up(p.xl_chain_off + 2 * H * M * d * 2);
     xl = align_up(p.xl_proj_off + 2 * M * uint64_t(c.xlayer_rank) * 4);
   }
-  p.scratch_bytes = std::max(attn, xl);
+  // per-tile stable sort of a call's cluster ids (k-means update): for every
+  // (layer of the call, K|V, head, 256-token tile) a permutation (u8 x 256)
+  // and per-cluster offsets (u16 x (C+1)); placed after the cross-layer
+  // buffers, which the encoder uses at the same time
+  p.sort_tiles = (uint64_t(p.cfg.max_chunk_tokens) + 255) / 256;
+  const uint64_t units = C <= uint64_t(kSortMaxClusters) ? 2 * uint64_t(c.n_layers) * H * p.sort_tiles : 0;
+  p.sort_perm_off = xl;
+  p.sort_off_off = align_up(p.sort_perm_off + units * 256);
+  const uint64_t enc = align_up(p.sort_off_off + units * (C + 1) * 2);
+  p.scratch_bytes = std::max(attn, enc);
   p.total_bytes = p.scratch_off + p.scratch_bytes;
   *plan = p;
   return QKV_OK;

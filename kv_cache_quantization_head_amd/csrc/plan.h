@@ -14,6 +14,7 @@ namespace qkv {
 
 constexpr int kMaxChunks = 256;      // snapshot slots per stream (header size)
 constexpr int kMaxSplits = 8;        // split-KV partitions of one attention call
+constexpr int kSortMaxClusters = 4096;  // k-means update through per-tile sorts up to this C
 constexpr uint64_t kAlign = 256;
 
 inline uint64_t align_up(uint64_t v, uint64_t a = kAlign) { return (v + a - 1) / a * a; }
@@ -46,6 +47,8 @@ struct Plan {
   uint64_t scratch_off, scratch_bytes;
   uint64_t attn_part_o_off, attn_part_lse_off;     // relative to scratch
   uint64_t xl_pred_off, xl_chain_off, xl_proj_off; // relative to scratch
+  uint64_t sort_perm_off, sort_off_off;            // relative to scratch (encode)
+  uint64_t sort_tiles;                             // 256-token tiles per call, max
   uint64_t total_bytes;
   int kv_elem_bytes;
 };
