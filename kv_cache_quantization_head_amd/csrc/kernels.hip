@@ -22,6 +22,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device.h"
 #include "launch.h"
 
@@ -1362,6 +1364,368 @@ __global__ __launch_bounds__(512, 1) void k_attend2(AttnArgs a) {
   }
 }
 
+// Attention, version 3 (used by qkv_attend).
+//
+// Same block shape and load pipeline as k_attend2 (8 waves, 32 queries each,
+// 64-key tiles double-buffered in LDS, ids two tiles ahead, packed data one
+// tile ahead), with the VALU work per score cut down:
+//  * K and V are rebuilt exactly as the reconstruction defines them (fp32,
+//    stage by stage, then nearest-even bf16); 2-bit codes are widened four at
+//    a time: a masked code word holds four codes in four bytes, which the
+//    byte-to-float conversions (v_cvt_f32_ubyte0..3) widen directly;
+//  * K/V items alternate between neighbouring threads so every wave shares
+//    the rebuild work evenly;
+//  * the softmax scale is folded into the exponent's fma; the running max is
+//    only raised (and O, l rescaled) when a tile's max exceeds it by more
+//    than 8 (log2 units), so exponentials stay <= 256;
+//  * row sums of P come from one extra MFMA against a fragment of ones.
+constexpr float AT3_TAU = 8.0f;
+
+template <int D, int G, int BITS, bool CB_BF16, int SMAX>
+__global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
+  // SMAX = the number of PRQ stages (a template parameter so that the staging
+  // registers are sized exactly)
+  constexpr int NG = D / G;
+  constexpr int KP = D + 8;                // bf16 elements per K row in LDS
+  constexpr int VP = AT_BK + 8;            // bf16 elements per V^T row in LDS
+  constexpr int EB = CB_BF16 ? 2 : 4;
+  constexpr int KW = G * BITS / 32;        // code words of an item (one key, one group)
+  constexpr int KC = G * EB / 16;          // uint4 of an item's centroid slice
+  static_assert(2 * 64 * NG <= 512, "one item per thread");
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][AT_BK * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VP];
+  __shared__ int32_t starts_s[kMaxChunks + 1];
+  __shared__ int32_t nch_s;
+
+  const DevLayout &L = a.L;
+  const int h = blockIdx.y, split = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int g4 = lane >> 4, c16 = lane & 15;
+  const float sc = 1.4426950408889634f / sqrtf(float(D));
+
+  // Rebuild items: one (tensor, key, group of G channels) per thread, K on
+  // even and V on odd threads, so every wave runs the same rebuild code and
+  // the four threads of one key read one centroid row.  V is stored
+  // transposed ([d][key]) with the key column XOR-swizzled by 8*(d/32 mod 4),
+  // which spreads the rows written by one store over different banks and
+  // keeps each aligned run of 4 keys contiguous for the PV operand reads.
+  const int it_kv = tid & 1, it_rem = tid >> 1;
+  const bool has_item = it_rem < 64 * NG;
+  const int it_key = it_rem / NG, it_g = it_rem % NG;
+  const int it_ch = it_g * G;
+  const uint8_t *st = it_kv ? a.stream_v : a.stream_k;
+  const uint8_t *idp = st + L.ids_off + uint64_t(h) * L.ids_head;
+
+  if (tid == 0) nch_s = ((const StreamHeader *)(a.stream_k + L.header_off))->n_chunks;
+  __syncthreads();
+  for (int i = tid; i < nch_s; i += blockDim.x)
+    starts_s[i] = ((const StreamHeader *)(a.stream_k + L.header_off))->start[i];
+
+  const int ks = split * a.split_len;
+  const int ke = min(a.n_keys, ks + a.split_len);
+  const int n_tiles = ke > ks ? (ke - ks + AT_BK - 1) / AT_BK : 0;
+
+  // query fragments (B operand of S^T = K Q^T): Q[q][32*step + 8*g4 .. +8] in bf16
+  bf16x8 qf[2][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int q = blockIdx.x * AT_BQ + wave * 32 + qb * 16 + c16;
+#pragma unroll
+    for (int step = 0; step < D / 32; ++step) {
+      bf16x8 v;
+      if (q < a.n_q) {
+        const uint64_t off = (uint64_t(h) * a.n_q + q) * D + step * 32 + g4 * 8;
+        if (a.q_bf16) {
+          v = *(const bf16x8 *)((const uint16_t *)a.q + off);
+        } else {
+          const float *qp = (const float *)a.q + off;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)qp[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+      }
+      qf[qb][step] = v;
+    }
+  }
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+
+  floatx4 o[D / 16][2];
+  floatx4 lacc[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    lacc[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) o[db][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  float m_run[2] = {-INFINITY, -INFINITY};
+
+  // id of the item's key in a tile (-1: no key)
+  auto load_ids = [&](int tile) -> int {
+    if (!has_item || tile >= n_tiles) return -1;
+    const int t = ks + tile * AT_BK + it_key;
+    if (t >= ke) return -1;
+    return L.id_bytes == 1 ? int(idp[t]) : int(((const uint16_t *)idp)[t]);
+  };
+  struct Regs {
+    uint32_t codes[SMAX][KW];
+    uint32_t meta[SMAX];
+    uint4 cent[KC];
+  } R;
+  // packed data of the item's key t: centroid slice, codes, (sigma, z)
+  auto load_data = [&](int tile, int id) {
+    if (id < 0) return;
+    const int t = ks + tile * AT_BK + it_key;
+    const int slot = chunk_of_lds(starts_s, nch_s, t);
+    const uint8_t *crow = st + L.cb_off + uint64_t(slot) * L.cb_chunk + uint64_t(h) * L.cb_head +
+                          uint64_t(id) * D * EB + uint64_t(it_ch) * EB;
+#pragma unroll
+    for (int i = 0; i < KC; ++i) R.cent[i] = *(const uint4 *)(crow + 16 * i);
+#pragma unroll
+    for (int s2 = 0; s2 < SMAX; ++s2) {
+      const uint8_t *cp = st + L.codes_off + uint64_t(s2) * L.codes_stage + uint64_t(h) * L.codes_head +
+                          uint64_t(t) * L.codes_token + uint64_t(it_g) * (G * BITS / 8);
+      if constexpr (KW == 2) {
+        const uint2 v = *(const uint2 *)cp;
+        R.codes[s2][0] = v.x; R.codes[s2][1] = v.y;
+      } else {
+#pragma unroll
+        for (int w = 0; w < KW; w += 4) {
+          const uint4 v = *(const uint4 *)(cp + 4 * w);
+          R.codes[s2][w] = v.x; R.codes[s2][w + 1] = v.y; R.codes[s2][w + 2] = v.z; R.codes[s2][w + 3] = v.w;
+        }
+      }
+      R.meta[s2] = *((const uint32_t *)(st + L.meta_off + uint64_t(s2) * L.meta_stage + uint64_t(h) * L.meta_head +
+                                        uint64_t(t) * L.meta_token) + it_g);
+    }
+  };
+  // one PRQ stage folded into 16 channels: xh[c] = fmaf(q_c, sigma, xh[c]) (the
+  // zero points of all stages are added to the centroid beforehand)
+  auto stage16 = [&](const uint32_t *cw, float sf, float *xh) {
+    if constexpr (BITS == 2) {
+#pragma unroll
+      for (int sh = 0; sh < 4; ++sh) {
+        const uint32_t m = (cw[0] >> (2 * sh)) & 0x03030303u;  // bytes: channels 4*byte + sh
+#pragma unroll
+        for (int by = 0; by < 4; ++by) xh[4 * by + sh] = fmaf(float((m >> (8 * by)) & 0xffu), sf, xh[4 * by + sh]);
+      }
+    } else {
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          const uint32_t m = (cw[w] >> (4 * sh)) & 0x0f0f0f0fu;  // bytes: channels 8w + 2*byte + sh
+#pragma unroll
+          for (int by = 0; by < 4; ++by)
+            xh[8 * w + 2 * by + sh] = fmaf(float((m >> (8 * by)) & 0xffu), sf, xh[8 * w + 2 * by + sh]);
+        }
+    }
+  };
+  // centroid channel e of the item as fp32
+  auto cent_f32 = [&](int e) -> float {
+    if constexpr (CB_BF16) {
+      const uint4 v = R.cent[e >> 3];
+      const uint32_t w = ((e & 7) >> 1) == 0 ? v.x : ((e & 7) >> 1) == 1 ? v.y : ((e & 7) >> 1) == 2 ? v.z : v.w;
+      return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+    } else {
+      const uint4 v = R.cent[e >> 2];
+      const uint32_t w = (e & 3) == 0 ? v.x : (e & 3) == 1 ? v.y : (e & 3) == 2 ? v.z : v.w;
+      return __uint_as_float(w);
+    }
+  };
+  // Rebuild the item for the products: xh = fmaf(q_S, sigma_S, ... fmaf(q_1,
+  // sigma_1, c + (z_1 + ... + z_S))), then nearest-even bf16.  This differs
+  // from the stage-by-stage reconstruction (c + rhat_1) + rhat_2 ... by a few
+  // fp32 ulps, which changes the bf16 operand only for values within those
+  // ulps of a bf16 rounding boundary.
+  auto dequant_store = [&](int buf, int id) {
+    if (!has_item) return;
+    float xh[G];
+    if (id >= 0) {
+      float zs = 0.0f;
+#pragma unroll
+      for (int s2 = 0; s2 < SMAX; ++s2) zs += f16_bits_to_f32(uint16_t(R.meta[s2] >> 16));
+#pragma unroll
+      for (int e = 0; e < G; ++e) xh[e] = cent_f32(e) + zs;
+#pragma unroll
+      for (int s2 = 0; s2 < SMAX; ++s2) {
+        const float sf = f16_bits_to_f32(uint16_t(R.meta[s2] & 0xffffu));
+#pragma unroll
+        for (int b16 = 0; b16 < G / 16; ++b16) stage16(&R.codes[s2][b16 * (BITS / 2)], sf, &xh[16 * b16]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < G; ++e) xh[e] = 0.0f;
+    }
+    if (it_kv == 0) {
+      uint16_t *dst = &Ks[buf][it_key * KP + it_ch];
+#pragma unroll
+      for (int j = 0; j < G; j += 8) {
+        uint4 v;
+        v.x = uint32_t(f32_to_bf16_bits(xh[j])) | (uint32_t(f32_to_bf16_bits(xh[j + 1])) << 16);
+        v.y = uint32_t(f32_to_bf16_bits(xh[j + 2])) | (uint32_t(f32_to_bf16_bits(xh[j + 3])) << 16);
+        v.z = uint32_t(f32_to_bf16_bits(xh[j + 4])) | (uint32_t(f32_to_bf16_bits(xh[j + 5])) << 16);
+        v.w = uint32_t(f32_to_bf16_bits(xh[j + 6])) | (uint32_t(f32_to_bf16_bits(xh[j + 7])) << 16);
+        *(uint4 *)(dst + j) = v;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const int d = it_ch + j;
+        Vt[buf][d * VP + (it_key ^ (8 * ((d >> 5) & 3)))] = f32_to_bf16_bits(xh[j]);
+      }
+    }
+  };
+
+  auto compute_tile = [&](int tile) {
+    const int buf = tile & 1;
+    const int kt0 = ks + tile * AT_BK;
+    floatx4 s[4][2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int step = 0; step < D / 32; ++step) {
+        const bf16x8 ka = *(const bf16x8 *)&Ks[buf][(kb * 16 + c16) * KP + step * 32 + g4 * 8];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qb][step], s[kb][qb], 0, 0, 0);
+      }
+    }
+    const bool full = kt0 + AT_BK <= ke;
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float tmax = -INFINITY;
+      if (full) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[kb][qb][r]);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (kt0 + kb * 16 + g4 * 4 + r >= ke) s[kb][qb][r] = -INFINITY;
+            tmax = fmaxf(tmax, s[kb][qb][r]);
+          }
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mt = tmax * sc;
+      const bool need = mt > m_run[qb] + AT3_TAU;
+      if (__any(need)) {
+        const float mnew = need ? mt : m_run[qb];
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run[qb] - mnew) : 1.0f;
+        m_run[qb] = mnew;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) o[db][qb] *= alpha;
+        lacc[qb] *= alpha;
+      }
+      const float nm = -m_run[qb];
+#pragma unroll
+      for (int st2 = 0; st2 < 2; ++st2) {
+        bf16x8 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * st2][qb][r], sc, nm));
+          v[4 + r] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * st2 + 1][qb][r], sc, nm));
+        }
+        pb[qb][st2] = v;
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) {
+#pragma unroll
+      for (int st2 = 0; st2 < 2; ++st2) {
+        const int vd = db * 16 + c16, sw = 8 * ((vd >> 5) & 3);
+        const uint16_t *vrow = &Vt[buf][vd * VP];
+        const bf16x4 lo = *(const bf16x4 *)(vrow + ((st2 * 32 + g4 * 4) ^ sw));
+        const bf16x4 hi = *(const bf16x4 *)(vrow + ((st2 * 32 + 16 + g4 * 4) ^ sw));
+        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qb][st2], o[db][qb], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qb][st2], lacc[qb], 0, 0, 0);
+  };
+
+  // Pipeline: at iteration i every wave rebuilds tile i+1 from data loaded
+  // during iteration i-1 and issues the loads of tile i+2 (ids of tile i+3);
+  // one barrier per tile.  Two waves share each SIMD; half of the waves
+  // multiply tile i before rebuilding and half after, so one wave's MFMA work
+  // overlaps its partner's VALU work.  The split flips between waves w and
+  // w+4 and between waves 2k and 2k+1, whichever way waves sit on SIMDs.
+  const bool mfma_first = ((wave >> 2) ^ wave) & 1;
+  __syncthreads();  // chunk table in LDS
+  int id1, id2;
+  {
+    const int id0 = load_ids(0);
+    load_data(0, id0);
+    dequant_store(0, id0);
+    id1 = load_ids(1);
+    load_data(1, id1);
+    id2 = load_ids(2);
+  }
+  __syncthreads();
+
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int buf = tile & 1;
+    if (mfma_first) compute_tile(tile);
+    if (tile + 1 < n_tiles) dequant_store(buf ^ 1, id1);   // data of tile+1 already in R
+    load_data(tile + 2, id2);
+    id1 = id2;
+    id2 = load_ids(tile + 3);
+    if (!mfma_first) compute_tile(tile);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int q = blockIdx.x * AT_BQ + wave * 32 + qb * 16 + c16;
+    if (q >= a.n_q) continue;
+    const float l = lacc[qb][0];
+    const bool empty = !(l > 0.0f);
+    const float inv_l = empty ? 0.0f : 1.0f / l;
+    const float lse = empty ? -INFINITY : (m_run[qb] + log2f(l)) * 0.6931471805599453f;
+    if (a.n_splits == 1) {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const uint64_t off = (uint64_t(h) * a.n_q + q) * D + db * 16 + g4 * 4;
+        const floatx4 v = o[db][qb] * inv_l;
+        if (a.out_bf16) {
+          uint16_t *op = (uint16_t *)a.out + off;
+          const uint32_t p0 = uint32_t(f32_to_bf16_bits(v[0])) | (uint32_t(f32_to_bf16_bits(v[1])) << 16);
+          const uint32_t p1 = uint32_t(f32_to_bf16_bits(v[2])) | (uint32_t(f32_to_bf16_bits(v[3])) << 16);
+          *(uint2 *)op = make_uint2(p0, p1);
+        } else {
+          *(float4 *)((float *)a.out + off) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+      if (a.lse && g4 == 0) a.lse[uint64_t(h) * a.n_q + q] = lse;
+    } else {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const uint64_t off = ((uint64_t(split) * L.H + h) * a.n_q + q) * D + db * 16 + g4 * 4;
+        const floatx4 v = o[db][qb] * inv_l;
+        *(float4 *)(a.part_o + off) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+      if (g4 == 0) a.part_lse[(uint64_t(split) * L.H + h) * a.n_q + q] = lse;
+    }
+  }
+}
+
 // Merge split partials: O = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - max).
 // One thread per (query, channel); blockIdx.y = head.
 __global__ __launch_bounds__(256) void k_attend_merge(AttnArgs a) {
@@ -1501,8 +1865,13 @@ static void launch_recon_t(const ReconArgs &a, int n_layers, int64_t out_tokens,
 
 template <int D, int G, int BITS, bool BF>
 static void launch_attend_t(const AttnArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((k_attend2<D, G, BITS, BF>), dim3(cdiv(a.n_q, AT_BQ), a.L.H, a.n_splits), dim3(512),
-                     0, st, a);
+  const dim3 grid(cdiv(a.n_q, AT_BQ), a.L.H, a.n_splits);
+  switch (a.L.S) {
+    case 1: hipLaunchKernelGGL((k_attend3<D, G, BITS, BF, 1>), grid, dim3(512), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_attend3<D, G, BITS, BF, 2>), grid, dim3(512), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_attend3<D, G, BITS, BF, 3>), grid, dim3(512), 0, st, a); break;
+    default: hipLaunchKernelGGL((k_attend3<D, G, BITS, BF, 4>), grid, dim3(512), 0, st, a); break;
+  }
 }
 
 // (D, G, BITS, BF) dispatch for the codec-shaped kernels
