@@ -31,40 +31,71 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run a plain 1 GiB device copy (a known-size "
+                         "reference for HBM byte counters)")
     return ap.parse_args()
 
 
-def cpu_baseline(cfgs, k_dev, v_dev, q_dev):
-    """The oracle, as it stands, on a bounded sample: head 0 of K and V (1/12 of
-    the layer): full k-means + PRQ encode, reconstruction, and attention of all
-    4680 queries of that head.  Scaled to the same GB/s unit as the GPU line."""
+def cpu_baseline(cfgs, k_dev, v_dev, q_dev, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    whole heads of the layer, one after another, until about ``budget_s``
+    seconds of CPU work are done.  Per head: full encode of K and V (k-means
+    + PRQ), reconstruction, attention of all of that head's queries.  Scaled
+    to the same GB/s unit as the GPU line (bf16 K+V bytes of the heads done
+    per second)."""
     import numpy as np
     import torch
     from oracle import attend as o_attend
     from oracle import stream as o_stream
 
     threads = torch.get_num_threads()
-    k = k_dev[:1].float().cpu().numpy()
-    v = v_dev[:1].float().cpu().numpy()
-    q = q_dev[:1].float().cpu().numpy()
+    H = k_dev.shape[0]
     t = time.perf_counter()
-    xs = []
-    for x in (k, v):
-        s = o_stream.Stream(1, cfgs.head_dim, cfgs.n_clusters, cfgs.iters, cfgs.n_stages, cfgs.bits,
-                            cfgs.group, "bf16")
-        s.encode(x)
-        xs.append(s.xhat())
-    o_attend.attend(q, xs[0], xs[1])
+    heads = 0
+    while heads < H:
+        k = k_dev[heads:heads + 1].float().cpu().numpy()
+        v = v_dev[heads:heads + 1].float().cpu().numpy()
+        q = q_dev[heads:heads + 1].float().cpu().numpy()
+        xs = []
+        for x in (k, v):
+            s = o_stream.Stream(1, cfgs.head_dim, cfgs.n_clusters, cfgs.iters, cfgs.n_stages,
+                                cfgs.bits, cfgs.group, "bf16")
+            s.encode(x)
+            xs.append(s.xhat())
+        o_attend.attend(q, xs[0], xs[1])
+        heads += 1
+        if time.perf_counter() - t >= budget_s:
+            break
     dt = time.perf_counter() - t
-    sample_bytes = 2 * k.shape[1] * k.shape[2] * 2     # bf16 K+V of one head
+    sample_bytes = heads * 2 * k_dev.shape[1] * k_dev.shape[2] * 2     # bf16 K+V of the heads done
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
     return {"value": round(sample_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": cores,
             "blas_threads": threads, "kind": "oracle", "seconds": round(dt, 2),
-            "sample": "head 0 of K and V (1/12 of the layer): full encode (5 k-means iterations + "
-                      "2 PRQ stages), reconstruction, attention of all 4680 queries of that head"}
+            "sample": f"heads 0..{heads - 1} of {H} of the layer, K and V: full encode "
+                      f"({cfgs.iters} k-means iterations + {cfgs.n_stages} PRQ stages), "
+                      f"reconstruction, attention of all {q_dev.shape[1]} queries of each head"}
+
+
+def recorded_traffic(kernel_source):
+    """HBM bytes per launch of the attention kernel, from the committed counter
+    summary, or None when the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "k_attend3_wan_layer_pmc.txt")
+    try:
+        fields = dict(line.split(":", 1) for line in open(path) if ":" in line)
+    except OSError:
+        return None
+    digest = hashlib.sha256(open(kernel_source, "rb").read()).hexdigest()
+    if fields.get("kernels_sha256", "").strip() != digest:
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"].strip())
+    except (KeyError, ValueError):
+        return None
 
 
 def main():
@@ -150,10 +181,19 @@ def main():
         "reconstruct_GBps": round(recon_gbs, 2),
         "attend_q_tokens_per_s": round(Tq / (ms["attend"] * 1e-3), 1),
         "attend_TFLOPs": round(att_tflops, 2),
-        "roofline": {"kernel": "qkv_attend (k_attend + split merge)", "bound": "mfma",
+        "roofline": {"kernel": "k_attend3 (qkv_attend is one launch at this shape)", "bound": "mfma",
                      "achieved": round(att_tflops, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(att_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(att_tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": recorded_traffic(os.path.join(ROOT, "kv_cache_quantization_head_amd",
+                                                              "csrc", "kernels.hip"))},
     }
+    if args.copy_calibration:
+        src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfgs, k, v, q)
     print(json.dumps(result), flush=True)

@@ -138,7 +138,15 @@ extern "C" int qkv_attend(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Plan &p = ctx->plan;
   const int64_t n_keys = ctx->layers[layer].n_tokens;
-  int splits = attention_splits(p, n_keys, n_q);
+  if (ctx->n_cu <= 0) {
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n_cu > 0)
+      ctx->n_cu = n_cu;
+    else
+      ctx->n_cu = 256;
+  }
+  int splits = attention_splits(p, n_keys, n_q, ctx->n_cu);
   int64_t split_len = (n_keys + splits - 1) / splits;
   split_len = (split_len + 63) / 64 * 64;
   splits = int((n_keys + split_len - 1) / split_len);

@@ -73,6 +73,7 @@ struct qkv_ctx {
   // [chain_t0, chain_t0 + chain_n) is held in scratch after an encode call
   int32_t chain_layer = -1;
   int64_t chain_t0 = 0, chain_n = 0;
+  int n_cu = 0;                  // compute units of the device, read at the first attention call
   int last_hip_error = 0;
   std::string last_error;
 };
@@ -89,8 +90,9 @@ int check_reconstruct(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int3
                       int64_t t1, const void *out, int32_t out_dtype);
 int check_rewind(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int64_t n_tokens);
 
-// Number of KV splits used by an attention call over n_keys keys.
-int attention_splits(const Plan &p, int64_t n_keys, int64_t n_q);
+// Number of KV splits used by an attention call over n_keys keys on a device
+// with n_cu compute units.
+int attention_splits(const Plan &p, int64_t n_keys, int64_t n_q, int n_cu);
 
 // Byte offset of stream (layer, kv) from the arena base.
 inline uint64_t stream_offset(const Plan &p, int layer, int kv) {
