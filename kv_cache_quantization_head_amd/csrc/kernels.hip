@@ -3,13 +3,19 @@
 //   k_header      chunk table of every stream touched by an encode call
 //   k_init        initial codebook of a call: previous snapshot (centroid
 //                 caching) or strided tokens
-//   k_assign      nearest centroid per token: fp32 scores screen the
-//                 candidates under a proven error bound; near ties are decided
-//                 by the exact fp64 distance, channels summed in order
-//   k_update      fp64 member sums in token order -> mean -> one rounding
+//   k_assign_mfma nearest centroid per token for bf16 caches with C <= 512:
+//                 bf16 MFMA scores screen the candidates under a proven error
+//                 bound; close calls are decided by the exact fp64 distance,
+//                 channels summed in order
+//   k_assign      the same decision with fp32 VALU screening (fp32 caches,
+//                 C > 512)
+//   k_tile_sort, k_update_sorted
+//                 k-means update: stable per-tile sort of the ids, then fp64
+//                 member sums in token order -> mean -> one rounding
+//   k_update      the same update through in-LDS member lists (C > 4096)
 //   k_quantize    centroid (or prediction) subtraction + S PRQ stages + packing
 //   k_reconstruct unpack + dequantize + add base, fp32 or bf16 out
-//   k_attend      split-KV attention reading the packed cache: tiles are
+//   k_attend3     split-KV attention reading the packed cache: tiles are
 //                 rebuilt in bf16 in LDS and fed to bf16 MFMA (16x16x32)
 //   k_attend_merge  LSE merge of the split partials
 //   k_xl_project, k_xl_predict  cross-layer block-diagonal + low-rank
@@ -862,219 +868,35 @@ __global__ __launch_bounds__(256) void k_reconstruct(ReconArgs a, int64_t out_to
 
 // -------------------------------------------------------------- attention
 //
-// Block = 4 waves = 128 queries of one head (32 per wave, two 16-column MFMA
-// blocks); grid = (query blocks, heads, KV splits).  Per 64-key tile the
-// block rebuilds K and V in bf16 into LDS (K as [key][d], V transposed as
-// [d][key]), then each wave computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16
-// (so each lane's accumulator column is one query), runs the online softmax
-// in fp32 with exp2, and accumulates O^T += V^T P^T with the probabilities
-// rounded to bf16.  The key order inside one 32-key MFMA step is permuted
-// identically in both operands so that P^T comes straight from the S^T
-// accumulator registers.
-constexpr int ATT_BQ = 128;
-constexpr int ATT_BK = 64;
-
-template <int D, int G, int BITS, bool CB_BF16>
-__global__ __launch_bounds__(256) void k_attend(AttnArgs a) {
-  constexpr int NG = D / G;
-  constexpr int KP = D + 8;          // Ks row pitch (elements)
-  constexpr int VP = ATT_BK + 8;     // Vt row pitch (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[ATT_BK * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
-  const DevLayout &L = a.L;
-  const int h = blockIdx.y, split = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g4 = lane >> 4, c16 = lane & 15;
-  const float sc = 1.4426950408889634f / sqrtf(float(D));   // log2(e)/sqrt(d)
-
-  // query fragments (B operand of S^T = K Q^T): lane holds Q[q][32*step + 8*g4 .. +8]
-  bf16x8 qf[2][D / 32];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int q = blockIdx.x * ATT_BQ + wave * 32 + qb * 16 + c16;
-#pragma unroll
-    for (int step = 0; step < D / 32; ++step) {
-      bf16x8 v;
-      if (q < a.n_q) {
-        const uint64_t off = (uint64_t(h) * a.n_q + q) * D + step * 32 + g4 * 8;
-        if (a.q_bf16) {
-          v = *(const bf16x8 *)((const uint16_t *)a.q + off);
-        } else {
-          const float *qp = (const float *)a.q + off;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (__bf16)qp[e];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
-      }
-      qf[qb][step] = v;
-    }
-  }
-
-  floatx4 o[D / 16][2];
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) o[db][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-
-  const int ks = split * a.split_len;
-  const int ke = min(a.n_keys, ks + a.split_len);
-  for (int kt0 = ks; kt0 < ke; kt0 += ATT_BK) {
-    __syncthreads();
-    // rebuild the K and V tile in bf16
-    for (int it = threadIdx.x; it < ATT_BK * NG; it += blockDim.x) {
-      const int key = it / NG, g = it % NG;
-      const int tt = kt0 + key;
-      float xk[G], xv[G];
-      if (tt < ke) {
-        centroid_base<D, G, CB_BF16>(a.stream_k, L, h, tt, g, xk);
-        add_stages<D, G, BITS>(a.stream_k, L, h, tt, g, xk);
-        centroid_base<D, G, CB_BF16>(a.stream_v, L, h, tt, g, xv);
-        add_stages<D, G, BITS>(a.stream_v, L, h, tt, g, xv);
-      } else {
-#pragma unroll
-        for (int j = 0; j < G; ++j) xk[j] = xv[j] = 0.0f;
-      }
-#pragma unroll
-      for (int j = 0; j < G; j += 2) {
-        const uint32_t pk = uint32_t(f32_to_bf16_bits(xk[j])) | (uint32_t(f32_to_bf16_bits(xk[j + 1])) << 16);
-        *(uint32_t *)&Ks[key * KP + g * G + j] = pk;
-      }
-#pragma unroll
-      for (int j = 0; j < G; ++j) Vt[(g * G + j) * VP + key] = f32_to_bf16_bits(xv[j]);
-    }
-    __syncthreads();
-
-    // S^T blocks: s[kb][qb], rows = keys 16kb + 4g4 + r, column = query c16
-    floatx4 s[4][2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int step = 0; step < D / 32; ++step) {
-        const bf16x8 ka = *(const bf16x8 *)&Ks[(kb * 16 + c16) * KP + step * 32 + g4 * 8];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qb][step], s[kb][qb], 0, 0, 0);
-      }
-    }
-    // online softmax per query column
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float tmax = -INFINITY;
-      float sv[4][4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kt0 + kb * 16 + g4 * 4 + r;
-          const float v = key < ke ? s[kb][qb][r] * sc : -INFINITY;
-          sv[kb][r] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mnew = fmaxf(m_run[qb], tmax);
-      const float alpha = exp2f(m_run[qb] - mnew);
-      float rs = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(sv[kb][r] - mnew);
-          sv[kb][r] = p;
-          rs += p;
-        }
-      rs += __shfl_xor(rs, 16);
-      rs += __shfl_xor(rs, 32);
-      l_run[qb] = l_run[qb] * alpha + rs;
-      m_run[qb] = mnew;
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) o[db][qb] *= alpha;
-#pragma unroll
-      for (int st2 = 0; st2 < 2; ++st2) {
-        bf16x8 v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = (__bf16)sv[2 * st2][r];
-          v[4 + r] = (__bf16)sv[2 * st2 + 1][r];
-        }
-        pb[qb][st2] = v;
-      }
-    }
-    // O^T += V^T P^T; A = V^T rows d, key slots (32*st2 + 4*g4 + 0..3, 32*st2 + 16 + 4*g4 + 0..3)
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-#pragma unroll
-      for (int st2 = 0; st2 < 2; ++st2) {
-        const uint16_t *vr = &Vt[(db * 16 + c16) * VP + st2 * 32 + g4 * 4];
-        const bf16x4 lo = *(const bf16x4 *)vr;
-        const bf16x4 hi = *(const bf16x4 *)(vr + 16);
-        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qb][st2], o[db][qb], 0, 0, 0);
-      }
-    }
-  }
-
-  // write: lane holds O[q][16db + 4g4 + r]
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int q = blockIdx.x * ATT_BQ + wave * 32 + qb * 16 + c16;
-    if (q >= a.n_q) continue;
-    const bool empty = l_run[qb] == 0.0f;
-    const float inv_l = empty ? 0.0f : 1.0f / l_run[qb];
-    const float lse = empty ? -INFINITY : (m_run[qb] + log2f(l_run[qb])) * 0.6931471805599453f;
-    if (a.n_splits == 1) {
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const uint64_t off = (uint64_t(h) * a.n_q + q) * D + db * 16 + g4 * 4;
-        const floatx4 v = o[db][qb] * inv_l;
-        if (a.out_bf16) {
-          uint16_t *op = (uint16_t *)a.out + off;
-          const uint32_t p0 = uint32_t(f32_to_bf16_bits(v[0])) | (uint32_t(f32_to_bf16_bits(v[1])) << 16);
-          const uint32_t p1 = uint32_t(f32_to_bf16_bits(v[2])) | (uint32_t(f32_to_bf16_bits(v[3])) << 16);
-          *(uint2 *)op = make_uint2(p0, p1);
-        } else {
-          *(float4 *)((float *)a.out + off) = make_float4(v[0], v[1], v[2], v[3]);
-        }
-      }
-      if (a.lse && g4 == 0) a.lse[uint64_t(h) * a.n_q + q] = lse;
-    } else {
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const uint64_t off = ((uint64_t(split) * L.H + h) * a.n_q + q) * D + db * 16 + g4 * 4;
-        const floatx4 v = o[db][qb] * inv_l;
-        *(float4 *)(a.part_o + off) = make_float4(v[0], v[1], v[2], v[3]);
-      }
-      if (g4 == 0) a.part_lse[(uint64_t(split) * L.H + h) * a.n_q + q] = lse;
-    }
-  }
-}
-
-// Attention, version used by qkv_attend: block = 8 waves (two per SIMD, so
-// one wave's MFMA overlaps the other's softmax/dequant VALU work) = 256
+// Fused read of the packed cache.  Block = 8 waves (two per SIMD) = 256
 // queries of one head, 32 per wave; grid = (query blocks, heads, KV splits).
-// Tiles of 64 keys are rebuilt in bf16 into a double-buffered LDS tile (K as
-// [key][d], V transposed as [d][key]): one (tensor, key, group) item per
-// thread.  Loads are software-pipelined: the cluster ids of tile i+2 and the
-// packed data (codes, scale/zero, centroid rows) of tile i+1 are in flight
-// while tile i is multiplied.  The chunk table is cached in LDS.
+// Per 64-key tile the block rebuilds K and V in bf16 into a double-buffered
+// LDS tile (K as [key][d]; V transposed as [d][key] with the key column
+// XOR-swizzled by 8*(d/32 mod 4)); each wave then computes S^T = K Q^T with
+// v_mfma_f32_16x16x32_bf16 (one lane's accumulator column is one query, so
+// softmax statistics need two cross-lane exchanges), runs the online softmax
+// in fp32 and accumulates O^T += V^T P^T with the probabilities rounded to
+// bf16.  The key order inside a 32-key MFMA step is permuted identically in
+// both operands so that P^T comes straight from the S^T accumulators.
+//
+//  * Rebuild items: one (tensor, key, group of G channels) per thread, K on
+//    even and V on odd threads (every wave runs the same code; the four
+//    threads of a key read one centroid row).  The rebuild is
+//    bf16(fl32 chain: c + sum_s z_s, then fmaf(q_s, sigma_s, .) per stage);
+//    2-bit codes are widened four at a time from one masked code word
+//    (byte-to-float conversions).
+//  * Loads are software-pipelined: ids of tile i+2 and the packed data
+//    (codes, scale/zero, centroid rows) of tile i+1 are in flight while tile
+//    i is rebuilt and multiplied; half of the waves multiply before they
+//    rebuild and half after, so MFMA and VALU work of the two waves on a SIMD
+//    overlap.  The chunk table is cached in LDS.
+//  * The softmax scale is folded into the exponent's fma; the running max is
+//    only raised (and O, l rescaled) when a tile's max exceeds it by more
+//    than 8 (log2 units), so exponentials stay <= 256; row sums of P come
+//    from one extra MFMA against a fragment of ones.
 constexpr int AT_WAVES = 8;
 constexpr int AT_BQ = 32 * AT_WAVES;
 constexpr int AT_BK = 64;
-
-template <int WORDS, int CV, int SMAX>
-struct TileRegs {                 // packed inputs of one (tensor, key, group) item
-  uint32_t codes[SMAX][WORDS];    // S stages of G codes
-  uint32_t meta[SMAX];            // (sigma, z) fp16 pairs
-  uint4 cent[CV];                 // the centroid slice: G values of the cache dtype
-};
 
 __device__ __forceinline__ int chunk_of_lds(const int32_t *starts, int n_chunks, int t) {
   int lo = 0, hi = n_chunks - 1;
@@ -1085,300 +907,6 @@ __device__ __forceinline__ int chunk_of_lds(const int32_t *starts, int n_chunks,
   return lo;
 }
 
-template <int D, int G, int BITS, bool CB_BF16>
-__global__ __launch_bounds__(512, 1) void k_attend2(AttnArgs a) {
-  constexpr int NG = D / G;
-  constexpr int NI = AT_BK * NG;           // items per tensor per tile
-  constexpr int KP = D + 8;
-  constexpr int VP = AT_BK + 8;
-  constexpr int WORDS = G * BITS / 32;
-  constexpr int EB = CB_BF16 ? 2 : 4;
-  constexpr int CV = G * EB / 16;          // uint4 per centroid slice
-  constexpr int SMAX = 4;
-  constexpr uint32_t MASK = (1u << BITS) - 1u;
-  static_assert(2 * NI <= 512, "one item per thread");
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][AT_BK * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VP];
-  __shared__ int32_t starts_s[kMaxChunks + 1];
-  __shared__ int32_t nch_s;
-
-  const DevLayout &L = a.L;
-  const int h = blockIdx.y, split = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int g4 = lane >> 4, c16 = lane & 15;
-  const float sc = 1.4426950408889634f / sqrtf(float(D));
-
-  // my item: tensor (0 = K, 1 = V), key within the tile, group
-  const bool has_item = tid < 2 * NI;
-  const int it_kv = tid / NI, it_rem = tid % NI;
-  const int it_key = it_rem / NG, it_g = it_rem % NG;
-  const uint8_t *st = it_kv ? a.stream_v : a.stream_k;
-  const uint8_t *idp = st + L.ids_off + uint64_t(h) * L.ids_head;
-
-  if (tid == 0) nch_s = ((const StreamHeader *)(a.stream_k + L.header_off))->n_chunks;
-  __syncthreads();
-  for (int i = tid; i < nch_s; i += blockDim.x)
-    starts_s[i] = ((const StreamHeader *)(a.stream_k + L.header_off))->start[i];
-
-  const int ks = split * a.split_len;
-  const int ke = min(a.n_keys, ks + a.split_len);
-  const int n_tiles = ke > ks ? (ke - ks + AT_BK - 1) / AT_BK : 0;
-
-  // queries
-  bf16x8 qf[2][D / 32];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int q = blockIdx.x * AT_BQ + wave * 32 + qb * 16 + c16;
-#pragma unroll
-    for (int step = 0; step < D / 32; ++step) {
-      bf16x8 v;
-      if (q < a.n_q) {
-        const uint64_t off = (uint64_t(h) * a.n_q + q) * D + step * 32 + g4 * 8;
-        if (a.q_bf16) {
-          v = *(const bf16x8 *)((const uint16_t *)a.q + off);
-        } else {
-          const float *qp = (const float *)a.q + off;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (__bf16)qp[e];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
-      }
-      qf[qb][step] = v;
-    }
-  }
-  floatx4 o[D / 16][2];
-#pragma unroll
-  for (int db = 0; db < D / 16; ++db)
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) o[db][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-
-  // ---- software pipeline over tiles
-  auto load_id = [&](int tile) -> int {
-    const int t = ks + tile * AT_BK + it_key;
-    if (!has_item || tile >= n_tiles || t >= ke) return -1;
-    return L.id_bytes == 1 ? int(idp[t]) : int(((const uint16_t *)idp)[t]);
-  };
-  TileRegs<WORDS, CV, SMAX> R;
-  auto load_data = [&](int tile, int id) {
-    const int t = ks + tile * AT_BK + it_key;
-    if (id < 0) return;
-    const int slot = chunk_of_lds(starts_s, nch_s, t);
-    const uint8_t *crow = st + L.cb_off + uint64_t(slot) * L.cb_chunk + uint64_t(h) * L.cb_head +
-                          uint64_t(id) * D * EB + uint64_t(it_g) * G * EB;
-#pragma unroll
-    for (int i = 0; i < CV; ++i) R.cent[i] = *(const uint4 *)(crow + 16 * i);
-#pragma unroll
-    for (int s = 0; s < SMAX; ++s) {
-      if (s < L.S) {
-        const uint8_t *cp = st + L.codes_off + uint64_t(s) * L.codes_stage + uint64_t(h) * L.codes_head +
-                            uint64_t(t) * L.codes_token + uint64_t(it_g) * (G * BITS / 8);
-        if constexpr (WORDS == 2) {
-          const uint2 v = *(const uint2 *)cp;
-          R.codes[s][0] = v.x; R.codes[s][1] = v.y;
-        } else {
-#pragma unroll
-          for (int w = 0; w < WORDS; w += 4) {
-            const uint4 v = *(const uint4 *)(cp + 4 * w);
-            R.codes[s][w] = v.x; R.codes[s][w + 1] = v.y; R.codes[s][w + 2] = v.z; R.codes[s][w + 3] = v.w;
-          }
-        }
-        R.meta[s] = *((const uint32_t *)(st + L.meta_off + uint64_t(s) * L.meta_stage +
-                                         uint64_t(h) * L.meta_head + uint64_t(t) * L.meta_token) + it_g);
-      }
-    }
-  };
-  auto dequant_store = [&](int buf, int id) {
-    if (!has_item) return;
-    float xh[G];
-    if (id >= 0) {
-#pragma unroll
-      for (int i = 0; i < CV; ++i) {
-        const uint32_t w4[4] = {R.cent[i].x, R.cent[i].y, R.cent[i].z, R.cent[i].w};
-        if constexpr (CB_BF16) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) xh[i * 8 + e] = bf16_to_f32((w4[e >> 1] >> (16 * (e & 1))) & 0xffffu);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) xh[i * 4 + e] = __uint_as_float(w4[e]);
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < SMAX; ++s) {
-        if (s < L.S) {
-          const float sf = f16_bits_to_f32(uint16_t(R.meta[s] & 0xffffu));
-          const float zf = f16_bits_to_f32(uint16_t(R.meta[s] >> 16));
-#pragma unroll
-          for (int j = 0; j < G; ++j) {
-            const float q = float((R.codes[s][(j * BITS) / 32] >> ((j * BITS) % 32)) & MASK);
-            xh[j] = xh[j] + fmaf(q, sf, zf);
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < G; ++j) xh[j] = 0.0f;
-    }
-    if (it_kv == 0) {
-      uint16_t *dst = &Ks[buf][it_key * KP + it_g * G];
-#pragma unroll
-      for (int j = 0; j < G; j += 8) {
-        uint4 v;
-        v.x = uint32_t(f32_to_bf16_bits(xh[j])) | (uint32_t(f32_to_bf16_bits(xh[j + 1])) << 16);
-        v.y = uint32_t(f32_to_bf16_bits(xh[j + 2])) | (uint32_t(f32_to_bf16_bits(xh[j + 3])) << 16);
-        v.z = uint32_t(f32_to_bf16_bits(xh[j + 4])) | (uint32_t(f32_to_bf16_bits(xh[j + 5])) << 16);
-        v.w = uint32_t(f32_to_bf16_bits(xh[j + 6])) | (uint32_t(f32_to_bf16_bits(xh[j + 7])) << 16);
-        *(uint4 *)(dst + j) = v;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < G; ++j) Vt[buf][(it_g * G + j) * VP + it_key] = f32_to_bf16_bits(xh[j]);
-    }
-  };
-
-  __syncthreads();  // chunk table in LDS
-  int id_cur = load_id(0);
-  int id_next = load_id(1);
-  load_data(0, id_cur);
-  dequant_store(0, id_cur);
-  __syncthreads();
-
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
-    const int kt0 = ks + tile * AT_BK;
-    // prefetch: data of tile+1, ids of tile+2
-    load_data(tile + 1, id_next);
-    const int id_after = load_id(tile + 2);
-
-    floatx4 s[4][2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int step = 0; step < D / 32; ++step) {
-        const bf16x8 ka = *(const bf16x8 *)&Ks[buf][(kb * 16 + c16) * KP + step * 32 + g4 * 8];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qb][step], s[kb][qb], 0, 0, 0);
-      }
-    }
-    const bool full = kt0 + AT_BK <= ke;
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float sv[4][4];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = s[kb][qb][r] * sc;
-          if (!full && kt0 + kb * 16 + g4 * 4 + r >= ke) v = -INFINITY;
-          sv[kb][r] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mnew = fmaxf(m_run[qb], tmax);
-      const float alpha = exp2f(m_run[qb] - mnew);
-      float rs = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = exp2f(sv[kb][r] - mnew);
-          sv[kb][r] = p;
-          rs += p;
-        }
-      rs += __shfl_xor(rs, 16);
-      rs += __shfl_xor(rs, 32);
-      l_run[qb] = l_run[qb] * alpha + rs;
-      m_run[qb] = mnew;
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) o[db][qb] *= alpha;
-#pragma unroll
-      for (int st2 = 0; st2 < 2; ++st2) {
-        bf16x8 v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = (__bf16)sv[2 * st2][r];
-          v[4 + r] = (__bf16)sv[2 * st2 + 1][r];
-        }
-        pb[qb][st2] = v;
-      }
-    }
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-#pragma unroll
-      for (int st2 = 0; st2 < 2; ++st2) {
-        const uint16_t *vr = &Vt[buf][(db * 16 + c16) * VP + st2 * 32 + g4 * 4];
-        const bf16x4 lo = *(const bf16x4 *)vr;
-        const bf16x4 hi = *(const bf16x4 *)(vr + 16);
-        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qb][st2], o[db][qb], 0, 0, 0);
-      }
-    }
-    // rebuild tile+1 into the other buffer
-    if (tile + 1 < n_tiles) dequant_store(buf ^ 1, id_next);
-    id_next = id_after;
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int q = blockIdx.x * AT_BQ + wave * 32 + qb * 16 + c16;
-    if (q >= a.n_q) continue;
-    const bool empty = l_run[qb] == 0.0f;
-    const float inv_l = empty ? 0.0f : 1.0f / l_run[qb];
-    const float lse = empty ? -INFINITY : (m_run[qb] + log2f(l_run[qb])) * 0.6931471805599453f;
-    if (a.n_splits == 1) {
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const uint64_t off = (uint64_t(h) * a.n_q + q) * D + db * 16 + g4 * 4;
-        const floatx4 v = o[db][qb] * inv_l;
-        if (a.out_bf16) {
-          uint16_t *op = (uint16_t *)a.out + off;
-          const uint32_t p0 = uint32_t(f32_to_bf16_bits(v[0])) | (uint32_t(f32_to_bf16_bits(v[1])) << 16);
-          const uint32_t p1 = uint32_t(f32_to_bf16_bits(v[2])) | (uint32_t(f32_to_bf16_bits(v[3])) << 16);
-          *(uint2 *)op = make_uint2(p0, p1);
-        } else {
-          *(float4 *)((float *)a.out + off) = make_float4(v[0], v[1], v[2], v[3]);
-        }
-      }
-      if (a.lse && g4 == 0) a.lse[uint64_t(h) * a.n_q + q] = lse;
-    } else {
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const uint64_t off = ((uint64_t(split) * L.H + h) * a.n_q + q) * D + db * 16 + g4 * 4;
-        const floatx4 v = o[db][qb] * inv_l;
-        *(float4 *)(a.part_o + off) = make_float4(v[0], v[1], v[2], v[3]);
-      }
-      if (g4 == 0) a.part_lse[(uint64_t(split) * L.H + h) * a.n_q + q] = lse;
-    }
-  }
-}
-
-// Attention, version 3 (used by qkv_attend).
-//
-// Same block shape and load pipeline as k_attend2 (8 waves, 32 queries each,
-// 64-key tiles double-buffered in LDS, ids two tiles ahead, packed data one
-// tile ahead), with the VALU work per score cut down:
-//  * K and V are rebuilt exactly as the reconstruction defines them (fp32,
-//    stage by stage, then nearest-even bf16); 2-bit codes are widened four at
-//    a time: a masked code word holds four codes in four bytes, which the
-//    byte-to-float conversions (v_cvt_f32_ubyte0..3) widen directly;
-//  * K/V items alternate between neighbouring threads so every wave shares
-//    the rebuild work evenly;
-//  * the softmax scale is folded into the exponent's fma; the running max is
-//    only raised (and O, l rescaled) when a tile's max exceeds it by more
-//    than 8 (log2 units), so exponentials stay <= 256;
-//  * row sums of P come from one extra MFMA against a fragment of ones.
 constexpr float AT3_TAU = 8.0f;
 
 template <int D, int G, int BITS, bool CB_BF16, int SMAX>
