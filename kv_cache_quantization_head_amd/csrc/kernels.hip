@@ -871,16 +871,16 @@ __global__ __launch_bounds__(256) void k_reconstruct(ReconArgs a, int64_t out_to
 // Fused read of the packed cache.  Block = 8 waves (two per SIMD) = 256
 // queries of one head, 32 per wave; grid = (query blocks, heads, KV splits).
 // Per 64-key tile the block rebuilds K and V in bf16 into a double-buffered
-// LDS tile (K as [key][d]; V transposed as [d][key] with the key column
-// XOR-swizzled by 8*(d/32 mod 4)); each wave then computes S^T = K Q^T with
+// LDS tile (K and V both as [key][d]; V is read for the PV step with
+// transposing LDS loads); each wave then computes S^T = K Q^T with
 // v_mfma_f32_16x16x32_bf16 (one lane's accumulator column is one query, so
 // softmax statistics need two cross-lane exchanges), runs the online softmax
 // in fp32 and accumulates O^T += V^T P^T with the probabilities rounded to
 // bf16.  The key order inside a 32-key MFMA step is permuted identically in
 // both operands so that P^T comes straight from the S^T accumulators.
 //
-//  * Rebuild items: one (tensor, key, group of G channels) per thread, K on
-//    even and V on odd threads (every wave runs the same code; the four
+//  * Rebuild items: one (tensor, key, 32 channels) per thread, K on even and
+//    V on odd threads (every wave runs the same code, stores included; the
 //    threads of a key read one centroid row).  The rebuild is
 //    bf16(fl32 chain: c + sum_s z_s, then fmaf(q_s, sigma_s, .) per stage);
 //    2-bit codes are widened four at a time from one masked code word
@@ -898,6 +898,16 @@ constexpr int AT_WAVES = 8;
 constexpr int AT_BQ = 32 * AT_WAVES;
 constexpr int AT_BK = 64;
 
+// Transposing LDS load (ds_read_b64_tr_b16): within each 16-lane group,
+// lane l receives element l%4 of the 8-byte rows addressed by lanes
+// l/4 + 4j (j = 0..3), as element j.
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t *p) {
+  const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4 *)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
 __device__ __forceinline__ int chunk_of_lds(const int32_t *starts, int n_chunks, int t) {
   int lo = 0, hi = n_chunks - 1;
   while (lo < hi) {
@@ -913,15 +923,18 @@ template <int D, int G, int BITS, bool CB_BF16, int SMAX>
 __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   // SMAX = the number of PRQ stages (a template parameter so that the staging
   // registers are sized exactly)
-  constexpr int NG = D / G;
+  constexpr int IC = 32;                   // channels of one rebuild item
+  constexpr int NI = D / IC;               // items per key and tensor
   constexpr int KP = D + 8;                // bf16 elements per K row in LDS
-  constexpr int VP = AT_BK + 8;            // bf16 elements per V^T row in LDS
+  constexpr int VP = D + 16;               // bf16 elements per V row in LDS (rows 8 banks
+                                           // apart: conflict-free transposing reads)
   constexpr int EB = CB_BF16 ? 2 : 4;
-  constexpr int KW = G * BITS / 32;        // code words of an item (one key, one group)
-  constexpr int KC = G * EB / 16;          // uint4 of an item's centroid slice
-  static_assert(2 * 64 * NG <= 512, "one item per thread");
+  constexpr int KW = IC * BITS / 32;       // code words of an item
+  constexpr int KC = IC * EB / 16;         // uint4 of an item's centroid slice
+  static_assert(2 * 64 * NI <= 512, "one item per thread");
+  static_assert(G % IC == 0, "an item lies inside one quantization group");
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][AT_BK * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][AT_BK * VP];
   __shared__ int32_t starts_s[kMaxChunks + 1];
   __shared__ int32_t nch_s;
 
@@ -932,16 +945,14 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   const int g4 = lane >> 4, c16 = lane & 15;
   const float sc = 1.4426950408889634f / sqrtf(float(D));
 
-  // Rebuild items: one (tensor, key, group of G channels) per thread, K on
-  // even and V on odd threads, so every wave runs the same rebuild code and
-  // the four threads of one key read one centroid row.  V is stored
-  // transposed ([d][key]) with the key column XOR-swizzled by 8*(d/32 mod 4),
-  // which spreads the rows written by one store over different banks and
-  // keeps each aligned run of 4 keys contiguous for the PV operand reads.
+  // Rebuild items: one (tensor, key, 32 channels) per thread, K on even and
+  // V on odd threads, so every wave runs the same rebuild code and the
+  // threads of one key read one centroid row.  K and V tiles are
+  // both stored [key][d]; the PV step reads V with transposing LDS loads.
   const int it_kv = tid & 1, it_rem = tid >> 1;
-  const bool has_item = it_rem < 64 * NG;
-  const int it_key = it_rem / NG, it_g = it_rem % NG;
-  const int it_ch = it_g * G;
+  const bool has_item = it_rem < 64 * NI;
+  const int it_key = it_rem / NI;
+  const int it_ch = (it_rem % NI) * IC, it_g = it_ch / G;
   const uint8_t *st = it_kv ? a.stream_v : a.stream_k;
   const uint8_t *idp = st + L.ids_off + uint64_t(h) * L.ids_head;
 
@@ -1016,7 +1027,7 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
 #pragma unroll
     for (int s2 = 0; s2 < SMAX; ++s2) {
       const uint8_t *cp = st + L.codes_off + uint64_t(s2) * L.codes_stage + uint64_t(h) * L.codes_head +
-                          uint64_t(t) * L.codes_token + uint64_t(it_g) * (G * BITS / 8);
+                          uint64_t(t) * L.codes_token + uint64_t(it_ch) * BITS / 8;
       if constexpr (KW == 2) {
         const uint2 v = *(const uint2 *)cp;
         R.codes[s2][0] = v.x; R.codes[s2][1] = v.y;
@@ -1037,7 +1048,10 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     if constexpr (BITS == 2) {
 #pragma unroll
       for (int sh = 0; sh < 4; ++sh) {
-        const uint32_t m = (cw[0] >> (2 * sh)) & 0x03030303u;  // bytes: channels 4*byte + sh
+        uint32_t m = (cw[0] >> (2 * sh)) & 0x03030303u;  // bytes: channels 4*byte + sh
+        // hide m's known-zero bits so that each byte is widened by one
+        // byte-to-float conversion instead of a bit-field extract + convert
+        asm("" : "+v"(m));
 #pragma unroll
         for (int by = 0; by < 4; ++by) xh[4 * by + sh] = fmaf(float((m >> (8 * by)) & 0xffu), sf, xh[4 * by + sh]);
       }
@@ -1046,7 +1060,8 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
       for (int w = 0; w < 2; ++w)
 #pragma unroll
         for (int sh = 0; sh < 2; ++sh) {
-          const uint32_t m = (cw[w] >> (4 * sh)) & 0x0f0f0f0fu;  // bytes: channels 8w + 2*byte + sh
+          uint32_t m = (cw[w] >> (4 * sh)) & 0x0f0f0f0fu;  // bytes: channels 8w + 2*byte + sh
+          asm("" : "+v"(m));
 #pragma unroll
           for (int by = 0; by < 4; ++by)
             xh[8 * w + 2 * by + sh] = fmaf(float((m >> (8 * by)) & 0xffu), sf, xh[8 * w + 2 * by + sh]);
@@ -1072,40 +1087,32 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   // ulps of a bf16 rounding boundary.
   auto dequant_store = [&](int buf, int id) {
     if (!has_item) return;
-    float xh[G];
+    float xh[IC];
     if (id >= 0) {
       float zs = 0.0f;
 #pragma unroll
       for (int s2 = 0; s2 < SMAX; ++s2) zs += f16_bits_to_f32(uint16_t(R.meta[s2] >> 16));
 #pragma unroll
-      for (int e = 0; e < G; ++e) xh[e] = cent_f32(e) + zs;
+      for (int e = 0; e < IC; ++e) xh[e] = cent_f32(e) + zs;
 #pragma unroll
       for (int s2 = 0; s2 < SMAX; ++s2) {
         const float sf = f16_bits_to_f32(uint16_t(R.meta[s2] & 0xffffu));
 #pragma unroll
-        for (int b16 = 0; b16 < G / 16; ++b16) stage16(&R.codes[s2][b16 * (BITS / 2)], sf, &xh[16 * b16]);
+        for (int b16 = 0; b16 < IC / 16; ++b16) stage16(&R.codes[s2][b16 * (BITS / 2)], sf, &xh[16 * b16]);
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < G; ++e) xh[e] = 0.0f;
+      for (int e = 0; e < IC; ++e) xh[e] = 0.0f;
     }
-    if (it_kv == 0) {
-      uint16_t *dst = &Ks[buf][it_key * KP + it_ch];
+    uint16_t *dst = it_kv ? &Vs[buf][it_key * VP + it_ch] : &Ks[buf][it_key * KP + it_ch];
 #pragma unroll
-      for (int j = 0; j < G; j += 8) {
-        uint4 v;
-        v.x = uint32_t(f32_to_bf16_bits(xh[j])) | (uint32_t(f32_to_bf16_bits(xh[j + 1])) << 16);
-        v.y = uint32_t(f32_to_bf16_bits(xh[j + 2])) | (uint32_t(f32_to_bf16_bits(xh[j + 3])) << 16);
-        v.z = uint32_t(f32_to_bf16_bits(xh[j + 4])) | (uint32_t(f32_to_bf16_bits(xh[j + 5])) << 16);
-        v.w = uint32_t(f32_to_bf16_bits(xh[j + 6])) | (uint32_t(f32_to_bf16_bits(xh[j + 7])) << 16);
-        *(uint4 *)(dst + j) = v;
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < G; ++j) {
-        const int d = it_ch + j;
-        Vt[buf][d * VP + (it_key ^ (8 * ((d >> 5) & 3)))] = f32_to_bf16_bits(xh[j]);
-      }
+    for (int j = 0; j < IC; j += 8) {
+      uint4 v;
+      v.x = uint32_t(f32_to_bf16_bits(xh[j])) | (uint32_t(f32_to_bf16_bits(xh[j + 1])) << 16);
+      v.y = uint32_t(f32_to_bf16_bits(xh[j + 2])) | (uint32_t(f32_to_bf16_bits(xh[j + 3])) << 16);
+      v.z = uint32_t(f32_to_bf16_bits(xh[j + 4])) | (uint32_t(f32_to_bf16_bits(xh[j + 5])) << 16);
+      v.w = uint32_t(f32_to_bf16_bits(xh[j + 6])) | (uint32_t(f32_to_bf16_bits(xh[j + 7])) << 16);
+      *(uint4 *)(dst + j) = v;
     }
   };
 
@@ -1168,14 +1175,18 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
         pb[qb][st2] = v;
       }
     }
+    // A operand of O^T += V^T P^T for d-block db and keys of S^T blocks 2*st2
+    // (k = 0..3 of each lane group) and 2*st2+1 (k = 4..7): one transposing
+    // load per half.  In a 16-lane group the load hands lane l element l%4 of
+    // the 4-element rows loaded by lanes l/4 + 4j, j = 0..3; lane l therefore
+    // addresses key 16*kb + 4*g4 + l/4, channels 4*(l%4) .. +3 of the block.
+    const uint16_t *vbase = &Vs[buf][(4 * g4 + (c16 >> 2)) * VP + 4 * (c16 & 3)];
 #pragma unroll
     for (int db = 0; db < D / 16; ++db) {
 #pragma unroll
       for (int st2 = 0; st2 < 2; ++st2) {
-        const int vd = db * 16 + c16, sw = 8 * ((vd >> 5) & 3);
-        const uint16_t *vrow = &Vt[buf][vd * VP];
-        const bf16x4 lo = *(const bf16x4 *)(vrow + ((st2 * 32 + g4 * 4) ^ sw));
-        const bf16x4 hi = *(const bf16x4 *)(vrow + ((st2 * 32 + 16 + g4 * 4) ^ sw));
+        const bf16x4 lo = lds_read_tr16(vbase + (32 * st2) * VP + 16 * db);
+        const bf16x4 hi = lds_read_tr16(vbase + (32 * st2 + 16) * VP + 16 * db);
         const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb)
