@@ -16,11 +16,14 @@ ARCH = os.environ.get("QKV_OFFLOAD_ARCH", "gfx950")
 # -ffp-contract=off: the codec's fp32 arithmetic is specified operation by
 #   operation (fused multiply-adds are written explicitly as fmaf);
 # -fno-gpu-flush-denormals-to-zero: IEEE subnormals in fp32;
-# -packed-fp32-ops off: no packed fp32 VALU instructions are generated.
+# -packed-fp32-ops off: no packed fp32 VALU instructions are generated;
+# -amdgpu-mfma-vgpr-form: MFMA accumulators stay in VGPRs (the k-means
+#   screening reads every accumulator right after its MFMA).
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

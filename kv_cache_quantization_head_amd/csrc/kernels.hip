@@ -53,6 +53,12 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// median of three unsigned values (v_med3_u32)
+__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
+  uint32_t r;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);
 }
@@ -255,8 +261,8 @@ __global__ __launch_bounds__(256) void k_assign(EncodeArgs a) {
 // adds x.c, so acc = -D/2 (D the squared distance).  Each lane owns one token
 // column and four cluster rows; the fp32 bits of acc with the low 9 bits
 // replaced by the cluster index form a key whose unsigned order is the order
-// of D (acc <= 0 up to rounding), ties to the lowest index, and a running
-// (min, second min) of the keys is kept with v_min / v_med3.  The screening
+// of D (acc <= 0 up to rounding), ties to the lowest index, and the three
+// smallest keys are kept with one v_min and two v_med3 per key.  The screening
 // error (MFMA accumulation over D+1 terms, rounding of the start value, the
 // 9 dropped bits) is below E; a token whose two best keys are within 2E goes
 // to the exact fp64 decision shared with k_assign.
@@ -335,7 +341,9 @@ __global__ __launch_bounds__(256) void k_assign_mfma(EncodeArgs a, int tiles_per
       for (int step = 0; step < STEPS; ++step)
         ca[step] = *(const bf16x8 *)(cbs + (k0 + c16) * KP + step * 32 + g4 * 8);
       const float4 ch = *(const float4 *)(cnh + k0 + g4 * 4);
-      const uint32_t kidx = uint32_t(k0 + g4 * 4);
+      uint32_t kidx[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) kidx[r] = uint32_t(k0 + g4 * 4 + r);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         floatx4 acc = {ch.x + xnh[nt], ch.y + xnh[nt], ch.z + xnh[nt], ch.w + xnh[nt]};
@@ -344,9 +352,11 @@ __global__ __launch_bounds__(256) void k_assign_mfma(EncodeArgs a, int tiles_per
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[step], xf[nt][step], acc, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const uint32_t key = (__float_as_uint(acc[r]) & ~0x1ffu) | (kidx + r);
-          const uint32_t n3 = max(m2[nt], min(m3[nt], key));
-          const uint32_t n2 = max(m1[nt], min(m2[nt], key));
+          // with m1 <= m2 <= m3: new third = med3(m2, m3, key), new second =
+          // med3(m1, m2, key), new first = min(m1, key)
+          const uint32_t key = (__float_as_uint(acc[r]) & ~0x1ffu) | kidx[r];
+          const uint32_t n3 = umed3(m2[nt], m3[nt], key);
+          const uint32_t n2 = umed3(m1[nt], m2[nt], key);
           m1[nt] = min(m1[nt], key);
           m2[nt] = n2;
           m3[nt] = n3;
