@@ -26,6 +26,8 @@
 // written as fmaf where the definition has one).
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include <type_traits>
@@ -251,9 +253,10 @@ __global__ __launch_bounds__(256) void k_assign(EncodeArgs a) {
   }
 }
 
-// MFMA screening for bf16 caches with C <= 512.  blockIdx.x = group of
-// token tiles, y = head, z = stream; 4 waves, each owning 64 tokens of a
-// 256-token tile (four 16-token MFMA column blocks).
+// MFMA screening for bf16 caches with C <= 512.  The (stream, head, 256-token
+// tile) space is flattened; block b takes tiles_per_block consecutive tiles
+// (restaging the codebook when the (stream, head) changes); 8 waves, each
+// owning 32 tokens of a tile (two 16-token MFMA column blocks).
 //
 // The head's codebook (bf16, rows padded to the 16-row MFMA block) and
 // -||c||^2/2 are staged in LDS once per block.  For a 16-cluster block the
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(256) void k_assign(EncodeArgs a) {
 // 9 dropped bits) is below E; a token whose two best keys are within 2E goes
 // to the exact fp64 decision shared with k_assign.
 template <int D>
-__global__ __launch_bounds__(256) void k_assign_mfma(EncodeArgs a, int tiles_per_block) {
+__global__ __launch_bounds__(512) void k_assign_mfma(EncodeArgs a, int tiles_per_block, int streams) {
   constexpr int KP = D + 8;                 // LDS row pitch (bf16 elements)
   constexpr int STEPS = D / 32;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -277,38 +280,49 @@ __global__ __launch_bounds__(256) void k_assign_mfma(EncodeArgs a, int tiles_per
   float *cnh = (float *)(smem + size_t(C16) * KP * 2);       // [C16]
   __shared__ uint32_t cmax_bits;
 
-  const int h = blockIdx.y, z = blockIdx.z, lrel = z >> 1, kv = z & 1;
-  uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, kv);
-  const uint16_t *x = (const uint16_t *)((kv ? a.v_in : a.k_in)) + (uint64_t(lrel) * L.H + h) * uint64_t(a.n) * D;
-  const uint16_t *cb = (const uint16_t *)(st + L.cb_off + uint64_t(a.slot) * L.cb_chunk + uint64_t(h) * L.cb_head);
-  const float *cn = (const float *)(st + L.cn_off + uint64_t(a.slot) * L.cn_chunk + uint64_t(h) * L.cn_head);
-  uint8_t *ids = st + L.ids_off + uint64_t(h) * L.ids_head;
-
-  if (threadIdx.x == 0) cmax_bits = 0;
-  __syncthreads();
-  for (int i = threadIdx.x; i < C16 * (D / 8); i += blockDim.x) {
-    const int k = i / (D / 8), c8 = i % (D / 8);
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (k < L.C) v = *(const uint4 *)(cb + uint64_t(k) * D + c8 * 8);
-    *(uint4 *)(cbs + k * KP + c8 * 8) = v;
-  }
-  for (int k = threadIdx.x; k < C16; k += blockDim.x) {
-    const float c = k < L.C ? cn[k] : 0.0f;
-    cnh[k] = k < L.C ? -0.5f * c : -INFINITY;
-    if (k < L.C) atomicMax(&cmax_bits, __float_as_uint(c));
-  }
-  __syncthreads();
-  const float cmax = __uint_as_float(cmax_bits);
-
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g4 = lane >> 4, c16 = lane & 15;
   const int n_tiles = (a.n + 255) / 256;
-  for (int tile = blockIdx.x * tiles_per_block; tile < min(n_tiles, (blockIdx.x + 1) * tiles_per_block); ++tile) {
-    const int tb = tile * 256 + wave * 64;
-    bf16x8 xf[4][STEPS];
-    float xnh[4], xn[4];
+  const int64_t total = int64_t(n_tiles) * L.H * streams;
+  int cur = -1;                             // (stream, head) whose codebook is in LDS
+  const uint16_t *x = nullptr;
+  uint8_t *ids = nullptr;
+  float cmax = 0.0f;
+  for (int64_t f = int64_t(blockIdx.x) * tiles_per_block;
+       f < min(total, int64_t(blockIdx.x + 1) * tiles_per_block); ++f) {
+    const int tile = int(f % n_tiles);
+    const int zh = int(f / n_tiles);
+    if (zh != cur) {
+      // stage the codebook of (stream, head) zh
+      cur = zh;
+      const int h = zh % L.H, z = zh / L.H, lrel = z >> 1, kv = z & 1;
+      uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, kv);
+      x = (const uint16_t *)((kv ? a.v_in : a.k_in)) + (uint64_t(lrel) * L.H + h) * uint64_t(a.n) * D;
+      const uint16_t *cb = (const uint16_t *)(st + L.cb_off + uint64_t(a.slot) * L.cb_chunk + uint64_t(h) * L.cb_head);
+      const float *cn = (const float *)(st + L.cn_off + uint64_t(a.slot) * L.cn_chunk + uint64_t(h) * L.cn_head);
+      ids = st + L.ids_off + uint64_t(h) * L.ids_head;
+      __syncthreads();  // previous codebook no longer read
+      if (threadIdx.x == 0) cmax_bits = 0;
+      __syncthreads();
+      for (int i = threadIdx.x; i < C16 * (D / 8); i += blockDim.x) {
+        const int k = i / (D / 8), c8 = i % (D / 8);
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (k < L.C) v = *(const uint4 *)(cb + uint64_t(k) * D + c8 * 8);
+        *(uint4 *)(cbs + k * KP + c8 * 8) = v;
+      }
+      for (int k = threadIdx.x; k < C16; k += blockDim.x) {
+        const float c = k < L.C ? cn[k] : 0.0f;
+        cnh[k] = k < L.C ? -0.5f * c : -INFINITY;
+        if (k < L.C) atomicMax(&cmax_bits, __float_as_uint(c));
+      }
+      __syncthreads();
+      cmax = __uint_as_float(cmax_bits);
+    }
+    const int tb = tile * 256 + wave * 32;
+    bf16x8 xf[2][STEPS];
+    float xnh[2], xn[2];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < 2; ++nt) {
       const int t = tb + nt * 16 + c16;
       float ss = 0.0f;
 #pragma unroll
@@ -332,9 +346,9 @@ __global__ __launch_bounds__(256) void k_assign_mfma(EncodeArgs a, int tiles_per
       xn[nt] = ss;
       xnh[nt] = -0.5f * ss;
     }
-    uint32_t m1[4], m2[4], m3[4];
+    uint32_t m1[2], m2[2], m3[2];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) m1[nt] = m2[nt] = m3[nt] = 0xffffffffu;
+    for (int nt = 0; nt < 2; ++nt) m1[nt] = m2[nt] = m3[nt] = 0xffffffffu;
     for (int k0 = 0; k0 < C16; k0 += 16) {
       bf16x8 ca[STEPS];
 #pragma unroll
@@ -345,7 +359,7 @@ __global__ __launch_bounds__(256) void k_assign_mfma(EncodeArgs a, int tiles_per
 #pragma unroll
       for (int r = 0; r < 4; ++r) kidx[r] = uint32_t(k0 + g4 * 4 + r);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
+      for (int nt = 0; nt < 2; ++nt) {
         floatx4 acc = {ch.x + xnh[nt], ch.y + xnh[nt], ch.z + xnh[nt], ch.w + xnh[nt]};
 #pragma unroll
         for (int step = 0; step < STEPS; ++step)
@@ -365,7 +379,7 @@ __global__ __launch_bounds__(256) void k_assign_mfma(EncodeArgs a, int tiles_per
     }
     // merge the sorted triples of the four lanes that share a token column
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
       for (int off = 16; off <= 32; off <<= 1) {
         const uint32_t b1 = __shfl_xor(m1[nt], off), b2 = __shfl_xor(m2[nt], off), b3 = __shfl_xor(m3[nt], off);
@@ -380,7 +394,7 @@ __global__ __launch_bounds__(256) void k_assign_mfma(EncodeArgs a, int tiles_per
       return m == 0xffffffffu ? INFINITY : -2.0f * __uint_as_float(m & ~0x1ffu);
     };
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
+    for (int nt = 0; nt < 2; ++nt) {
       const int t = tb + nt * 16 + c16;
       const bool valid = t < a.n && g4 == 0;
       const float d1 = decode(m1[nt]), d2 = decode(m2[nt]), d3 = decode(m3[nt]);
@@ -1375,14 +1389,16 @@ static void launch_assign_t(const EncodeArgs &a, int streams, hipStream_t st) {
   if (BF && a.L.C <= 512) {
     // MFMA screening; about four 256-token tiles per block so that the
     // codebook is staged in LDS once per 1024 tokens
-    const int n_tiles = int(cdiv(a.n, 256));
-    const int per_block = n_tiles >= 16 ? 4 : 1;
+    // about 512 blocks (two per compute unit of a 256-CU device, each
+    // holding its codebook in LDS), each taking an equal run of tiles
+    const int64_t total = cdiv(a.n, 256) * int64_t(a.L.H) * streams;
+    const int per_block = int(std::max<int64_t>(1, cdiv(total, 512)));
     const int C16 = (a.L.C + 15) & ~15;
     const size_t lds = size_t(C16) * (D + 8) * 2 + size_t(C16) * 4;
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_assign_mfma<D>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    hipLaunchKernelGGL((k_assign_mfma<D>), dim3(cdiv(n_tiles, per_block), a.L.H, streams), dim3(256), lds, st,
-                       a, per_block);
+    hipLaunchKernelGGL((k_assign_mfma<D>), dim3(unsigned(cdiv(total, per_block))), dim3(512), lds, st,
+                       a, per_block, streams);
     return;
   }
   hipLaunchKernelGGL((k_assign<D, BF>), dim3(cdiv(a.n, 256), a.L.H, streams), dim3(256), 0, st, a);
