@@ -146,10 +146,7 @@ extern "C" int qkv_attend(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t 
     else
       ctx->n_cu = 256;
   }
-  int splits = attention_splits(p, n_keys, n_q, ctx->n_cu);
-  int64_t split_len = (n_keys + splits - 1) / splits;
-  split_len = (split_len + 63) / 64 * 64;
-  splits = int((n_keys + split_len - 1) / split_len);
+  const AttnSplit w = attention_split(p, n_keys, n_q, ctx->n_cu);
 
   AttnArgs a{};
   a.L = dev_layout(p);
@@ -159,8 +156,11 @@ extern "C" int qkv_attend(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t 
   a.q_bf16 = q_dtype == QKV_BF16;
   a.n_q = int32_t(n_q);
   a.n_keys = int32_t(n_keys);
-  a.split_len = int32_t(split_len);
-  a.n_splits = splits;
+  a.n_qblocks = int32_t(w.n_qblocks);
+  a.n_ktiles = int32_t(w.n_ktiles);
+  a.units_per_block = int32_t(w.units_per_block);
+  a.max_segments = int32_t(w.max_segments);
+  a.xcd_remap = w.n_blocks % 8 == 0;
   a.out = d_out;
   a.out_bf16 = out_dtype == QKV_BF16;
   a.lse = d_lse;

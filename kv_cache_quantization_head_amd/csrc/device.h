@@ -75,12 +75,18 @@ struct AttnArgs {
   const uint8_t *stream_k, *stream_v;   // stream bases of the layer
   const void *q;                        // [H][n_q][D]
   int32_t q_bf16;
-  int32_t n_q, n_keys, split_len, n_splits;
-  void *out;                            // final [H][n_q][D] when n_splits == 1
+  int32_t n_q, n_keys;
+  // stream-K work split over (head, query block, key tile) units
+  int32_t n_qblocks;                    // query blocks of 256
+  int32_t n_ktiles;                     // key tiles of 64 (at least 1)
+  int32_t units_per_block;              // consecutive units per block
+  int32_t max_segments;                 // most blocks sharing one query block
+  int32_t xcd_remap;                    // number blocks XCD by XCD (grid % 8 == 0)
+  void *out;                            // final [H][n_q][D]
   int32_t out_bf16;
   float *lse;                           // final [H][n_q] or null
-  float *part_o;                        // [splits][H][n_q][D] when n_splits > 1
-  float *part_lse;                      // [splits][H][n_q]
+  float *part_o;                        // [max_segments][H][n_q][D] partials
+  float *part_lse;                      // [max_segments][H][n_q]
 };
 
 struct XlArgs {

@@ -963,7 +963,6 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   __shared__ int32_t nch_s;
 
   const DevLayout &L = a.L;
-  const int h = blockIdx.y, split = blockIdx.z;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int g4 = lane >> 4, c16 = lane & 15;
@@ -978,340 +977,378 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   const int it_key = it_rem / NI;
   const int it_ch = (it_rem % NI) * IC, it_g = it_ch / G;
   const uint8_t *st = it_kv ? a.stream_v : a.stream_k;
-  const uint8_t *idp = st + L.ids_off + uint64_t(h) * L.ids_head;
 
   if (tid == 0) nch_s = ((const StreamHeader *)(a.stream_k + L.header_off))->n_chunks;
   __syncthreads();
   for (int i = tid; i < nch_s; i += blockDim.x)
     starts_s[i] = ((const StreamHeader *)(a.stream_k + L.header_off))->start[i];
 
-  const int ks = split * a.split_len;
-  const int ke = min(a.n_keys, ks + a.split_len);
-  const int n_tiles = ke > ks ? (ke - ks + AT_BK - 1) / AT_BK : 0;
+  // Stream-K work split: the (head, query block, key tile) units are dealt
+  // out in equal consecutive runs, one run per block; a block walks its run
+  // segment by segment (one segment per query block it touches).  A segment
+  // that covers all key tiles of its query block writes the result; the
+  // others write a partial (O, LSE) into slot (block - first block of the
+  // query block) for the merge kernel.  Blocks are numbered so that each XCD
+  // (blocks are dealt to the 8 XCDs round robin) gets a consecutive range of
+  // runs: the query blocks of one head then share that XCD's L2.
+  const int lb = a.xcd_remap ? (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int64_t T = a.n_ktiles, U = a.units_per_block;
+  const int64_t total = T * a.n_qblocks * L.H;
+  int64_t u = int64_t(lb) * U;
+  const int64_t u_end = min(total, u + U);
+  __syncthreads();  // chunk table in LDS
+  while (u < u_end) {
+    const int64_t seg = u / T;
+    const int h = int(seg / a.n_qblocks), qblk = int(seg % a.n_qblocks);
+    const int t0 = int(u % T);
+    const int t1 = int(min(T, t0 + (u_end - u)));
+    const int slot = (t0 == 0 && t1 == T) ? -1 : int(lb - (seg * T) / U);
+    u += t1 - t0;
+    const uint8_t *idp = st + L.ids_off + uint64_t(h) * L.ids_head;
+    const int ks = t0 * AT_BK;
+    const int ke = min(a.n_keys, t1 * AT_BK);
+    const int n_tiles = ke > ks ? (ke - ks + AT_BK - 1) / AT_BK : 0;
 
-  // query fragments (B operand of S^T = K Q^T): Q[q][32*step + 8*g4 .. +8] in bf16
-  bf16x8 qf[2][D / 32];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int q = blockIdx.x * AT_BQ + wave * 32 + qb * 16 + c16;
-#pragma unroll
-    for (int step = 0; step < D / 32; ++step) {
-      bf16x8 v;
-      if (q < a.n_q) {
-        const uint64_t off = (uint64_t(h) * a.n_q + q) * D + step * 32 + g4 * 8;
-        if (a.q_bf16) {
-          v = *(const bf16x8 *)((const uint16_t *)a.q + off);
-        } else {
-          const float *qp = (const float *)a.q + off;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (__bf16)qp[e];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
-      }
-      qf[qb][step] = v;
-    }
-  }
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
-
-  floatx4 o[D / 16][2];
-  floatx4 lacc[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    lacc[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) o[db][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
-  float m_run[2] = {-INFINITY, -INFINITY};
-
-  // id of the item's key in a tile (-1: no key)
-  auto load_ids = [&](int tile) -> int {
-    if (!has_item || tile >= n_tiles) return -1;
-    const int t = ks + tile * AT_BK + it_key;
-    if (t >= ke) return -1;
-    return L.id_bytes == 1 ? int(idp[t]) : int(((const uint16_t *)idp)[t]);
-  };
-  struct Regs {
-    uint32_t codes[SMAX][KW];
-    uint32_t meta[SMAX];
-    uint4 cent[KC];
-  } R;
-  // packed data of the item's key t: centroid slice, codes, (sigma, z)
-  auto load_data = [&](int tile, int id) {
-    if (id < 0) return;
-    const int t = ks + tile * AT_BK + it_key;
-    const int slot = chunk_of_lds(starts_s, nch_s, t);
-    const uint8_t *crow = st + L.cb_off + uint64_t(slot) * L.cb_chunk + uint64_t(h) * L.cb_head +
-                          uint64_t(id) * D * EB + uint64_t(it_ch) * EB;
-#pragma unroll
-    for (int i = 0; i < KC; ++i) R.cent[i] = *(const uint4 *)(crow + 16 * i);
-#pragma unroll
-    for (int s2 = 0; s2 < SMAX; ++s2) {
-      const uint8_t *cp = st + L.codes_off + uint64_t(s2) * L.codes_stage + uint64_t(h) * L.codes_head +
-                          uint64_t(t) * L.codes_token + uint64_t(it_ch) * BITS / 8;
-      if constexpr (KW == 2) {
-        const uint2 v = *(const uint2 *)cp;
-        R.codes[s2][0] = v.x; R.codes[s2][1] = v.y;
-      } else {
-#pragma unroll
-        for (int w = 0; w < KW; w += 4) {
-          const uint4 v = *(const uint4 *)(cp + 4 * w);
-          R.codes[s2][w] = v.x; R.codes[s2][w + 1] = v.y; R.codes[s2][w + 2] = v.z; R.codes[s2][w + 3] = v.w;
-        }
-      }
-      R.meta[s2] = *((const uint32_t *)(st + L.meta_off + uint64_t(s2) * L.meta_stage + uint64_t(h) * L.meta_head +
-                                        uint64_t(t) * L.meta_token) + it_g);
-    }
-  };
-  // one PRQ stage folded into 16 channels: xh[c] = fmaf(q_c, sigma, xh[c]) (the
-  // zero points of all stages are added to the centroid beforehand)
-  auto stage16 = [&](const uint32_t *cw, float sf, float *xh) {
-    if constexpr (BITS == 2) {
-#pragma unroll
-      for (int sh = 0; sh < 4; ++sh) {
-        uint32_t m = (cw[0] >> (2 * sh)) & 0x03030303u;  // bytes: channels 4*byte + sh
-        // hide m's known-zero bits so that each byte is widened by one
-        // byte-to-float conversion instead of a bit-field extract + convert
-        asm("" : "+v"(m));
-#pragma unroll
-        for (int by = 0; by < 4; ++by) xh[4 * by + sh] = fmaf(float((m >> (8 * by)) & 0xffu), sf, xh[4 * by + sh]);
-      }
-    } else {
-#pragma unroll
-      for (int w = 0; w < 2; ++w)
-#pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-          uint32_t m = (cw[w] >> (4 * sh)) & 0x0f0f0f0fu;  // bytes: channels 8w + 2*byte + sh
-          asm("" : "+v"(m));
-#pragma unroll
-          for (int by = 0; by < 4; ++by)
-            xh[8 * w + 2 * by + sh] = fmaf(float((m >> (8 * by)) & 0xffu), sf, xh[8 * w + 2 * by + sh]);
-        }
-    }
-  };
-  // centroid channel e of the item as fp32
-  auto cent_f32 = [&](int e) -> float {
-    if constexpr (CB_BF16) {
-      const uint4 v = R.cent[e >> 3];
-      const uint32_t w = ((e & 7) >> 1) == 0 ? v.x : ((e & 7) >> 1) == 1 ? v.y : ((e & 7) >> 1) == 2 ? v.z : v.w;
-      return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
-    } else {
-      const uint4 v = R.cent[e >> 2];
-      const uint32_t w = (e & 3) == 0 ? v.x : (e & 3) == 1 ? v.y : (e & 3) == 2 ? v.z : v.w;
-      return __uint_as_float(w);
-    }
-  };
-  // Rebuild the item for the products: xh = fmaf(q_S, sigma_S, ... fmaf(q_1,
-  // sigma_1, c + (z_1 + ... + z_S))), then nearest-even bf16.  This differs
-  // from the stage-by-stage reconstruction (c + rhat_1) + rhat_2 ... by a few
-  // fp32 ulps, which changes the bf16 operand only for values within those
-  // ulps of a bf16 rounding boundary.
-  auto dequant_store = [&](int buf, int id) {
-    if (!has_item) return;
-    float xh[IC];
-    if (id >= 0) {
-      float zs = 0.0f;
-#pragma unroll
-      for (int s2 = 0; s2 < SMAX; ++s2) zs += f16_bits_to_f32(uint16_t(R.meta[s2] >> 16));
-#pragma unroll
-      for (int e = 0; e < IC; ++e) xh[e] = cent_f32(e) + zs;
-#pragma unroll
-      for (int s2 = 0; s2 < SMAX; ++s2) {
-        const float sf = f16_bits_to_f32(uint16_t(R.meta[s2] & 0xffffu));
-#pragma unroll
-        for (int b16 = 0; b16 < IC / 16; ++b16) stage16(&R.codes[s2][b16 * (BITS / 2)], sf, &xh[16 * b16]);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < IC; ++e) xh[e] = 0.0f;
-    }
-    uint16_t *dst = it_kv ? &Vs[buf][it_key * VP + it_ch] : &Ks[buf][it_key * KP + it_ch];
-#pragma unroll
-    for (int j = 0; j < IC; j += 8) {
-      uint4 v;
-      v.x = uint32_t(f32_to_bf16_bits(xh[j])) | (uint32_t(f32_to_bf16_bits(xh[j + 1])) << 16);
-      v.y = uint32_t(f32_to_bf16_bits(xh[j + 2])) | (uint32_t(f32_to_bf16_bits(xh[j + 3])) << 16);
-      v.z = uint32_t(f32_to_bf16_bits(xh[j + 4])) | (uint32_t(f32_to_bf16_bits(xh[j + 5])) << 16);
-      v.w = uint32_t(f32_to_bf16_bits(xh[j + 6])) | (uint32_t(f32_to_bf16_bits(xh[j + 7])) << 16);
-      *(uint4 *)(dst + j) = v;
-    }
-  };
-
-  auto compute_tile = [&](int tile) {
-    const int buf = tile & 1;
-    const int kt0 = ks + tile * AT_BK;
-    floatx4 s[4][2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int step = 0; step < D / 32; ++step) {
-        const bf16x8 ka = *(const bf16x8 *)&Ks[buf][(kb * 16 + c16) * KP + step * 32 + g4 * 8];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qb][step], s[kb][qb], 0, 0, 0);
-      }
-    }
-    const bool full = kt0 + AT_BK <= ke;
-    bf16x8 pb[2][2];
-#pragma unroll
+    // query fragments (B operand of S^T = K Q^T): Q[q][32*step + 8*g4 .. +8] in bf16
+    bf16x8 qf[2][D / 32];
+  #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float tmax = -INFINITY;
-      if (full) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[kb][qb][r]);
+      const int q = qblk * AT_BQ + wave * 32 + qb * 16 + c16;
+  #pragma unroll
+      for (int step = 0; step < D / 32; ++step) {
+        bf16x8 v;
+        if (q < a.n_q) {
+          const uint64_t off = (uint64_t(h) * a.n_q + q) * D + step * 32 + g4 * 8;
+          if (a.q_bf16) {
+            v = *(const bf16x8 *)((const uint16_t *)a.q + off);
+          } else {
+            const float *qp = (const float *)a.q + off;
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = (__bf16)qp[e];
+          }
+        } else {
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+        }
+        qf[qb][step] = v;
+      }
+    }
+    bf16x8 ones;
+  #pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+
+    floatx4 o[D / 16][2];
+    floatx4 lacc[2];
+  #pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      lacc[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int db = 0; db < D / 16; ++db) o[db][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+    float m_run[2] = {-INFINITY, -INFINITY};
+
+    // id of the item's key in a tile (-1: no key)
+    auto load_ids = [&](int tile) -> int {
+      if (!has_item || tile >= n_tiles) return -1;
+      const int t = ks + tile * AT_BK + it_key;
+      if (t >= ke) return -1;
+      return L.id_bytes == 1 ? int(idp[t]) : int(((const uint16_t *)idp)[t]);
+    };
+    struct Regs {
+      uint32_t codes[SMAX][KW];
+      uint32_t meta[SMAX];
+      uint4 cent[KC];
+    } R;
+    // packed data of the item's key t: centroid slice, codes, (sigma, z)
+    auto load_data = [&](int tile, int id) {
+      if (id < 0) return;
+      const int t = ks + tile * AT_BK + it_key;
+      const int slot = chunk_of_lds(starts_s, nch_s, t);
+      const uint8_t *crow = st + L.cb_off + uint64_t(slot) * L.cb_chunk + uint64_t(h) * L.cb_head +
+                            uint64_t(id) * D * EB + uint64_t(it_ch) * EB;
+  #pragma unroll
+      for (int i = 0; i < KC; ++i) R.cent[i] = *(const uint4 *)(crow + 16 * i);
+  #pragma unroll
+      for (int s2 = 0; s2 < SMAX; ++s2) {
+        const uint8_t *cp = st + L.codes_off + uint64_t(s2) * L.codes_stage + uint64_t(h) * L.codes_head +
+                            uint64_t(t) * L.codes_token + uint64_t(it_ch) * BITS / 8;
+        if constexpr (KW == 2) {
+          const uint2 v = *(const uint2 *)cp;
+          R.codes[s2][0] = v.x; R.codes[s2][1] = v.y;
+        } else {
+  #pragma unroll
+          for (int w = 0; w < KW; w += 4) {
+            const uint4 v = *(const uint4 *)(cp + 4 * w);
+            R.codes[s2][w] = v.x; R.codes[s2][w + 1] = v.y; R.codes[s2][w + 2] = v.z; R.codes[s2][w + 3] = v.w;
+          }
+        }
+        R.meta[s2] = *((const uint32_t *)(st + L.meta_off + uint64_t(s2) * L.meta_stage + uint64_t(h) * L.meta_head +
+                                          uint64_t(t) * L.meta_token) + it_g);
+      }
+    };
+    // one PRQ stage folded into 16 channels: xh[c] = fmaf(q_c, sigma, xh[c]) (the
+    // zero points of all stages are added to the centroid beforehand)
+    auto stage16 = [&](const uint32_t *cw, float sf, float *xh) {
+      if constexpr (BITS == 2) {
+  #pragma unroll
+        for (int sh = 0; sh < 4; ++sh) {
+          uint32_t m = (cw[0] >> (2 * sh)) & 0x03030303u;  // bytes: channels 4*byte + sh
+          // hide m's known-zero bits so that each byte is widened by one
+          // byte-to-float conversion instead of a bit-field extract + convert
+          asm("" : "+v"(m));
+  #pragma unroll
+          for (int by = 0; by < 4; ++by) xh[4 * by + sh] = fmaf(float((m >> (8 * by)) & 0xffu), sf, xh[4 * by + sh]);
+        }
       } else {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (kt0 + kb * 16 + g4 * 4 + r >= ke) s[kb][qb][r] = -INFINITY;
-            tmax = fmaxf(tmax, s[kb][qb][r]);
+  #pragma unroll
+        for (int w = 0; w < 2; ++w)
+  #pragma unroll
+          for (int sh = 0; sh < 2; ++sh) {
+            uint32_t m = (cw[w] >> (4 * sh)) & 0x0f0f0f0fu;  // bytes: channels 8w + 2*byte + sh
+            asm("" : "+v"(m));
+  #pragma unroll
+            for (int by = 0; by < 4; ++by)
+              xh[8 * w + 2 * by + sh] = fmaf(float((m >> (8 * by)) & 0xffu), sf, xh[8 * w + 2 * by + sh]);
           }
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mt = tmax * sc;
-      const bool need = mt > m_run[qb] + AT3_TAU;
-      if (__any(need)) {
-        const float mnew = need ? mt : m_run[qb];
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_run[qb] - mnew) : 1.0f;
-        m_run[qb] = mnew;
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) o[db][qb] *= alpha;
-        lacc[qb] *= alpha;
+    };
+    // centroid channel e of the item as fp32
+    auto cent_f32 = [&](int e) -> float {
+      if constexpr (CB_BF16) {
+        const uint4 v = R.cent[e >> 3];
+        const uint32_t w = ((e & 7) >> 1) == 0 ? v.x : ((e & 7) >> 1) == 1 ? v.y : ((e & 7) >> 1) == 2 ? v.z : v.w;
+        return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+      } else {
+        const uint4 v = R.cent[e >> 2];
+        const uint32_t w = (e & 3) == 0 ? v.x : (e & 3) == 1 ? v.y : (e & 3) == 2 ? v.z : v.w;
+        return __uint_as_float(w);
       }
-      const float nm = -m_run[qb];
-#pragma unroll
-      for (int st2 = 0; st2 < 2; ++st2) {
-        bf16x8 v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          v[r] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * st2][qb][r], sc, nm));
-          v[4 + r] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * st2 + 1][qb][r], sc, nm));
+    };
+    // Rebuild the item for the products: xh = fmaf(q_S, sigma_S, ... fmaf(q_1,
+    // sigma_1, c + (z_1 + ... + z_S))), then nearest-even bf16.  This differs
+    // from the stage-by-stage reconstruction (c + rhat_1) + rhat_2 ... by a few
+    // fp32 ulps, which changes the bf16 operand only for values within those
+    // ulps of a bf16 rounding boundary.
+    auto dequant_store = [&](int buf, int id) {
+      if (!has_item) return;
+      float xh[IC];
+      if (id >= 0) {
+        float zs = 0.0f;
+  #pragma unroll
+        for (int s2 = 0; s2 < SMAX; ++s2) zs += f16_bits_to_f32(uint16_t(R.meta[s2] >> 16));
+  #pragma unroll
+        for (int e = 0; e < IC; ++e) xh[e] = cent_f32(e) + zs;
+  #pragma unroll
+        for (int s2 = 0; s2 < SMAX; ++s2) {
+          const float sf = f16_bits_to_f32(uint16_t(R.meta[s2] & 0xffffu));
+  #pragma unroll
+          for (int b16 = 0; b16 < IC / 16; ++b16) stage16(&R.codes[s2][b16 * (BITS / 2)], sf, &xh[16 * b16]);
         }
-        pb[qb][st2] = v;
+      } else {
+  #pragma unroll
+        for (int e = 0; e < IC; ++e) xh[e] = 0.0f;
       }
-    }
-    // A operand of O^T += V^T P^T for d-block db and keys of S^T blocks 2*st2
-    // (k = 0..3 of each lane group) and 2*st2+1 (k = 4..7): one transposing
-    // load per half.  In a 16-lane group the load hands lane l element l%4 of
-    // the 4-element rows loaded by lanes l/4 + 4j, j = 0..3; lane l therefore
-    // addresses key 16*kb + 4*g4 + l/4, channels 4*(l%4) .. +3 of the block.
-    const uint16_t *vbase = &Vs[buf][(4 * g4 + (c16 >> 2)) * VP + 4 * (c16 & 3)];
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-#pragma unroll
-      for (int st2 = 0; st2 < 2; ++st2) {
-        const bf16x4 lo = lds_read_tr16(vbase + (32 * st2) * VP + 16 * db);
-        const bf16x4 hi = lds_read_tr16(vbase + (32 * st2 + 16) * VP + 16 * db);
-        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qb][st2], o[db][qb], 0, 0, 0);
+      uint16_t *dst = it_kv ? &Vs[buf][it_key * VP + it_ch] : &Ks[buf][it_key * KP + it_ch];
+  #pragma unroll
+      for (int j = 0; j < IC; j += 8) {
+        uint4 v;
+        v.x = uint32_t(f32_to_bf16_bits(xh[j])) | (uint32_t(f32_to_bf16_bits(xh[j + 1])) << 16);
+        v.y = uint32_t(f32_to_bf16_bits(xh[j + 2])) | (uint32_t(f32_to_bf16_bits(xh[j + 3])) << 16);
+        v.z = uint32_t(f32_to_bf16_bits(xh[j + 4])) | (uint32_t(f32_to_bf16_bits(xh[j + 5])) << 16);
+        v.w = uint32_t(f32_to_bf16_bits(xh[j + 6])) | (uint32_t(f32_to_bf16_bits(xh[j + 7])) << 16);
+        *(uint4 *)(dst + j) = v;
       }
-    }
-#pragma unroll
-    for (int st2 = 0; st2 < 2; ++st2)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qb][st2], lacc[qb], 0, 0, 0);
-  };
+    };
 
-  // Pipeline: at iteration i every wave rebuilds tile i+1 from data loaded
-  // during iteration i-1 and issues the loads of tile i+2 (ids of tile i+3);
-  // one barrier per tile.  Two waves share each SIMD; half of the waves
-  // multiply tile i before rebuilding and half after, so one wave's MFMA work
-  // overlaps its partner's VALU work.  The split flips between waves w and
-  // w+4 and between waves 2k and 2k+1, whichever way waves sit on SIMDs.
-  const bool mfma_first = ((wave >> 2) ^ wave) & 1;
-  __syncthreads();  // chunk table in LDS
-  int id1, id2;
-  {
-    const int id0 = load_ids(0);
-    load_data(0, id0);
-    dequant_store(0, id0);
-    id1 = load_ids(1);
-    load_data(1, id1);
-    id2 = load_ids(2);
-  }
-  __syncthreads();
-
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
-    if (mfma_first) compute_tile(tile);
-    if (tile + 1 < n_tiles) dequant_store(buf ^ 1, id1);   // data of tile+1 already in R
-    load_data(tile + 2, id2);
-    id1 = id2;
-    id2 = load_ids(tile + 3);
-    if (!mfma_first) compute_tile(tile);
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int q = blockIdx.x * AT_BQ + wave * 32 + qb * 16 + c16;
-    if (q >= a.n_q) continue;
-    const float l = lacc[qb][0];
-    const bool empty = !(l > 0.0f);
-    const float inv_l = empty ? 0.0f : 1.0f / l;
-    const float lse = empty ? -INFINITY : (m_run[qb] + log2f(l)) * 0.6931471805599453f;
-    if (a.n_splits == 1) {
-#pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-        const uint64_t off = (uint64_t(h) * a.n_q + q) * D + db * 16 + g4 * 4;
-        const floatx4 v = o[db][qb] * inv_l;
-        if (a.out_bf16) {
-          uint16_t *op = (uint16_t *)a.out + off;
-          const uint32_t p0 = uint32_t(f32_to_bf16_bits(v[0])) | (uint32_t(f32_to_bf16_bits(v[1])) << 16);
-          const uint32_t p1 = uint32_t(f32_to_bf16_bits(v[2])) | (uint32_t(f32_to_bf16_bits(v[3])) << 16);
-          *(uint2 *)op = make_uint2(p0, p1);
+    auto compute_tile = [&](int tile) {
+      const int buf = tile & 1;
+      const int kt0 = ks + tile * AT_BK;
+      floatx4 s[4][2];
+  #pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+  #pragma unroll
+        for (int qb = 0; qb < 2; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int step = 0; step < D / 32; ++step) {
+          const bf16x8 ka = *(const bf16x8 *)&Ks[buf][(kb * 16 + c16) * KP + step * 32 + g4 * 8];
+  #pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qb][step], s[kb][qb], 0, 0, 0);
+        }
+      }
+      const bool full = kt0 + AT_BK <= ke;
+      bf16x8 pb[2][2];
+  #pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float tmax = -INFINITY;
+        if (full) {
+  #pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[kb][qb][r]);
         } else {
-          *(float4 *)((float *)a.out + off) = make_float4(v[0], v[1], v[2], v[3]);
+  #pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              if (kt0 + kb * 16 + g4 * 4 + r >= ke) s[kb][qb][r] = -INFINITY;
+              tmax = fmaxf(tmax, s[kb][qb][r]);
+            }
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float mt = tmax * sc;
+        const bool need = mt > m_run[qb] + AT3_TAU;
+        if (__any(need)) {
+          const float mnew = need ? mt : m_run[qb];
+          const float alpha = need ? __builtin_amdgcn_exp2f(m_run[qb] - mnew) : 1.0f;
+          m_run[qb] = mnew;
+  #pragma unroll
+          for (int db = 0; db < D / 16; ++db) o[db][qb] *= alpha;
+          lacc[qb] *= alpha;
+        }
+        const float nm = -m_run[qb];
+  #pragma unroll
+        for (int st2 = 0; st2 < 2; ++st2) {
+          bf16x8 v;
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            v[r] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * st2][qb][r], sc, nm));
+            v[4 + r] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * st2 + 1][qb][r], sc, nm));
+          }
+          pb[qb][st2] = v;
         }
       }
-      if (a.lse && g4 == 0) a.lse[uint64_t(h) * a.n_q + q] = lse;
-    } else {
-#pragma unroll
+      // A operand of O^T += V^T P^T for d-block db and keys of S^T blocks 2*st2
+      // (k = 0..3 of each lane group) and 2*st2+1 (k = 4..7): one transposing
+      // load per half.  In a 16-lane group the load hands lane l element l%4 of
+      // the 4-element rows loaded by lanes l/4 + 4j, j = 0..3; lane l therefore
+      // addresses key 16*kb + 4*g4 + l/4, channels 4*(l%4) .. +3 of the block.
+      const uint16_t *vbase = &Vs[buf][(4 * g4 + (c16 >> 2)) * VP + 4 * (c16 & 3)];
+  #pragma unroll
       for (int db = 0; db < D / 16; ++db) {
-        const uint64_t off = ((uint64_t(split) * L.H + h) * a.n_q + q) * D + db * 16 + g4 * 4;
-        const floatx4 v = o[db][qb] * inv_l;
-        *(float4 *)(a.part_o + off) = make_float4(v[0], v[1], v[2], v[3]);
+  #pragma unroll
+        for (int st2 = 0; st2 < 2; ++st2) {
+          const bf16x4 lo = lds_read_tr16(vbase + (32 * st2) * VP + 16 * db);
+          const bf16x4 hi = lds_read_tr16(vbase + (32 * st2 + 16) * VP + 16 * db);
+          const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  #pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qb][st2], o[db][qb], 0, 0, 0);
+        }
       }
-      if (g4 == 0) a.part_lse[(uint64_t(split) * L.H + h) * a.n_q + q] = lse;
+  #pragma unroll
+      for (int st2 = 0; st2 < 2; ++st2)
+  #pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qb][st2], lacc[qb], 0, 0, 0);
+    };
+
+    // Pipeline: at iteration i every wave rebuilds tile i+1 from data loaded
+    // during iteration i-1 and issues the loads of tile i+2 (ids of tile i+3);
+    // one barrier per tile.  Two waves share each SIMD; half of the waves
+    // multiply tile i before rebuilding and half after, so one wave's MFMA work
+    // overlaps its partner's VALU work.  The split flips between waves w and
+    // w+4 and between waves 2k and 2k+1, whichever way waves sit on SIMDs.
+    const bool mfma_first = ((wave >> 2) ^ wave) & 1;
+    __syncthreads();  // previous segment's tiles no longer read
+    int id1, id2;
+    {
+      const int id0 = load_ids(0);
+      load_data(0, id0);
+      dequant_store(0, id0);
+      id1 = load_ids(1);
+      load_data(1, id1);
+      id2 = load_ids(2);
+    }
+    __syncthreads();
+
+    for (int tile = 0; tile < n_tiles; ++tile) {
+      const int buf = tile & 1;
+      if (mfma_first) compute_tile(tile);
+      if (tile + 1 < n_tiles) dequant_store(buf ^ 1, id1);   // data of tile+1 already in R
+      load_data(tile + 2, id2);
+      id1 = id2;
+      id2 = load_ids(tile + 3);
+      if (!mfma_first) compute_tile(tile);
+      __syncthreads();
+    }
+
+  #pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int q = qblk * AT_BQ + wave * 32 + qb * 16 + c16;
+      if (q >= a.n_q) continue;
+      const float l = lacc[qb][0];
+      const bool empty = !(l > 0.0f);
+      const float inv_l = empty ? 0.0f : 1.0f / l;
+      const float lse = empty ? -INFINITY : (m_run[qb] + log2f(l)) * 0.6931471805599453f;
+      if (slot < 0) {
+  #pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+          const uint64_t off = (uint64_t(h) * a.n_q + q) * D + db * 16 + g4 * 4;
+          const floatx4 v = o[db][qb] * inv_l;
+          if (a.out_bf16) {
+            uint16_t *op = (uint16_t *)a.out + off;
+            const uint32_t p0 = uint32_t(f32_to_bf16_bits(v[0])) | (uint32_t(f32_to_bf16_bits(v[1])) << 16);
+            const uint32_t p1 = uint32_t(f32_to_bf16_bits(v[2])) | (uint32_t(f32_to_bf16_bits(v[3])) << 16);
+            *(uint2 *)op = make_uint2(p0, p1);
+          } else {
+            *(float4 *)((float *)a.out + off) = make_float4(v[0], v[1], v[2], v[3]);
+          }
+        }
+        if (a.lse && g4 == 0) a.lse[uint64_t(h) * a.n_q + q] = lse;
+      } else {
+  #pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+          const uint64_t off = ((uint64_t(slot) * L.H + h) * a.n_q + q) * D + db * 16 + g4 * 4;
+          const floatx4 v = o[db][qb] * inv_l;
+          *(float4 *)(a.part_o + off) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+        if (g4 == 0) a.part_lse[(uint64_t(slot) * L.H + h) * a.n_q + q] = lse;
+      }
     }
   }
 }
 
-// Merge split partials: O = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - max).
-// One thread per (query, channel); blockIdx.y = head.
+// Merge the partials of query blocks shared by several blocks:
+// O = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - max).  One thread per
+// (query, 4 channels); blockIdx.y = head.  Query blocks covered by one block
+// were written directly and are skipped.
 __global__ __launch_bounds__(256) void k_attend_merge(AttnArgs a) {
-  const int D = a.L.D;
+  const int D = a.L.D, D4 = D / 4;
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= int64_t(a.n_q) * D) return;
-  const int q = int(idx / D), dd = int(idx % D), h = blockIdx.y;
+  if (idx >= int64_t(a.n_q) * D4) return;
+  const int q = int(idx / D4), d4 = int(idx % D4), h = blockIdx.y;
+  const int64_t T = a.n_ktiles, U = a.units_per_block;
+  const int64_t first = (int64_t(h) * a.n_qblocks + q / AT_BQ) * T;
+  const int nseg = int((first + T - 1) / U - first / U) + 1;
+  if (nseg == 1) return;
+  float ls[kMaxSplits];
   float mx = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s)
-    mx = fmaxf(mx, a.part_lse[(uint64_t(s) * a.L.H + h) * a.n_q + q]);
-  float wsum = 0.0f, acc = 0.0f;
-  for (int s = 0; s < a.n_splits; ++s) {
-    const float ls = a.part_lse[(uint64_t(s) * a.L.H + h) * a.n_q + q];
-    if (ls == -INFINITY) continue;
-    const float w = expf(ls - mx);
-    wsum += w;
-    acc = fmaf(w, a.part_o[((uint64_t(s) * a.L.H + h) * a.n_q + q) * D + dd], acc);
+  for (int s = 0; s < nseg; ++s) {
+    ls[s] = a.part_lse[(uint64_t(s) * a.L.H + h) * a.n_q + q];
+    mx = fmaxf(mx, ls[s]);
   }
-  const float v = acc / wsum;
-  const uint64_t off = (uint64_t(h) * a.n_q + q) * D + dd;
-  if (a.out_bf16) ((uint16_t *)a.out)[off] = f32_to_bf16_bits(v);
-  else ((float *)a.out)[off] = v;
-  if (a.lse && dd == 0) a.lse[uint64_t(h) * a.n_q + q] = mx + logf(wsum);
+  float wsum = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < nseg; ++s) {
+    if (ls[s] == -INFINITY) continue;
+    const float w = expf(ls[s] - mx);
+    wsum += w;
+    const float4 v = *(const float4 *)(a.part_o + ((uint64_t(s) * a.L.H + h) * a.n_q + q) * D + 4 * d4);
+    acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
+    acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  const uint64_t off = (uint64_t(h) * a.n_q + q) * D + 4 * d4;
+  if (a.out_bf16) {
+    *(uint2 *)((uint16_t *)a.out + off) = make_uint2(
+        uint32_t(f32_to_bf16_bits(acc.x * inv)) | (uint32_t(f32_to_bf16_bits(acc.y * inv)) << 16),
+        uint32_t(f32_to_bf16_bits(acc.z * inv)) | (uint32_t(f32_to_bf16_bits(acc.w * inv)) << 16));
+  } else {
+    *(float4 *)((float *)a.out + off) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  }
+  if (a.lse && d4 == 0) a.lse[uint64_t(h) * a.n_q + q] = wsum > 0.0f ? mx + logf(wsum) : -INFINITY;
 }
 
 // ------------------------------------------------------------ cross layer
@@ -1430,7 +1467,8 @@ static void launch_recon_t(const ReconArgs &a, int n_layers, int64_t out_tokens,
 
 template <int D, int G, int BITS, bool BF>
 static void launch_attend_t(const AttnArgs &a, hipStream_t st) {
-  const dim3 grid(cdiv(a.n_q, AT_BQ), a.L.H, a.n_splits);
+  const int64_t total = int64_t(a.n_ktiles) * a.n_qblocks * a.L.H;
+  const dim3 grid(unsigned(cdiv(total, a.units_per_block)));
   switch (a.L.S) {
     case 1: hipLaunchKernelGGL((k_attend3<D, G, BITS, BF, 1>), grid, dim3(512), 0, st, a); break;
     case 2: hipLaunchKernelGGL((k_attend3<D, G, BITS, BF, 2>), grid, dim3(512), 0, st, a); break;
@@ -1474,8 +1512,8 @@ void launch_reconstruct(const ReconArgs &a, int n_layers, int64_t out_tokens, in
 }
 void launch_attend(const AttnArgs &a, hipStream_t st) {
   QKV_DISPATCH_CODEC(a.L, launch_attend_t, a, st);
-  if (a.n_splits > 1)
-    hipLaunchKernelGGL(k_attend_merge, dim3(cdiv(int64_t(a.n_q) * a.L.D, 256), a.L.H), dim3(256), 0, st, a);
+  if (a.max_segments > 1)
+    hipLaunchKernelGGL(k_attend_merge, dim3(cdiv(int64_t(a.n_q) * (a.L.D / 4), 256), a.L.H), dim3(256), 0, st, a);
 }
 void launch_xl_predict(const XlArgs &a, int kv0, int n_kv, hipStream_t st) {
   int rp = 1;

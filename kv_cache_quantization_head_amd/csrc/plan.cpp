@@ -169,25 +169,19 @@ int check_rewind(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int64_t n
   return QKV_OK;
 }
 
-int attention_splits(const Plan &p, int64_t n_keys, int64_t n_q, int n_cu) {
-  // One block (256 queries of one head, one key range) occupies a compute
-  // unit.  The call lasts about (rounds of blocks) x (key tiles per split);
-  // pick the split count that minimises it, charging splitting a few percent
-  // for the partial writes and the merge, and keep at least 8 key tiles of
-  // 64 per split.
-  const int64_t q_blocks = (n_q + 255) / 256;
-  const int64_t base = int64_t(p.cfg.n_heads) * q_blocks;
-  const int64_t tiles = std::max<int64_t>((n_keys + 63) / 64, 1);
+AttnSplit attention_split(const Plan &p, int64_t n_keys, int64_t n_q, int n_cu) {
+  AttnSplit w{};
+  w.n_qblocks = (n_q + 255) / 256;
+  w.n_ktiles = std::max<int64_t>(1, (n_keys + 63) / 64);
+  const int64_t total = w.n_qblocks * w.n_ktiles * p.cfg.n_heads;
   const int64_t cus = std::max(n_cu, 1);
-  const int64_t max_s = std::max<int64_t>(1, std::min<int64_t>(kMaxSplits, (tiles + 7) / 8));
-  int64_t best = 1;
-  double best_cost = 0.0;
-  for (int64_t s = 1; s <= max_s; ++s) {
-    const double rounds = double((base * s + cus - 1) / cus);
-    const double cost = rounds * double((tiles + s - 1) / s) * (s > 1 ? 1.03 : 1.0);
-    if (s == 1 || cost < best_cost) { best = s; best_cost = cost; }
-  }
-  return int(best);
+  // one run per compute unit, but no query block shared by more than
+  // kMaxSplits blocks (the partial slots of the scratch region)
+  w.units_per_block = std::max((total + cus - 1) / cus, (w.n_ktiles + kMaxSplits - 2) / (kMaxSplits - 1));
+  w.n_blocks = (total + w.units_per_block - 1) / w.units_per_block;
+  // blocks meeting one query block: at most ceil((T - 1) / U) + 1
+  w.max_segments = std::min<int64_t>(kMaxSplits, (w.n_ktiles - 1 + w.units_per_block - 1) / w.units_per_block + 1);
+  return w;
 }
 
 }  // namespace qkv

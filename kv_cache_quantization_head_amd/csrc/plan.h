@@ -90,9 +90,13 @@ int check_reconstruct(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int3
                       int64_t t1, const void *out, int32_t out_dtype);
 int check_rewind(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int64_t n_tokens);
 
-// Number of KV splits used by an attention call over n_keys keys on a device
-// with n_cu compute units.
-int attention_splits(const Plan &p, int64_t n_keys, int64_t n_q, int n_cu);
+// Work split of an attention call (stream-K): the (head, query block of
+// 256, key tile of 64) units are dealt out in runs of units_per_block
+// consecutive units, one run per block, about one block per compute unit.
+struct AttnSplit {
+  int64_t n_qblocks, n_ktiles, units_per_block, n_blocks, max_segments;
+};
+AttnSplit attention_split(const Plan &p, int64_t n_keys, int64_t n_q, int n_cu);
 
 // Byte offset of stream (layer, kv) from the arena base.
 inline uint64_t stream_offset(const Plan &p, int layer, int kv) {
