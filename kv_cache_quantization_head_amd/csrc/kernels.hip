@@ -118,46 +118,49 @@ __global__ void k_header(EncodeArgs a) {
   hdr->n_tokens = a.t0 + a.n;
 }
 
-// blockIdx.x = head, blockIdx.y = stream of the call
+// One wave per codebook row: blockIdx.x = group of 4 rows, y = head,
+// z = stream of the call.  Row k is the previous call's snapshot row
+// (centroid caching) or token floor(k*n/C) (strided start); the norm
+// ||c_k||^2 (used only by the screening and its error bound) is summed over
+// the wave in fp64.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void k_init(EncodeArgs a) {
   constexpr int EB = BF16 ? 2 : 4;
+  constexpr int CPL = D / 64;               // channels per lane
   const DevLayout &L = a.L;
-  const int h = blockIdx.x, z = blockIdx.y, lrel = z >> 1, kv = z & 1;
+  const int lane = threadIdx.x & 63;
+  const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int h = blockIdx.y, z = blockIdx.z, lrel = z >> 1, kv = z & 1;
+  if (k >= L.C) return;
   uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, kv);
-  const uint8_t *x = (kv ? a.v_in : a.k_in) + (uint64_t(lrel) * L.H + h) * uint64_t(a.n) * D * EB;
   uint8_t *cb = st + L.cb_off + uint64_t(a.slot) * L.cb_chunk + uint64_t(h) * L.cb_head;
   float *cn = (float *)(st + L.cn_off + uint64_t(a.slot) * L.cn_chunk + uint64_t(h) * L.cn_head);
+  const uint8_t *src;
   if (a.prev_slot >= 0) {
-    const uint32_t *src =
-        (const uint32_t *)(st + L.cb_off + uint64_t(a.prev_slot) * L.cb_chunk + uint64_t(h) * L.cb_head);
-    const float *pcn =
-        (const float *)(st + L.cn_off + uint64_t(a.prev_slot) * L.cn_chunk + uint64_t(h) * L.cn_head);
-    uint32_t *dst = (uint32_t *)cb;
-    const int words = L.C * D * EB / 4;
-    for (int i = threadIdx.x; i < words; i += blockDim.x) dst[i] = src[i];
-    for (int k = threadIdx.x; k < L.C; k += blockDim.x) cn[k] = pcn[k];
-    return;
-  }
-  for (int k = threadIdx.x; k < L.C; k += blockDim.x) {
+    src = st + L.cb_off + uint64_t(a.prev_slot) * L.cb_chunk + uint64_t(h) * L.cb_head + uint64_t(k) * D * EB;
+  } else {
     const int64_t row = (int64_t(k) * a.n) / L.C;
-    const uint8_t *src = x + uint64_t(row) * D * EB;
-    uint8_t *dst = cb + uint64_t(k) * D * EB;
-    double acc = 0.0;
-    for (int j = 0; j < D; ++j) {
-      float v;
-      if constexpr (BF16) {
-        const uint16_t b = ((const uint16_t *)src)[j];
-        ((uint16_t *)dst)[j] = b;
-        v = bf16_to_f32(b);
-      } else {
-        v = ((const float *)src)[j];
-        ((float *)dst)[j] = v;
-      }
-      acc = acc + double(v) * double(v);
-    }
-    cn[k] = float(acc);
+    src = (kv ? a.v_in : a.k_in) + (uint64_t(lrel) * L.H + h) * uint64_t(a.n) * D * EB + uint64_t(row) * D * EB;
   }
+  uint8_t *dst = cb + uint64_t(k) * D * EB;
+  double acc = 0.0;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int j = lane * CPL + c;
+    float v;
+    if constexpr (BF16) {
+      const uint16_t b = ((const uint16_t *)src)[j];
+      ((uint16_t *)dst)[j] = b;
+      v = bf16_to_f32(b);
+    } else {
+      v = ((const float *)src)[j];
+      ((float *)dst)[j] = v;
+    }
+    acc = acc + double(v) * double(v);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) cn[k] = float(acc);
 }
 
 // One thread per token.  blockIdx.x = token tile of 256, y = head, z = stream.
@@ -1419,7 +1422,7 @@ static inline unsigned cdiv(int64_t a, int64_t b) { return unsigned((a + b - 1) 
 
 template <int D, bool BF>
 static void launch_init_t(const EncodeArgs &a, int streams, hipStream_t st) {
-  hipLaunchKernelGGL((k_init<D, BF>), dim3(a.L.H, streams), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_init<D, BF>), dim3(cdiv(a.L.C, 4), a.L.H, streams), dim3(256), 0, st, a);
 }
 template <int D, bool BF>
 static void launch_assign_t(const EncodeArgs &a, int streams, hipStream_t st) {
