@@ -431,8 +431,13 @@ __global__ __launch_bounds__(512) void k_assign_mfma(EncodeArgs a, int tiles_per
           const uint16_t *xrow = x + uint64_t(tb + nt * 16 + tok_c16) * D;
           const uint16_t *crow = cbs + cand * KP;
           dd = 0.0;
+          // the token row is read in one go (one memory latency, not D/8)
+          uint4 xr[D / 8];
+#pragma unroll
+          for (int j8 = 0; j8 < D / 8; ++j8) xr[j8] = *(const uint4 *)(xrow + j8 * 8);
+#pragma unroll
           for (int j8 = 0; j8 < D / 8; ++j8) {
-            const uint4 xv = *(const uint4 *)(xrow + j8 * 8);
+            const uint4 xv = xr[j8];
             const uint4 cv = *(const uint4 *)(crow + j8 * 8);
             const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, cw[4] = {cv.x, cv.y, cv.z, cv.w};
 #pragma unroll
