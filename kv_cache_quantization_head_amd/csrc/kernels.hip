@@ -39,6 +39,7 @@ namespace qkv {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // ------------------------------------------------------------------ helpers
@@ -60,6 +61,11 @@ __device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
   uint32_t r;
   asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
+}
+// two floats -> packed nearest-even bf16 pair (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);
@@ -859,43 +865,92 @@ __device__ __forceinline__ void centroid_base(const uint8_t *st, const DevLayout
   for (int j = 0; j < G; ++j) xh[j] = load_elem<CB_BF16>(crow, j);
 }
 
+// Store the 16-byte pieces `v` of this thread's contiguous output run
+// (thread i of the wave owns bytes [i*P*16, (i+1)*P*16) of the wave's
+// region starting at `dst`) so that each store instruction writes one
+// contiguous 1 KiB span: the pieces are exchanged through the wave's LDS
+// slice `buf` (P*1 KiB).  Stores in which a lane's 16 B sit a whole run
+// apart from its neighbour's reach about half the HBM write bandwidth.
+template <int P>
+__device__ __forceinline__ void store_wave_contiguous(uint4 *dst, uint4 *buf, const uint4 *v, int lane,
+                                                      int valid_lanes) {
+#pragma unroll
+  for (int j = 0; j < P; ++j) buf[lane * P + j] = v[j];
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    const int piece = j * 64 + lane;              // piece index inside the wave's region
+    if (piece < valid_lanes * P) dst[piece] = buf[piece];
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
 // One thread per (token, group).  blockIdx.x = item tile, y = head, z = layer.
+// The output of a wave (64 consecutive (token, group) items) is one
+// contiguous run of memory; it is stored through LDS in lane-contiguous
+// pieces.
 template <int D, int G, int BITS, bool CB_BF16>
 __global__ __launch_bounds__(256) void k_reconstruct(ReconArgs a, int64_t out_tokens, int32_t out_t_off) {
   constexpr int NG = D / G;
+  constexpr int PB = G * 2 / 16;             // 16-byte pieces of a group in bf16
+  constexpr int PF = G * 4 / 16;             // ... in fp32
+  // per-wave exchange slices of 64 x PS pieces (PS = PF for fp32 output,
+  // else PB), sized at launch; a wave's stores of the output and of the
+  // chain both use its own slice
+  extern __shared__ uint4 xbuf_dyn[];
+  const int PS = (a.out && !a.out_bf16) ? PF : PB;
   const DevLayout &L = a.L;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = idx / NG, g = idx % NG;
-  if (t >= a.n) return;
   const int h = blockIdx.y, lrel = blockIdx.z;
+  const bool valid = t < a.n;
+  // items of this wave that exist (the run ends at the last token)
+  const int wave_item0 = idx - lane;
+  const int valid_lanes = int(min<int64_t>(64, int64_t(a.n) * NG - wave_item0));
+  if (valid_lanes <= 0) return;             // whole wave past the end
   const uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, a.kv);
-  const int tt = a.t0 + t;
+  const int tt = a.t0 + min(t, a.n - 1);
   float xh[G];
   if (a.pred) {
-    const float *p = a.pred + (uint64_t(h) * a.n + t) * D + g * G;
+    const float *p = a.pred + (uint64_t(h) * a.n + min(t, a.n - 1)) * D + g * G;
 #pragma unroll
     for (int j = 0; j < G; ++j) xh[j] = p[j];
   } else {
     centroid_base<D, G, CB_BF16>(st, L, h, tt, g, xh);
   }
   add_stages<D, G, BITS>(st, L, h, tt, g, xh);
+  // first item of the wave: token t_w = wave_item0 / NG, group 0 (runs of a
+  // wave start at a token boundary because 64 % NG == 0)
+  const int t_w = wave_item0 / NG;
   if (a.out) {
-    const uint64_t o = ((uint64_t(lrel) * L.H + h) * uint64_t(out_tokens) + out_t_off + t) * D + g * G;
+    const uint64_t o = ((uint64_t(lrel) * L.H + h) * uint64_t(out_tokens) + out_t_off + t_w) * D;
     if (a.out_bf16) {
-      uint16_t *op = (uint16_t *)a.out + o;
+      uint4 v[PB];
 #pragma unroll
-      for (int j = 0; j < G; ++j) op[j] = f32_to_bf16_bits(xh[j]);
+      for (int j = 0; j < PB; ++j)
+        v[j] = make_uint4(pack_bf16x2(xh[8 * j], xh[8 * j + 1]), pack_bf16x2(xh[8 * j + 2], xh[8 * j + 3]),
+                          pack_bf16x2(xh[8 * j + 4], xh[8 * j + 5]), pack_bf16x2(xh[8 * j + 6], xh[8 * j + 7]));
+      store_wave_contiguous<PB>((uint4 *)((uint16_t *)a.out + o), xbuf_dyn + wave * 64 * PS, v, lane, valid_lanes);
     } else {
-      float *op = (float *)a.out + o;
+      uint4 v[PF];
 #pragma unroll
-      for (int j = 0; j < G; j += 4) *(float4 *)(op + j) = make_float4(xh[j], xh[j + 1], xh[j + 2], xh[j + 3]);
+      for (int j = 0; j < PF; ++j)
+        v[j] = make_uint4(__float_as_uint(xh[4 * j]), __float_as_uint(xh[4 * j + 1]),
+                          __float_as_uint(xh[4 * j + 2]), __float_as_uint(xh[4 * j + 3]));
+      store_wave_contiguous<PF>((uint4 *)((float *)a.out + o), xbuf_dyn + wave * 64 * PS, v, lane, valid_lanes);
     }
   }
   if (a.chain) {
-    uint16_t *cp = a.chain + (uint64_t(h) * a.n + t) * D + g * G;
+    uint4 v[PB];
 #pragma unroll
-    for (int j = 0; j < G; ++j) cp[j] = f32_to_bf16_bits(xh[j]);
+    for (int j = 0; j < PB; ++j)
+      v[j] = make_uint4(pack_bf16x2(xh[8 * j], xh[8 * j + 1]), pack_bf16x2(xh[8 * j + 2], xh[8 * j + 3]),
+                        pack_bf16x2(xh[8 * j + 4], xh[8 * j + 5]), pack_bf16x2(xh[8 * j + 6], xh[8 * j + 7]));
+    store_wave_contiguous<PB>((uint4 *)(a.chain + (uint64_t(h) * a.n + t_w) * D), xbuf_dyn + wave * 64 * PS, v, lane,
+                              valid_lanes);
   }
+  (void)valid;
 }
 
 // -------------------------------------------------------------- attention
@@ -1469,8 +1524,10 @@ template <int D, int G, int BITS, bool BF>
 static void launch_recon_t(const ReconArgs &a, int n_layers, int64_t out_tokens, int out_t_off,
                            hipStream_t st) {
   const int64_t items = int64_t(a.n) * (D / G);
+  // LDS: 4 waves x 64 lanes x one group of the output type
+  const size_t lds = size_t(4) * 64 * G * (a.out && !a.out_bf16 ? 4 : 2);
   hipLaunchKernelGGL((k_reconstruct<D, G, BITS, BF>), dim3(cdiv(items, 256), a.L.H, n_layers), dim3(256),
-                     0, st, a, out_tokens, out_t_off);
+                     lds, st, a, out_tokens, out_t_off);
 }
 
 template <int D, int G, int BITS, bool BF>
