@@ -1030,6 +1030,8 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   const int wave = tid >> 6, lane = tid & 63;
   const int g4 = lane >> 4, c16 = lane & 15;
   const float sc = 1.4426950408889634f / sqrtf(float(D));
+  // ds_bpermute byte addresses of lanes lane^16 and lane^32
+  const int bp_x16 = (lane ^ 16) << 2, bp_x32 = (lane ^ 32) << 2;
 
   // Rebuild items: one (tensor, key, 32 channels) per thread, K on even and
   // V on odd threads, so every wave runs the same rebuild code and the
@@ -1258,8 +1260,8 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
               tmax = fmaxf(tmax, s[kb][qb][r]);
             }
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        tmax = fmaxf(tmax, __int_as_float(__builtin_amdgcn_ds_bpermute(bp_x16, __float_as_int(tmax))));
+        tmax = fmaxf(tmax, __int_as_float(__builtin_amdgcn_ds_bpermute(bp_x32, __float_as_int(tmax))));
         const float mt = tmax * sc;
         const bool need = mt > m_run[qb] + AT3_TAU;
         if (__any(need)) {
