@@ -1124,31 +1124,47 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
       uint32_t meta[SMAX];
       uint4 cent[KC];
     } R;
-    // packed data of the item's key t: centroid slice, codes, (sigma, z)
+    // per-item pointers of the segment (key t = ks + AT_BK * tile + it_key)
+    const int t_first = ks + it_key;
+    const uint8_t *code_p = st + L.codes_off + uint64_t(h) * L.codes_head + uint64_t(t_first) * L.codes_token +
+                            it_ch * BITS / 8;
+    const uint8_t *meta_p = st + L.meta_off + uint64_t(h) * L.meta_head + uint64_t(t_first) * L.meta_token +
+                            4 * it_g;
+    const uint8_t *cb_p = st + L.cb_off + uint64_t(h) * L.cb_head + uint64_t(it_ch) * EB;
+    const uint64_t tile_codes = uint64_t(AT_BK) * L.codes_token, tile_meta = uint64_t(AT_BK) * L.meta_token;
+    // packed data of the item's key: centroid slice, codes, (sigma, z); all
+    // zero when there is no key, which rebuilds to zero
     auto load_data = [&](int tile, int id) {
-      if (id < 0) return;
-      const int t = ks + tile * AT_BK + it_key;
-      const int slot = chunk_of_lds(starts_s, nch_s, t);
-      const uint8_t *crow = st + L.cb_off + uint64_t(slot) * L.cb_chunk + uint64_t(h) * L.cb_head +
-                            uint64_t(id) * D * EB + uint64_t(it_ch) * EB;
+      if (id < 0) {
+  #pragma unroll
+        for (int i = 0; i < KC; ++i) R.cent[i] = make_uint4(0u, 0u, 0u, 0u);
+  #pragma unroll
+        for (int s2 = 0; s2 < SMAX; ++s2) {
+          R.meta[s2] = 0u;
+  #pragma unroll
+          for (int w = 0; w < KW; ++w) R.codes[s2][w] = 0u;
+        }
+        return;
+      }
+      const int cslot = nch_s > 1 ? chunk_of_lds(starts_s, nch_s, ks + tile * AT_BK + it_key) : 0;
+      const uint8_t *crow = cb_p + uint64_t(cslot) * L.cb_chunk + uint64_t(id) * (D * EB);
   #pragma unroll
       for (int i = 0; i < KC; ++i) R.cent[i] = *(const uint4 *)(crow + 16 * i);
+      const uint8_t *cp = code_p + uint64_t(tile) * tile_codes;
+      const uint8_t *mp = meta_p + uint64_t(tile) * tile_meta;
   #pragma unroll
       for (int s2 = 0; s2 < SMAX; ++s2) {
-        const uint8_t *cp = st + L.codes_off + uint64_t(s2) * L.codes_stage + uint64_t(h) * L.codes_head +
-                            uint64_t(t) * L.codes_token + uint64_t(it_ch) * BITS / 8;
         if constexpr (KW == 2) {
-          const uint2 v = *(const uint2 *)cp;
+          const uint2 v = *(const uint2 *)(cp + uint64_t(s2) * L.codes_stage);
           R.codes[s2][0] = v.x; R.codes[s2][1] = v.y;
         } else {
   #pragma unroll
           for (int w = 0; w < KW; w += 4) {
-            const uint4 v = *(const uint4 *)(cp + 4 * w);
+            const uint4 v = *(const uint4 *)(cp + uint64_t(s2) * L.codes_stage + 4 * w);
             R.codes[s2][w] = v.x; R.codes[s2][w + 1] = v.y; R.codes[s2][w + 2] = v.z; R.codes[s2][w + 3] = v.w;
           }
         }
-        R.meta[s2] = *((const uint32_t *)(st + L.meta_off + uint64_t(s2) * L.meta_stage + uint64_t(h) * L.meta_head +
-                                          uint64_t(t) * L.meta_token) + it_g);
+        R.meta[s2] = *(const uint32_t *)(mp + uint64_t(s2) * L.meta_stage);
       }
     };
     // one PRQ stage folded into 16 channels: xh[c] = fmaf(q_c, sigma, xh[c]) (the
@@ -1194,35 +1210,25 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     // from the stage-by-stage reconstruction (c + rhat_1) + rhat_2 ... by a few
     // fp32 ulps, which changes the bf16 operand only for values within those
     // ulps of a bf16 rounding boundary.
-    auto dequant_store = [&](int buf, int id) {
+    auto dequant_store = [&](int buf) {
       if (!has_item) return;
       float xh[IC];
-      if (id >= 0) {
-        float zs = 0.0f;
+      float zs = 0.0f;
   #pragma unroll
-        for (int s2 = 0; s2 < SMAX; ++s2) zs += f16_bits_to_f32(uint16_t(R.meta[s2] >> 16));
+      for (int s2 = 0; s2 < SMAX; ++s2) zs += f16_bits_to_f32(uint16_t(R.meta[s2] >> 16));
   #pragma unroll
-        for (int e = 0; e < IC; ++e) xh[e] = cent_f32(e) + zs;
+      for (int e = 0; e < IC; ++e) xh[e] = cent_f32(e) + zs;
   #pragma unroll
-        for (int s2 = 0; s2 < SMAX; ++s2) {
-          const float sf = f16_bits_to_f32(uint16_t(R.meta[s2] & 0xffffu));
+      for (int s2 = 0; s2 < SMAX; ++s2) {
+        const float sf = f16_bits_to_f32(uint16_t(R.meta[s2] & 0xffffu));
   #pragma unroll
-          for (int b16 = 0; b16 < IC / 16; ++b16) stage16(&R.codes[s2][b16 * (BITS / 2)], sf, &xh[16 * b16]);
-        }
-      } else {
-  #pragma unroll
-        for (int e = 0; e < IC; ++e) xh[e] = 0.0f;
+        for (int b16 = 0; b16 < IC / 16; ++b16) stage16(&R.codes[s2][b16 * (BITS / 2)], sf, &xh[16 * b16]);
       }
       uint16_t *dst = it_kv ? &Vs[buf][it_key * VP + it_ch] : &Ks[buf][it_key * KP + it_ch];
   #pragma unroll
-      for (int j = 0; j < IC; j += 8) {
-        uint4 v;
-        v.x = uint32_t(f32_to_bf16_bits(xh[j])) | (uint32_t(f32_to_bf16_bits(xh[j + 1])) << 16);
-        v.y = uint32_t(f32_to_bf16_bits(xh[j + 2])) | (uint32_t(f32_to_bf16_bits(xh[j + 3])) << 16);
-        v.z = uint32_t(f32_to_bf16_bits(xh[j + 4])) | (uint32_t(f32_to_bf16_bits(xh[j + 5])) << 16);
-        v.w = uint32_t(f32_to_bf16_bits(xh[j + 6])) | (uint32_t(f32_to_bf16_bits(xh[j + 7])) << 16);
-        *(uint4 *)(dst + j) = v;
-      }
+      for (int j = 0; j < IC; j += 8)
+        *(uint4 *)(dst + j) = make_uint4(pack_bf16x2(xh[j], xh[j + 1]), pack_bf16x2(xh[j + 2], xh[j + 3]),
+                                         pack_bf16x2(xh[j + 4], xh[j + 5]), pack_bf16x2(xh[j + 6], xh[j + 7]));
     };
 
     auto compute_tile = [&](int tile) {
@@ -1250,18 +1256,18 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
   #pragma unroll
-            for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, s[kb][qb][r]);
+            for (int r = 0; r < 4; ++r) tmax = __builtin_elementwise_maximum(tmax, s[kb][qb][r]);
         } else {
   #pragma unroll
           for (int kb = 0; kb < 4; ++kb)
   #pragma unroll
             for (int r = 0; r < 4; ++r) {
               if (kt0 + kb * 16 + g4 * 4 + r >= ke) s[kb][qb][r] = -INFINITY;
-              tmax = fmaxf(tmax, s[kb][qb][r]);
+              tmax = __builtin_elementwise_maximum(tmax, s[kb][qb][r]);
             }
         }
-        tmax = fmaxf(tmax, __int_as_float(__builtin_amdgcn_ds_bpermute(bp_x16, __float_as_int(tmax))));
-        tmax = fmaxf(tmax, __int_as_float(__builtin_amdgcn_ds_bpermute(bp_x32, __float_as_int(tmax))));
+        tmax = __builtin_elementwise_maximum(tmax, __int_as_float(__builtin_amdgcn_ds_bpermute(bp_x16, __float_as_int(tmax))));
+        tmax = __builtin_elementwise_maximum(tmax, __int_as_float(__builtin_amdgcn_ds_bpermute(bp_x32, __float_as_int(tmax))));
         const float mt = tmax * sc;
         const bool need = mt > m_run[qb] + AT3_TAU;
         if (__any(need)) {
@@ -1317,24 +1323,19 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     // w+4 and between waves 2k and 2k+1, whichever way waves sit on SIMDs.
     const bool mfma_first = ((wave >> 2) ^ wave) & 1;
     __syncthreads();  // previous segment's tiles no longer read
-    int id1, id2;
-    {
-      const int id0 = load_ids(0);
-      load_data(0, id0);
-      dequant_store(0, id0);
-      id1 = load_ids(1);
-      load_data(1, id1);
-      id2 = load_ids(2);
-    }
+    int id_next;   // id of the item's key in tile+2
+    load_data(0, load_ids(0));
+    dequant_store(0);
+    load_data(1, load_ids(1));
+    id_next = load_ids(2);
     __syncthreads();
 
     for (int tile = 0; tile < n_tiles; ++tile) {
       const int buf = tile & 1;
       if (mfma_first) compute_tile(tile);
-      if (tile + 1 < n_tiles) dequant_store(buf ^ 1, id1);   // data of tile+1 already in R
-      load_data(tile + 2, id2);
-      id1 = id2;
-      id2 = load_ids(tile + 3);
+      if (tile + 1 < n_tiles) dequant_store(buf ^ 1);   // data of tile+1 already in R
+      load_data(tile + 2, id_next);
+      id_next = load_ids(tile + 3);
       if (!mfma_first) compute_tile(tile);
       __syncthreads();
     }
