@@ -16,7 +16,7 @@
 //   k_quantize    centroid (or prediction) subtraction + S PRQ stages + packing
 //   k_reconstruct unpack + dequantize + add base, fp32 or bf16 out
 //   k_attend3     split-KV attention reading the packed cache: tiles are
-//                 rebuilt in bf16 in LDS and fed to bf16 MFMA (16x16x32)
+//                 rebuilt in bf16 in LDS and fed to bf16 MFMA (32x32x16)
 //   k_attend_merge  LSE merge of the split partials
 //   k_xl_project, k_xl_predict  cross-layer block-diagonal + low-rank
 //                 prediction in fp64 with a fixed summation order
@@ -956,31 +956,34 @@ __global__ __launch_bounds__(256) void k_reconstruct(ReconArgs a, int64_t out_to
 // -------------------------------------------------------------- attention
 //
 // Fused read of the packed cache.  Block = 8 waves (two per SIMD) = 256
-// queries of one head, 32 per wave; grid = (query blocks, heads, KV splits).
-// Per 64-key tile the block rebuilds K and V in bf16 into a double-buffered
-// LDS tile (K and V both as [key][d]; V is read for the PV step with
-// transposing LDS loads); each wave then computes S^T = K Q^T with
-// v_mfma_f32_16x16x32_bf16 (one lane's accumulator column is one query, so
-// softmax statistics need two cross-lane exchanges), runs the online softmax
-// in fp32 and accumulates O^T += V^T P^T with the probabilities rounded to
-// bf16.  The key order inside a 32-key MFMA step is permuted identically in
-// both operands so that P^T comes straight from the S^T accumulators.
+// queries of one head, 32 per wave; the (head, query block, key tile) units
+// are split stream-K style over the blocks.  Per 64-key tile the block
+// rebuilds K and V in bf16 into a double-buffered LDS tile (both as
+// [key][d]); each wave then computes S^T = K Q^T for its 32 queries with
+// v_mfma_f32_32x32x16_bf16 (a lane's accumulators hold 32 keys of one query;
+// lanes l and l^32 share the query, so the softmax statistics need one
+// cross-lane exchange), runs the online softmax in fp32 and accumulates
+// O^T += V^T P^T with the probabilities rounded to bf16.  V^T comes from
+// the row-major V tile through transposing LDS loads.  The key order inside
+// each 16-key MFMA step is permuted identically in both operands so that
+// P^T comes straight from the S^T accumulators.
 //
 //  * Rebuild items: one (tensor, key, 32 channels) per thread, K on even and
 //    V on odd threads (every wave runs the same code, stores included; the
 //    threads of a key read one centroid row).  The rebuild is
 //    bf16(fl32 chain: c + sum_s z_s, then fmaf(q_s, sigma_s, .) per stage);
 //    2-bit codes are widened four at a time from one masked code word
-//    (byte-to-float conversions).
+//    (byte-to-float conversions).  Keys past the end rebuild to zero from
+//    zeroed registers.
 //  * Loads are software-pipelined: ids of tile i+2 and the packed data
 //    (codes, scale/zero, centroid rows) of tile i+1 are in flight while tile
 //    i is rebuilt and multiplied; half of the waves multiply before they
-//    rebuild and half after, so MFMA and VALU work of the two waves on a SIMD
-//    overlap.  The chunk table is cached in LDS.
+//    rebuild and half after, so that the MFMA work of one wave of a SIMD
+//    overlaps the VALU work of the other.  The chunk table is cached in LDS.
 //  * The softmax scale is folded into the exponent's fma; the running max is
 //    only raised (and O, l rescaled) when a tile's max exceeds it by more
-//    than 8 (log2 units), so exponentials stay <= 256; row sums of P come
-//    from one extra MFMA against a fragment of ones.
+//    than 8 (log2 units), so exponentials stay <= 256; row sums of P are
+//    accumulated from the bf16 probabilities with v_dot2_f32_bf16.
 constexpr int AT_WAVES = 8;
 constexpr int AT_BQ = 32 * AT_WAVES;
 constexpr int AT_BK = 64;
@@ -993,6 +996,18 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t *p) {
   const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) shortx4 *)(p));
   return __builtin_bit_cast(bf16x4, v);
+}
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+// max / sum of the values of lanes l and l^32, identical on both lanes
+// (v_permlane32_swap_b32 hands each half the other half's values)
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ int chunk_of_lds(const int32_t *starts, int n_chunks, int t) {
@@ -1013,8 +1028,9 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   constexpr int IC = 32;                   // channels of one rebuild item
   constexpr int NI = D / IC;               // items per key and tensor
   constexpr int KP = D + 8;                // bf16 elements per K row in LDS
-  constexpr int VP = D + 16;               // bf16 elements per V row in LDS (rows 8 banks
-                                           // apart: conflict-free transposing reads)
+  constexpr int VP = D + 32;               // bf16 elements per V row in LDS (the 4 rows x
+                                           // 64 bytes of a transposing read by 32 lanes
+                                           // fall in distinct banks)
   constexpr int EB = CB_BF16 ? 2 : 4;
   constexpr int KW = IC * BITS / 32;       // code words of an item
   constexpr int KC = IC * EB / 16;         // uint4 of an item's centroid slice
@@ -1028,10 +1044,12 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   const DevLayout &L = a.L;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int g4 = lane >> 4, c16 = lane & 15;
+  const int hh = lane >> 5, c32 = lane & 31;
   const float sc = 1.4426950408889634f / sqrtf(float(D));
-  // ds_bpermute byte addresses of lanes lane^16 and lane^32
-  const int bp_x16 = (lane ^ 16) << 2, bp_x32 = (lane ^ 32) << 2;
+  constexpr int NS = D / 16, NDB = D / 32;
+  // lane's transposing-read address in a V tile: key 4*hh + (lane%16)/4 of a
+  // 16-key step, channels 16*((lane/16)%2) + 4*(lane%4) .. +3 of a 32-channel block
+  const int v_lane = (4 * hh + ((lane & 15) >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
   // Rebuild items: one (tensor, key, 32 channels) per thread, K on even and
   // V on odd threads, so every wave runs the same rebuild code and the
@@ -1074,43 +1092,37 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     const int ke = min(a.n_keys, t1 * AT_BK);
     const int n_tiles = ke > ks ? (ke - ks + AT_BK - 1) / AT_BK : 0;
 
-    // query fragments (B operand of S^T = K Q^T): Q[q][32*step + 8*g4 .. +8] in bf16
-    bf16x8 qf[2][D / 32];
+    const int q = qblk * AT_BQ + wave * 32 + c32;
+    // B operand of S^T = K Q^T, k-step s: Q[q][16 s + 8 hh .. +8] in bf16
+    bf16x8 qf[NS];
   #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int q = qblk * AT_BQ + wave * 32 + qb * 16 + c16;
-  #pragma unroll
-      for (int step = 0; step < D / 32; ++step) {
-        bf16x8 v;
-        if (q < a.n_q) {
-          const uint64_t off = (uint64_t(h) * a.n_q + q) * D + step * 32 + g4 * 8;
-          if (a.q_bf16) {
-            v = *(const bf16x8 *)((const uint16_t *)a.q + off);
-          } else {
-            const float *qp = (const float *)a.q + off;
-  #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = (__bf16)qp[e];
-          }
+    for (int s = 0; s < NS; ++s) {
+      bf16x8 v;
+      if (q < a.n_q) {
+        const uint64_t off = (uint64_t(h) * a.n_q + q) * D + s * 16 + hh * 8;
+        if (a.q_bf16) {
+          v = *(const bf16x8 *)((const uint16_t *)a.q + off);
         } else {
+          const float *qp = (const float *)a.q + off;
   #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)qp[e];
         }
-        qf[qb][step] = v;
+      } else {
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
       }
+      qf[s] = v;
     }
-    bf16x8 ones;
+    bf16x2 ones2;
+    ones2[0] = (__bf16)1.0f;
+    ones2[1] = (__bf16)1.0f;
+    floatx16 o[NDB];
   #pragma unroll
-    for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
-
-    floatx4 o[D / 16][2];
-    floatx4 lacc[2];
+    for (int db = 0; db < NDB; ++db)
   #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      lacc[qb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
-      for (int db = 0; db < D / 16; ++db) o[db][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
-    float m_run[2] = {-INFINITY, -INFINITY};
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+    float l_part = 0.0f;       // this lane's share of the row sum
+    float m_run = -INFINITY;
 
     // id of the item's key in a tile (-1: no key)
     auto load_ids = [&](int tile) -> int {
@@ -1234,85 +1246,69 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     auto compute_tile = [&](int tile) {
       const int buf = tile & 1;
       const int kt0 = ks + tile * AT_BK;
-      floatx4 s[4][2];
+      // S^T for keys 32*kb + (8*(r/4) + 4*hh + r%4) of the tile, query c32
+      floatx16 s0, s1;
   #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
+      const uint16_t *kp = &Ks[buf][c32 * KP + 8 * hh];
   #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) s[kb][qb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 k0 = *(const bf16x8 *)(kp + 16 * s);
+        const bf16x8 k1 = *(const bf16x8 *)(kp + 32 * KP + 16 * s);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], s1, 0, 0, 0);
+      }
+      if (kt0 + AT_BK > ke) {
   #pragma unroll
-        for (int step = 0; step < D / 32; ++step) {
-          const bf16x8 ka = *(const bf16x8 *)&Ks[buf][(kb * 16 + c16) * KP + step * 32 + g4 * 8];
-  #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qf[qb][step], s[kb][qb], 0, 0, 0);
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key >= ke) s0[r] = -INFINITY;
+          if (key + 32 >= ke) s1[r] = -INFINITY;
         }
       }
-      const bool full = kt0 + AT_BK <= ke;
-      bf16x8 pb[2][2];
+      float tmax = -INFINITY;
   #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float tmax = -INFINITY;
-        if (full) {
+      for (int r = 0; r < 16; ++r)
+        tmax = __builtin_elementwise_maximum(tmax, __builtin_elementwise_maximum(s0[r], s1[r]));
+      tmax = pair_max(tmax);
+      const float mt = tmax * sc;
+      const bool need = mt > m_run + AT3_TAU;
+      if (__any(need)) {
+        const float mnew = need ? mt : m_run;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;
+        m_run = mnew;
   #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+        l_part *= alpha;
+      }
+      const float nm = -m_run;
+      // O^T += V^T P^T over 16-key steps (kb, jj).  B operand: lane registers
+      // 8*jj .. 8*jj+7 of S^T block kb, i.e. k index 8*hh + e <-> key
+      // 32*kb + 16*jj + 8*(e/4) + 4*hh + e%4.  A operand (V^T, rows = channels
+      // 32*db + lane%32): two transposing loads, keys 32*kb + 16*jj + 4*hh +
+      // 0..3 and the same + 8.
+      const uint16_t *vp = &Vs[buf][v_lane];
   #pragma unroll
-            for (int r = 0; r < 4; ++r) tmax = __builtin_elementwise_maximum(tmax, s[kb][qb][r]);
-        } else {
+      for (int kb = 0; kb < 2; ++kb)
   #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
+        for (int jj = 0; jj < 2; ++jj) {
+          bf16x8 pb;
   #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              if (kt0 + kb * 16 + g4 * 4 + r >= ke) s[kb][qb][r] = -INFINITY;
-              tmax = __builtin_elementwise_maximum(tmax, s[kb][qb][r]);
-            }
-        }
-        tmax = __builtin_elementwise_maximum(tmax, __int_as_float(__builtin_amdgcn_ds_bpermute(bp_x16, __float_as_int(tmax))));
-        tmax = __builtin_elementwise_maximum(tmax, __int_as_float(__builtin_amdgcn_ds_bpermute(bp_x32, __float_as_int(tmax))));
-        const float mt = tmax * sc;
-        const bool need = mt > m_run[qb] + AT3_TAU;
-        if (__any(need)) {
-          const float mnew = need ? mt : m_run[qb];
-          const float alpha = need ? __builtin_amdgcn_exp2f(m_run[qb] - mnew) : 1.0f;
-          m_run[qb] = mnew;
+          for (int e = 0; e < 8; ++e)
+            pb[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(kb ? s1[8 * jj + e] : s0[8 * jj + e], sc, nm));
+          const uint4 w = __builtin_bit_cast(uint4, pb);
+          l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), ones2, l_part, false);
+          l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), ones2, l_part, false);
+          l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), ones2, l_part, false);
+          l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), ones2, l_part, false);
   #pragma unroll
-          for (int db = 0; db < D / 16; ++db) o[db][qb] *= alpha;
-          lacc[qb] *= alpha;
-        }
-        const float nm = -m_run[qb];
-  #pragma unroll
-        for (int st2 = 0; st2 < 2; ++st2) {
-          bf16x8 v;
-  #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            v[r] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * st2][qb][r], sc, nm));
-            v[4 + r] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[2 * st2 + 1][qb][r], sc, nm));
+          for (int db = 0; db < NDB; ++db) {
+            const bf16x4 lo = lds_read_tr16(vp + (32 * kb + 16 * jj) * VP + 32 * db);
+            const bf16x4 hi = lds_read_tr16(vp + (32 * kb + 16 * jj + 8) * VP + 32 * db);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                            pb, o[db], 0, 0, 0);
           }
-          pb[qb][st2] = v;
         }
-      }
-      // A operand of O^T += V^T P^T for d-block db and keys of S^T blocks 2*st2
-      // (k = 0..3 of each lane group) and 2*st2+1 (k = 4..7): one transposing
-      // load per half.  In a 16-lane group the load hands lane l element l%4 of
-      // the 4-element rows loaded by lanes l/4 + 4j, j = 0..3; lane l therefore
-      // addresses key 16*kb + 4*g4 + l/4, channels 4*(l%4) .. +3 of the block.
-      const uint16_t *vbase = &Vs[buf][(4 * g4 + (c16 >> 2)) * VP + 4 * (c16 & 3)];
-  #pragma unroll
-      for (int db = 0; db < D / 16; ++db) {
-  #pragma unroll
-        for (int st2 = 0; st2 < 2; ++st2) {
-          const bf16x4 lo = lds_read_tr16(vbase + (32 * st2) * VP + 16 * db);
-          const bf16x4 hi = lds_read_tr16(vbase + (32 * st2 + 16) * VP + 16 * db);
-          const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            o[db][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb[qb][st2], o[db][qb], 0, 0, 0);
-        }
-      }
-  #pragma unroll
-      for (int st2 = 0; st2 < 2; ++st2)
-  #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qb][st2], lacc[qb], 0, 0, 0);
     };
 
     // Pipeline: at iteration i every wave rebuilds tile i+1 from data loaded
@@ -1340,37 +1336,36 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
       __syncthreads();
     }
 
-  #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int q = qblk * AT_BQ + wave * 32 + qb * 16 + c16;
-      if (q >= a.n_q) continue;
-      const float l = lacc[qb][0];
+    const float l = pair_sum(l_part);
+    if (q < a.n_q) {
       const bool empty = !(l > 0.0f);
       const float inv_l = empty ? 0.0f : 1.0f / l;
-      const float lse = empty ? -INFINITY : (m_run[qb] + log2f(l)) * 0.6931471805599453f;
+      const float lse = empty ? -INFINITY : (m_run + log2f(l)) * 0.6931471805599453f;
+      // lane holds channels 32*db + 8*j + 4*hh + 0..3 in o[db][4j .. 4j+3]
       if (slot < 0) {
   #pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-          const uint64_t off = (uint64_t(h) * a.n_q + q) * D + db * 16 + g4 * 4;
-          const floatx4 v = o[db][qb] * inv_l;
-          if (a.out_bf16) {
-            uint16_t *op = (uint16_t *)a.out + off;
-            const uint32_t p0 = uint32_t(f32_to_bf16_bits(v[0])) | (uint32_t(f32_to_bf16_bits(v[1])) << 16);
-            const uint32_t p1 = uint32_t(f32_to_bf16_bits(v[2])) | (uint32_t(f32_to_bf16_bits(v[3])) << 16);
-            *(uint2 *)op = make_uint2(p0, p1);
-          } else {
-            *(float4 *)((float *)a.out + off) = make_float4(v[0], v[1], v[2], v[3]);
+        for (int db = 0; db < NDB; ++db)
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint64_t off = (uint64_t(h) * a.n_q + q) * D + 32 * db + 8 * j + 4 * hh;
+            const float v0 = o[db][4 * j] * inv_l, v1 = o[db][4 * j + 1] * inv_l;
+            const float v2 = o[db][4 * j + 2] * inv_l, v3 = o[db][4 * j + 3] * inv_l;
+            if (a.out_bf16)
+              *(uint2 *)((uint16_t *)a.out + off) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+            else
+              *(float4 *)((float *)a.out + off) = make_float4(v0, v1, v2, v3);
           }
-        }
-        if (a.lse && g4 == 0) a.lse[uint64_t(h) * a.n_q + q] = lse;
+        if (a.lse && hh == 0) a.lse[uint64_t(h) * a.n_q + q] = lse;
       } else {
   #pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-          const uint64_t off = ((uint64_t(slot) * L.H + h) * a.n_q + q) * D + db * 16 + g4 * 4;
-          const floatx4 v = o[db][qb] * inv_l;
-          *(float4 *)(a.part_o + off) = make_float4(v[0], v[1], v[2], v[3]);
-        }
-        if (g4 == 0) a.part_lse[(uint64_t(slot) * L.H + h) * a.n_q + q] = lse;
+        for (int db = 0; db < NDB; ++db)
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint64_t off = ((uint64_t(slot) * L.H + h) * a.n_q + q) * D + 32 * db + 8 * j + 4 * hh;
+            *(float4 *)(a.part_o + off) = make_float4(o[db][4 * j] * inv_l, o[db][4 * j + 1] * inv_l,
+                                                      o[db][4 * j + 2] * inv_l, o[db][4 * j + 3] * inv_l);
+          }
+        if (hh == 0) a.part_lse[(uint64_t(slot) * L.H + h) * a.n_q + q] = lse;
       }
     }
   }
