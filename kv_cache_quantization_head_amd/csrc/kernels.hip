@@ -1010,6 +1010,23 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// The 2-bit codes in the low and high nibble of byte B of w (each nibble
+// 00qq): the conversion reads a nibble as an E2M1 value, which is q/2 for
+// these patterns, and scales by 2 (a power of two, applied exactly), giving
+// float(q) for two codes in one v_cvt_scalef32_pk_f32_fp4.
+template <int B>
+__device__ __forceinline__ f32x2 nibble_codes(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 2.0f, B);
+}
+// The 4-bit codes in bytes 2*HI and 2*HI+1 of w (each byte 0000qqqq): an
+// E4M3 byte below 16 has the value byte * 2^-9, so the conversion scaled by
+// 2^9 gives float(q) for two codes in one v_cvt_scalef32_pk_f32_fp8.
+template <bool HI>
+__device__ __forceinline__ f32x2 byte_codes(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 512.0f, HI);
+}
+
 __device__ __forceinline__ int chunk_of_lds(const int32_t *starts, int n_chunks, int t) {
   int lo = 0, hi = n_chunks - 1;
   while (lo < hi) {
@@ -1183,26 +1200,38 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     // zero points of all stages are added to the centroid beforehand)
     auto stage16 = [&](const uint32_t *cw, float sf, float *xh) {
       if constexpr (BITS == 2) {
+        // nibbles of m0 hold the codes of channels 0, 2, .., 14, those of m1
+        // channels 1, 3, .., 15; byte b of m0 gives channels 4b and 4b+2
+        const uint32_t m0 = cw[0] & 0x33333333u, m1 = (cw[0] >> 2) & 0x33333333u;
+        const f32x2 e0 = nibble_codes<0>(m0), e1 = nibble_codes<1>(m0), e2 = nibble_codes<2>(m0),
+                    e3 = nibble_codes<3>(m0);
+        const f32x2 o0 = nibble_codes<0>(m1), o1 = nibble_codes<1>(m1), o2 = nibble_codes<2>(m1),
+                    o3 = nibble_codes<3>(m1);
+        const f32x2 ev[4] = {e0, e1, e2, e3}, od[4] = {o0, o1, o2, o3};
   #pragma unroll
-        for (int sh = 0; sh < 4; ++sh) {
-          uint32_t m = (cw[0] >> (2 * sh)) & 0x03030303u;  // bytes: channels 4*byte + sh
-          // hide m's known-zero bits so that each byte is widened by one
-          // byte-to-float conversion instead of a bit-field extract + convert
-          asm("" : "+v"(m));
-  #pragma unroll
-          for (int by = 0; by < 4; ++by) xh[4 * by + sh] = fmaf(float((m >> (8 * by)) & 0xffu), sf, xh[4 * by + sh]);
+        for (int by = 0; by < 4; ++by) {
+          xh[4 * by] = fmaf(ev[by][0], sf, xh[4 * by]);
+          xh[4 * by + 1] = fmaf(od[by][0], sf, xh[4 * by + 1]);
+          xh[4 * by + 2] = fmaf(ev[by][1], sf, xh[4 * by + 2]);
+          xh[4 * by + 3] = fmaf(od[by][1], sf, xh[4 * by + 3]);
         }
       } else {
+        // bytes of m0 hold the codes of channels 8w, 8w+2, 8w+4, 8w+6, those
+        // of m1 the odd channels
   #pragma unroll
-        for (int w = 0; w < 2; ++w)
-  #pragma unroll
-          for (int sh = 0; sh < 2; ++sh) {
-            uint32_t m = (cw[w] >> (4 * sh)) & 0x0f0f0f0fu;  // bytes: channels 8w + 2*byte + sh
-            asm("" : "+v"(m));
-  #pragma unroll
-            for (int by = 0; by < 4; ++by)
-              xh[8 * w + 2 * by + sh] = fmaf(float((m >> (8 * by)) & 0xffu), sf, xh[8 * w + 2 * by + sh]);
-          }
+        for (int w = 0; w < 2; ++w) {
+          const uint32_t m0 = cw[w] & 0x0f0f0f0fu, m1 = (cw[w] >> 4) & 0x0f0f0f0fu;
+          const f32x2 e0 = byte_codes<false>(m0), e1 = byte_codes<true>(m0);
+          const f32x2 o0 = byte_codes<false>(m1), o1 = byte_codes<true>(m1);
+          xh[8 * w] = fmaf(e0[0], sf, xh[8 * w]);
+          xh[8 * w + 1] = fmaf(o0[0], sf, xh[8 * w + 1]);
+          xh[8 * w + 2] = fmaf(e0[1], sf, xh[8 * w + 2]);
+          xh[8 * w + 3] = fmaf(o0[1], sf, xh[8 * w + 3]);
+          xh[8 * w + 4] = fmaf(e1[0], sf, xh[8 * w + 4]);
+          xh[8 * w + 5] = fmaf(o1[0], sf, xh[8 * w + 5]);
+          xh[8 * w + 6] = fmaf(e1[1], sf, xh[8 * w + 6]);
+          xh[8 * w + 7] = fmaf(o1[1], sf, xh[8 * w + 7]);
+        }
       }
     };
     // centroid channel e of the item as fp32
