@@ -82,6 +82,42 @@ __device__ __forceinline__ uint16_t f64_to_bf16_bits(double v) {
   return (uint16_t)(__float_as_uint(f) >> 16);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// The 2-bit codes in the low and high nibble of byte B of w (each nibble
+// 00qq): the conversion reads a nibble as an E2M1 value, which is q/2 for
+// these patterns, and scales by 2 (a power of two, applied exactly), giving
+// float(q) for two codes in one v_cvt_scalef32_pk_f32_fp4.
+template <int B>
+__device__ __forceinline__ f32x2 nibble_codes(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 2.0f, B);
+}
+// The 4-bit codes in bytes 2*HI and 2*HI+1 of w (each byte 0000qqqq): an
+// E4M3 byte below 16 has the value byte * 2^-9, so the conversion scaled by
+// 2^9 gives float(q) for two codes in one v_cvt_scalef32_pk_f32_fp8.
+template <bool HI>
+__device__ __forceinline__ f32x2 byte_codes(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 512.0f, HI);
+}
+
+// The 16 2-bit codes of word w (channel c at bits 2c, 2c+1) as floats.
+__device__ __forceinline__ void widen_codes2(uint32_t w, float *q) {
+  const uint32_t m0 = w & 0x33333333u, m1 = (w >> 2) & 0x33333333u;
+  const f32x2 e0 = nibble_codes<0>(m0), e1 = nibble_codes<1>(m0), e2 = nibble_codes<2>(m0), e3 = nibble_codes<3>(m0);
+  const f32x2 o0 = nibble_codes<0>(m1), o1 = nibble_codes<1>(m1), o2 = nibble_codes<2>(m1), o3 = nibble_codes<3>(m1);
+  q[0] = e0[0]; q[1] = o0[0]; q[2] = e0[1]; q[3] = o0[1];
+  q[4] = e1[0]; q[5] = o1[0]; q[6] = e1[1]; q[7] = o1[1];
+  q[8] = e2[0]; q[9] = o2[0]; q[10] = e2[1]; q[11] = o2[1];
+  q[12] = e3[0]; q[13] = o3[0]; q[14] = e3[1]; q[15] = o3[1];
+}
+// The 8 4-bit codes of word w (channel c at bits 4c .. 4c+3) as floats.
+__device__ __forceinline__ void widen_codes4(uint32_t w, float *q) {
+  const uint32_t m0 = w & 0x0f0f0f0fu, m1 = (w >> 4) & 0x0f0f0f0fu;
+  const f32x2 e0 = byte_codes<false>(m0), e1 = byte_codes<true>(m0);
+  const f32x2 o0 = byte_codes<false>(m1), o1 = byte_codes<true>(m1);
+  q[0] = e0[0]; q[1] = o0[0]; q[2] = e0[1]; q[3] = o0[1];
+  q[4] = e1[0]; q[5] = o1[0]; q[6] = e1[1]; q[7] = o1[1];
+}
+
 template <bool BF16>
 __device__ __forceinline__ float load_elem(const uint8_t *base, uint64_t idx) {
   if constexpr (BF16) return bf16_to_f32(((const uint16_t *)base)[idx]);
@@ -824,7 +860,6 @@ template <int D, int G, int BITS>
 __device__ __forceinline__ void add_stages(const uint8_t *st, const DevLayout &L, int h, int64_t tt,
                                            int g, float *xh) {
   constexpr int WORDS = G * BITS / 32;
-  constexpr uint32_t MASK = (1u << BITS) - 1u;
   for (int s = 0; s < L.S; ++s) {
     const uint8_t *cp = st + L.codes_off + uint64_t(s) * L.codes_stage + uint64_t(h) * L.codes_head +
                         uint64_t(tt) * L.codes_token + uint64_t(g) * (G * BITS / 8);
@@ -843,11 +878,14 @@ __device__ __forceinline__ void add_stages(const uint8_t *st, const DevLayout &L
                                             uint64_t(h) * L.meta_head + uint64_t(tt) * L.meta_token) + g);
     const float sf = f16_bits_to_f32(uint16_t(m & 0xffffu));
     const float zf = f16_bits_to_f32(uint16_t(m >> 16));
+    float q[G];
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      const float q = float((w[(j * BITS) / 32] >> ((j * BITS) % 32)) & MASK);
-      xh[j] = xh[j] + fmaf(q, sf, zf);
+    for (int i = 0; i < WORDS; ++i) {
+      if constexpr (BITS == 2) widen_codes2(w[i], q + 16 * i);
+      else widen_codes4(w[i], q + 8 * i);
     }
+#pragma unroll
+    for (int j = 0; j < G; ++j) xh[j] = xh[j] + fmaf(q[j], sf, zf);
   }
 }
 
@@ -1008,23 +1046,6 @@ __device__ __forceinline__ float pair_max(float x) {
 __device__ __forceinline__ float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-// The 2-bit codes in the low and high nibble of byte B of w (each nibble
-// 00qq): the conversion reads a nibble as an E2M1 value, which is q/2 for
-// these patterns, and scales by 2 (a power of two, applied exactly), giving
-// float(q) for two codes in one v_cvt_scalef32_pk_f32_fp4.
-template <int B>
-__device__ __forceinline__ f32x2 nibble_codes(uint32_t w) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 2.0f, B);
-}
-// The 4-bit codes in bytes 2*HI and 2*HI+1 of w (each byte 0000qqqq): an
-// E4M3 byte below 16 has the value byte * 2^-9, so the conversion scaled by
-// 2^9 gives float(q) for two codes in one v_cvt_scalef32_pk_f32_fp8.
-template <bool HI>
-__device__ __forceinline__ f32x2 byte_codes(uint32_t w) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 512.0f, HI);
 }
 
 __device__ __forceinline__ int chunk_of_lds(const int32_t *starts, int n_chunks, int t) {
@@ -1199,40 +1220,15 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     // one PRQ stage folded into 16 channels: xh[c] = fmaf(q_c, sigma, xh[c]) (the
     // zero points of all stages are added to the centroid beforehand)
     auto stage16 = [&](const uint32_t *cw, float sf, float *xh) {
+      float q[16];
       if constexpr (BITS == 2) {
-        // nibbles of m0 hold the codes of channels 0, 2, .., 14, those of m1
-        // channels 1, 3, .., 15; byte b of m0 gives channels 4b and 4b+2
-        const uint32_t m0 = cw[0] & 0x33333333u, m1 = (cw[0] >> 2) & 0x33333333u;
-        const f32x2 e0 = nibble_codes<0>(m0), e1 = nibble_codes<1>(m0), e2 = nibble_codes<2>(m0),
-                    e3 = nibble_codes<3>(m0);
-        const f32x2 o0 = nibble_codes<0>(m1), o1 = nibble_codes<1>(m1), o2 = nibble_codes<2>(m1),
-                    o3 = nibble_codes<3>(m1);
-        const f32x2 ev[4] = {e0, e1, e2, e3}, od[4] = {o0, o1, o2, o3};
-  #pragma unroll
-        for (int by = 0; by < 4; ++by) {
-          xh[4 * by] = fmaf(ev[by][0], sf, xh[4 * by]);
-          xh[4 * by + 1] = fmaf(od[by][0], sf, xh[4 * by + 1]);
-          xh[4 * by + 2] = fmaf(ev[by][1], sf, xh[4 * by + 2]);
-          xh[4 * by + 3] = fmaf(od[by][1], sf, xh[4 * by + 3]);
-        }
+        widen_codes2(cw[0], q);
       } else {
-        // bytes of m0 hold the codes of channels 8w, 8w+2, 8w+4, 8w+6, those
-        // of m1 the odd channels
-  #pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const uint32_t m0 = cw[w] & 0x0f0f0f0fu, m1 = (cw[w] >> 4) & 0x0f0f0f0fu;
-          const f32x2 e0 = byte_codes<false>(m0), e1 = byte_codes<true>(m0);
-          const f32x2 o0 = byte_codes<false>(m1), o1 = byte_codes<true>(m1);
-          xh[8 * w] = fmaf(e0[0], sf, xh[8 * w]);
-          xh[8 * w + 1] = fmaf(o0[0], sf, xh[8 * w + 1]);
-          xh[8 * w + 2] = fmaf(e0[1], sf, xh[8 * w + 2]);
-          xh[8 * w + 3] = fmaf(o0[1], sf, xh[8 * w + 3]);
-          xh[8 * w + 4] = fmaf(e1[0], sf, xh[8 * w + 4]);
-          xh[8 * w + 5] = fmaf(o1[0], sf, xh[8 * w + 5]);
-          xh[8 * w + 6] = fmaf(e1[1], sf, xh[8 * w + 6]);
-          xh[8 * w + 7] = fmaf(o1[1], sf, xh[8 * w + 7]);
-        }
+        widen_codes4(cw[0], q);
+        widen_codes4(cw[1], q + 8);
       }
+  #pragma unroll
+      for (int c = 0; c < 16; ++c) xh[c] = fmaf(q[c], sf, xh[c]);
     };
     // centroid channel e of the item as fp32
     auto cent_f32 = [&](int e) -> float {
