@@ -81,8 +81,9 @@ def cpu_baseline(cfgs, k_dev, v_dev, q_dev, budget_s=12.0):
 
 
 def recorded_traffic(kernel_source):
-    """HBM bytes per launch of the attention kernel, from the committed counter
-    summary, or None when the kernel source changed since it was taken."""
+    """HBM bytes of one qkv_attend call (attention kernel + merge), from the
+    committed counter summary, or None when the kernel source changed since
+    it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "k_attend3_wan_layer_pmc.txt")
     try:
@@ -181,7 +182,7 @@ def main():
         "reconstruct_GBps": round(recon_gbs, 2),
         "attend_q_tokens_per_s": round(Tq / (ms["attend"] * 1e-3), 1),
         "attend_TFLOPs": round(att_tflops, 2),
-        "roofline": {"kernel": "k_attend3 (qkv_attend is one launch at this shape)", "bound": "mfma",
+        "roofline": {"kernel": "qkv_attend (k_attend3 + k_attend_merge)", "bound": "mfma",
                      "achieved": round(att_tflops, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(att_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": recorded_traffic(os.path.join(ROOT, "kv_cache_quantization_head_amd",
