@@ -772,7 +772,8 @@ __global__ __launch_bounds__(256) void k_update_sorted(EncodeArgs a) {
 // items, y = head, z = stream.  Base = centroid of the token's cluster, or the
 // cross-layer prediction when a.pred is set (then the reconstruction is also
 // written to a.chain in bf16).
-template <int D, int G, int BITS, bool BF16>
+// CHAIN: also accumulate the reconstruction and write it to a.chain in bf16.
+template <int D, int G, int BITS, bool BF16, bool CHAIN>
 __global__ __launch_bounds__(256) void k_quantize(EncodeArgs a) {
   constexpr int EB = BF16 ? 2 : 4;
   constexpr int NG = D / G;
@@ -819,19 +820,42 @@ __global__ __launch_bounds__(256) void k_quantize(EncodeArgs a) {
     const float zf = f16_bits_to_f32(zb);
     const uint16_t sb = f32_to_f16_bits((mx - zf) / LEVELS);
     const float sf = f16_bits_to_f32(sb);
-    const bool live = sf != 0.0f;
-    const float inv = live ? 1.0f / sf : 0.0f;
     uint32_t w[WORDS];
+    if (sf != 0.0f) {
+      const float inv = 1.0f / sf;
+      // codes packed a byte at a time: the byte's codes combined as an exact
+      // small integer in fp32, then converted into its byte of the word
+      // (v_cvt_pk_u8_f32)
+      constexpr int PER_BYTE = 8 / BITS;
 #pragma unroll
-    for (int i = 0; i < WORDS; ++i) w[i] = 0;
+      for (int i = 0; i < WORDS; ++i) w[i] = 0;
 #pragma unroll
-    for (int j = 0; j < G; ++j) {
-      float q = 0.0f;
-      if (live) q = fminf(fmaxf(rintf((r[j] - zf) * inv), 0.0f), LEVELS);
-      w[(j * BITS) / 32] |= uint32_t(q) << ((j * BITS) % 32);
-      const float rh = fmaf(q, sf, zf);
-      r[j] = r[j] - rh;
-      xh[j] = xh[j] + rh;
+      for (int j0 = 0; j0 < G; j0 += PER_BYTE) {
+        float q[PER_BYTE];
+#pragma unroll
+        for (int e = 0; e < PER_BYTE; ++e) {
+          const int j = j0 + e;
+          q[e] = fminf(fmaxf(rintf((r[j] - zf) * inv), 0.0f), LEVELS);
+          const float rh = fmaf(q[e], sf, zf);
+          r[j] = r[j] - rh;
+          if constexpr (CHAIN) xh[j] = xh[j] + rh;
+        }
+        float byte = q[PER_BYTE - 1];
+#pragma unroll
+        for (int e = PER_BYTE - 2; e >= 0; --e) byte = fmaf(byte, float(1 << BITS), q[e]);
+        const int bi = j0 / PER_BYTE;   // byte index inside the group
+        w[bi / 4] = __builtin_amdgcn_cvt_pk_u8_f32(byte, bi % 4, w[bi / 4]);
+      }
+    } else {
+      // degenerate group: every code 0, r^ = z
+      const float rh = fmaf(0.0f, sf, zf);
+#pragma unroll
+      for (int i = 0; i < WORDS; ++i) w[i] = 0;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        r[j] = r[j] - rh;
+        if constexpr (CHAIN) xh[j] = xh[j] + rh;
+      }
     }
     uint8_t *cp = st + L.codes_off + uint64_t(s) * L.codes_stage + uint64_t(h) * L.codes_head +
                   uint64_t(tt) * L.codes_token + uint64_t(g) * (G * BITS / 8);
@@ -845,7 +869,7 @@ __global__ __launch_bounds__(256) void k_quantize(EncodeArgs a) {
                                 uint64_t(tt) * L.meta_token) + g;
     *mp = uint32_t(sb) | (uint32_t(zb) << 16);
   }
-  if (a.chain) {
+  if constexpr (CHAIN) {
     uint16_t *cp = a.chain + ((uint64_t(kv) * L.H + h) * uint64_t(a.n) + t) * D + g * G;
 #pragma unroll
     for (int j = 0; j < G; ++j) cp[j] = f32_to_bf16_bits(xh[j]);
@@ -1539,8 +1563,11 @@ static void launch_update_t(const EncodeArgs &a, int streams, hipStream_t st) {
 template <int D, int G, int BITS, bool BF>
 static void launch_quantize_t(const EncodeArgs &a, int streams, hipStream_t st) {
   const int64_t items = int64_t(a.n) * (D / G);
-  hipLaunchKernelGGL((k_quantize<D, G, BITS, BF>), dim3(cdiv(items, 256), a.L.H, streams), dim3(256), 0,
-                     st, a);
+  const dim3 grid(cdiv(items, 256), a.L.H, streams);
+  if (a.chain)
+    hipLaunchKernelGGL((k_quantize<D, G, BITS, BF, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_quantize<D, G, BITS, BF, false>), grid, dim3(256), 0, st, a);
 }
 
 template <int D, int G, int BITS, bool BF>
