@@ -927,6 +927,8 @@ __device__ __forceinline__ void centroid_base(const uint8_t *st, const DevLayout
   for (int j = 0; j < G; ++j) xh[j] = load_elem<CB_BF16>(crow, j);
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // Store the 16-byte pieces `v` of this thread's contiguous output run
 // (thread i of the wave owns bytes [i*P*16, (i+1)*P*16) of the wave's
 // region starting at `dst`) so that each store instruction writes one
@@ -942,7 +944,11 @@ __device__ __forceinline__ void store_wave_contiguous(uint4 *dst, uint4 *buf, co
 #pragma unroll
   for (int j = 0; j < P; ++j) {
     const int piece = j * 64 + lane;              // piece index inside the wave's region
-    if (piece < valid_lanes * P) dst[piece] = buf[piece];
+    if (piece < valid_lanes * P) {
+      // streaming output: non-temporal store (the data is not read back soon)
+      const uint4 v = buf[piece];
+      __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, (u32x4 *)&dst[piece]);
+    }
   }
   __builtin_amdgcn_wave_barrier();
 }
