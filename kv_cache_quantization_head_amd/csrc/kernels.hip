@@ -438,6 +438,9 @@ __global__ __launch_bounds__(512) void k_assign_mfma(EncodeArgs a, int tiles_per
     auto decode = [](uint32_t m) {
       return m == 0xffffffffu ? INFINITY : -2.0f * __uint_as_float(m & ~0x1ffu);
     };
+    // per token (lanes with g4 == 0 own the 16 tokens of each column block)
+    bool pair[2], full[2];
+    int k1v[2], k2v[2], kbest[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       const int t = tb + nt * 16 + c16;
@@ -446,58 +449,75 @@ __global__ __launch_bounds__(512) void k_assign_mfma(EncodeArgs a, int tiles_per
       const float E = float(D + 16) * 0x1p-22f * (xn[nt] + cmax) +
                       0x1p-12f * fmaxf(fabsf(d1), fmaxf(d2 == INFINITY ? 0.0f : fabsf(d2),
                                                         d3 == INFINITY ? 0.0f : fabsf(d3)));
-      const int k1 = int(m1[nt] & 0x1ffu), k2 = int(m2[nt] & 0x1ffu);
+      k1v[nt] = int(m1[nt] & 0x1ffu);
+      k2v[nt] = int(m2[nt] & 0x1ffu);
       // decided by the screen / exact check of the two best / exact check of all
-      const bool pair = valid && !(d2 - d1 > 2.0f * E) && (d3 - d1 > 2.0f * E);
-      const bool full = valid && !(d2 - d1 > 2.0f * E) && !(d3 - d1 > 2.0f * E);
-      int kbest = k1;
-      const uint64_t pm = __ballot(pair);
-      if (pm) {
-        // lane 2j / 2j+1 computes the exact distance of the j-th pair token to k1 / k2
-        const int np = __popcll(pm);
-        const int mine = pair ? __popcll(pm & ((uint64_t(1) << lane) - 1)) : -1;
-        int src_lane = -1;
+      pair[nt] = valid && !(d2 - d1 > 2.0f * E) && (d3 - d1 > 2.0f * E);
+      full[nt] = valid && !(d2 - d1 > 2.0f * E) && !(d3 - d1 > 2.0f * E);
+      kbest[nt] = k1v[nt];
+    }
+    // Exact decisions between the two best, for the pair tokens of both
+    // column blocks in one pass: the j-th pair token (column block 0 first,
+    // then 1; each in lane order) is scored by lanes 2j (its best) and 2j+1
+    // (its second best).
+    const uint64_t pm0 = __ballot(pair[0]), pm1 = __ballot(pair[1]);
+    if (pm0 | pm1) {
+      const int np0 = __popcll(pm0), np = np0 + __popcll(pm1);
+      const int j = lane >> 1;
+      const bool worker = j < np;
+      const int jn = j < np0 ? 0 : 1;                         // column block of token j
+      // lane of token j: the (j - np0*jn)-th set bit of its block's mask
+      uint64_t m = jn ? pm1 : pm0;
+      int rank = worker ? j - np0 * jn : 0, src = 0;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const uint64_t has = __ballot(mine == j);
-          if (has && lane / 2 == j) src_lane = __ffsll((unsigned long long)has) - 1;
-        }
-        const int sl = lane < 2 * np ? src_lane : 0;
-        const int tok_c16 = __shfl(c16, sl);
-        // both shuffles run on every lane (a shuffle under a divergent select
-        // would read the select taken by the source lane)
-        const int s_k1 = __shfl(k1, sl), s_k2 = __shfl(k2, sl);
-        const int cand = (lane & 1) ? s_k2 : s_k1;
-        double dd = INFINITY;
-        if (lane < 2 * np) {
-          const uint16_t *xrow = x + uint64_t(tb + nt * 16 + tok_c16) * D;
-          const uint16_t *crow = cbs + cand * KP;
-          dd = 0.0;
-          // the token row is read in one go (one memory latency, not D/8)
-          uint4 xr[D / 8];
+      for (int w = 32; w >= 1; w >>= 1) {
+        const int c = __popcll((m >> src) & ((uint64_t(1) << w) - 1));
+        if (rank >= c) { rank -= c; src += w; }
+      }
+      // both shuffles of each block run on every lane (a shuffle under a
+      // divergent select would read the select taken by the source lane)
+      const int a1 = __shfl(k1v[0], src), a2 = __shfl(k2v[0], src);
+      const int b1 = __shfl(k1v[1], src), b2 = __shfl(k2v[1], src);
+      const int cand = (lane & 1) ? (jn ? b2 : a2) : (jn ? b1 : a1);
+      double dd = INFINITY;
+      if (worker) {
+        const uint16_t *xrow = x + uint64_t(tb + jn * 16 + src) * D;
+        const uint16_t *crow = cbs + cand * KP;
+        dd = 0.0;
+        // the token row is read in one go (one memory latency, not D/8)
+        uint4 xr[D / 8];
 #pragma unroll
-          for (int j8 = 0; j8 < D / 8; ++j8) xr[j8] = *(const uint4 *)(xrow + j8 * 8);
+        for (int j8 = 0; j8 < D / 8; ++j8) xr[j8] = *(const uint4 *)(xrow + j8 * 8);
 #pragma unroll
-          for (int j8 = 0; j8 < D / 8; ++j8) {
-            const uint4 xv = xr[j8];
-            const uint4 cv = *(const uint4 *)(crow + j8 * 8);
-            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, cw[4] = {cv.x, cv.y, cv.z, cv.w};
+        for (int j8 = 0; j8 < D / 8; ++j8) {
+          const uint4 xv = xr[j8];
+          const uint4 cv = *(const uint4 *)(crow + j8 * 8);
+          const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, cw[4] = {cv.x, cv.y, cv.z, cv.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t xb = (xw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-              const uint32_t cbb = (cw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-              const double diff = double(bf16_to_f32(xb)) - double(bf16_to_f32(cbb));
-              dd = dd + diff * diff;
-            }
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t xb = (xw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            const uint32_t cbb = (cw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            const double diff = double(bf16_to_f32(xb)) - double(bf16_to_f32(cbb));
+            dd = dd + diff * diff;
           }
         }
-        const double od = __shfl_xor(dd, 1);
-        const int oc = __shfl_xor(cand, 1);
-        const int win = (dd < od || (dd == od && cand < oc)) ? cand : oc;
-        const int got = __shfl(win, 2 * (mine < 0 ? 0 : mine));
-        if (pair) kbest = got;
       }
-      uint64_t fm = __ballot(full);
+      const double od = __shfl_xor(dd, 1);
+      const int oc = __shfl_xor(cand, 1);
+      const int win = (dd < od || (dd == od && cand < oc)) ? cand : oc;
+      // back to the owners: token of block nt at position p of its mask
+      const int p0 = __popcll(pm0 & ((uint64_t(1) << lane) - 1));
+      const int p1 = np0 + __popcll(pm1 & ((uint64_t(1) << lane) - 1));
+      const int got0 = __shfl(win, 2 * (pair[0] ? p0 : 0));
+      const int got1 = __shfl(win, 2 * (pair[1] ? p1 : 0));
+      if (pair[0]) kbest[0] = got0;
+      if (pair[1]) kbest[1] = got1;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int t = tb + nt * 16 + c16;
+      const bool valid = t < a.n && g4 == 0;
+      uint64_t fm = __ballot(full[nt]);
       while (fm) {
         const int src = __ffsll((unsigned long long)fm) - 1;
         fm &= fm - 1;
@@ -528,12 +548,12 @@ __global__ __launch_bounds__(512) void k_assign_mfma(EncodeArgs a, int tiles_per
           const int ok = __shfl_xor(bk, off);
           if (ob < best || (ob == best && ok < bk)) { best = ob; bk = ok; }
         }
-        if (lane == src) kbest = bk;
+        if (lane == src) kbest[nt] = bk;
       }
       if (valid) {
         const int64_t tt = int64_t(a.t0) + t;
-        if (L.id_bytes == 1) ids[tt] = uint8_t(kbest);
-        else ((uint16_t *)ids)[tt] = uint16_t(kbest);
+        if (L.id_bytes == 1) ids[tt] = uint8_t(kbest[nt]);
+        else ((uint16_t *)ids)[tt] = uint16_t(kbest[nt]);
       }
     }
   }
