@@ -593,31 +593,51 @@ __device__ __forceinline__ void finalize_centroid(uint8_t *cb, float *cn, int k,
 // y = head, z = stream).  The block stages a segment of the call's ids in LDS;
 // each wave scans it in token order, appending its cluster's member token
 // indices to a list in LDS; a full list (or the end of the ids) is drained by
-// summing the listed rows in list order with UPD_UNROLL row loads in flight,
-// so every centroid sum is the sequential fp64 sum in token order.
+// summing the listed rows in list order with UPD_UNROLL (bf16 rows of 128
+// channels: UPD_UNROLL_BF, kept packed) row loads in flight, so every
+// centroid sum is the sequential fp64 sum in token order.
 constexpr int UPD_SEG = 16384;      // ids staged per pass
 constexpr int UPD_CAP = 512;        // list entries per cluster
 constexpr int UPD_UNROLL = 32;
+constexpr int UPD_UNROLL_BF = 64;    // bf16 rows kept packed (one register per row and lane)
 
 template <int D, bool BF16>
 __device__ __forceinline__ void drain_list(const uint8_t *x, const int32_t *list, int count, double *acc,
                                            int lane) {
   constexpr int EB = BF16 ? 2 : 4;
   constexpr int CPL = D / 64;
-  for (int i = 0; i < count; i += UPD_UNROLL) {
-    float v[UPD_UNROLL][CPL];
+  if constexpr (BF16 && CPL == 2) {
+    for (int i = 0; i < count; i += UPD_UNROLL_BF) {
+      uint32_t v[UPD_UNROLL_BF];
 #pragma unroll
-    for (int e = 0; e < UPD_UNROLL; ++e) {
-      const int row = list[min(i + e, count - 1)];   // tail: reload the last row, not added
-      const uint8_t *rp = x + uint64_t(row) * D * EB;
+      for (int e = 0; e < UPD_UNROLL_BF; ++e) {
+        const int row = list[min(i + e, count - 1)];   // tail: reload the last row, not added
+        v[e] = *((const uint32_t *)(x + uint64_t(row) * D * EB) + lane);
+      }
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) v[e][c] = load_elem<BF16>(rp, lane * CPL + c);
+      for (int e = 0; e < UPD_UNROLL_BF; ++e) {
+        if (i + e < count) {
+          acc[0] = acc[0] + double(__uint_as_float(v[e] << 16));
+          acc[1] = acc[1] + double(__uint_as_float(v[e] & 0xffff0000u));
+        }
+      }
     }
+  } else {
+    for (int i = 0; i < count; i += UPD_UNROLL) {
+      float v[UPD_UNROLL][CPL];
 #pragma unroll
-    for (int e = 0; e < UPD_UNROLL; ++e) {
-      if (i + e < count) {
+      for (int e = 0; e < UPD_UNROLL; ++e) {
+        const int row = list[min(i + e, count - 1)];   // tail: reload the last row, not added
+        const uint8_t *rp = x + uint64_t(row) * D * EB;
 #pragma unroll
-        for (int c = 0; c < CPL; ++c) acc[c] = acc[c] + double(v[e][c]);
+        for (int c = 0; c < CPL; ++c) v[e][c] = load_elem<BF16>(rp, lane * CPL + c);
+      }
+#pragma unroll
+      for (int e = 0; e < UPD_UNROLL; ++e) {
+        if (i + e < count) {
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) acc[c] = acc[c] + double(v[e][c]);
+        }
       }
     }
   }
