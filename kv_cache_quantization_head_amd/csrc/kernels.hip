@@ -1606,6 +1606,141 @@ __global__ __launch_bounds__(256) void k_xl_predict(XlArgs a, int kv0) {
   a.pred[(uint64_t(kv) * HD * a.n) + (uint64_t(h) * a.n + t) * a.D + i] = float(acc);
 }
 
+// Tiled forms of the two kernels above, for r <= 64.  Every product is of two
+// bf16 values, hence exact in fp64, so fma(p, q, acc) equals acc + p*q rounded
+// once: each output is still the same sequence of fp64 additions in the same
+// order as the per-thread loops above (and the oracle).
+
+// proj[t][k] = bf16(sum over m = 0 .. H*D-1 of y[t][m] V[m][k]).  Block = 256
+// threads = (token groups of 4) x (output groups of 8: 4 groups for r <= 32,
+// else 8), i.e. 256 or 128 tokens; the m axis is staged through LDS 32 at a
+// time (transposed, fp32; outputs past r read zero columns).
+constexpr int XL_MC = 32;
+__host__ __device__ constexpr int xl_project_groups(int r) { return r <= 32 ? 4 : 8; }
+__global__ __launch_bounds__(256) void k_xl_project2(XlArgs a, int kv0) {
+  __shared__ float ys[XL_MC][256 + 4];    // [m][token]
+  __shared__ float vs[XL_MC][64 + 4];     // [m][k]
+  const int KG = xl_project_groups(a.r), KP = 8 * KG, TG = 256 / KG, TT = 4 * TG;
+  const int tid = threadIdx.x, kv = kv0 + blockIdx.y;
+  const int kg = tid % KG, tg = tid / KG;
+  const int t0 = blockIdx.x * TT;
+  const uint64_t HD = uint64_t(a.H) * a.D;
+  const uint16_t *Vw = a.weights + uint64_t(kv) * a.kv_weight_stride + HD * a.D + HD * a.r;
+  const uint16_t *y = a.chain + uint64_t(kv) * HD * a.n;
+  double acc[4][8];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[u][c] = 0.0;
+  for (uint64_t m0 = 0; m0 < HD; m0 += XL_MC) {
+    const int hh = int(m0 / a.D), j0 = int(m0 % a.D);   // a chunk lies inside one head (D % 32 == 0)
+    __syncthreads();                                    // previous chunk consumed
+    for (int e = tid; e < TT * XL_MC; e += 256) {
+      const int tt = e / XL_MC, jj = e % XL_MC, t = min(t0 + tt, a.n - 1);
+      ys[jj][tt] = bf16_to_f32(y[(uint64_t(hh) * a.n + t) * a.D + j0 + jj]);
+    }
+    for (int e = tid; e < XL_MC * KP; e += 256) {
+      const int jj = e / KP, kk = e % KP;
+      vs[jj][kk] = kk < a.r ? bf16_to_f32(Vw[(m0 + jj) * a.r + kk]) : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int jj = 0; jj < XL_MC; ++jj) {
+      const float4 yv = *(const float4 *)&ys[jj][4 * tg];
+      const float4 v0 = *(const float4 *)&vs[jj][8 * kg], v1 = *(const float4 *)&vs[jj][8 * kg + 4];
+      const double yd[4] = {double(yv.x), double(yv.y), double(yv.z), double(yv.w)};
+      const double vd[8] = {double(v0.x), double(v0.y), double(v0.z), double(v0.w),
+                            double(v1.x), double(v1.y), double(v1.z), double(v1.w)};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[u][c] = fma(yd[u], vd[c], acc[u][c]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int t = t0 + 4 * tg + u;
+    if (t >= a.n) continue;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int kk = 8 * kg + c;
+      if (kk < a.r) a.proj[(uint64_t(kv) * a.n + t) * a.r + kk] = bf16_to_f32(f64_to_bf16_bits(acc[u][c]));
+    }
+  }
+}
+
+// pred[h][t][i] = sum_j B_h[i][j] y[t][j] (order j), then + sum_k U[h*D+i][k]
+// w[t][k] (order k), fp64, rounded once to fp32.  Block = 256 threads =
+// (token groups of 4) x (output groups of 8) over token tiles of 4*256/(D/8)
+// tokens; B_h and U_h are staged once per block (transposed, fp32) and the
+// block walks every gridDim.x-th token tile.
+__global__ __launch_bounds__(256) void k_xl_predict2(XlArgs a, int kv0) {
+  extern __shared__ float xs[];
+  const int D = a.D, RP = (a.r + 7) & ~7;
+  const int IG = D / 8, TG = 256 / IG, TT = 4 * TG;
+  float *bsT = xs;                            // [D j][D i]
+  float *usT = bsT + D * D;                   // [RP k][D i]
+  float *ysT = usT + RP * D;                  // [D j][TT]
+  float *wsT = ysT + D * TT;                  // [RP k][TT]
+  const int tid = threadIdx.x, h = blockIdx.y, kv = kv0 + blockIdx.z;
+  const int ig = tid % IG, tg = tid / IG;
+  const uint64_t HD = uint64_t(a.H) * D;
+  const uint16_t *W = a.weights + uint64_t(kv) * a.kv_weight_stride;
+  const uint16_t *B = W + uint64_t(h) * D * D;
+  const uint16_t *U = W + HD * D + uint64_t(h) * D * a.r;
+  const uint16_t *y = a.chain + uint64_t(kv) * HD * a.n + uint64_t(h) * a.n * D;
+  const float *w = a.proj + uint64_t(kv) * a.n * a.r;
+  for (int e = tid; e < D * D; e += 256) {
+    const int i = e / D, j = e % D;
+    bsT[j * D + i] = bf16_to_f32(B[e]);
+  }
+  for (int e = tid; e < D * RP; e += 256) {
+    const int i = e / RP, kk = e % RP;
+    usT[kk * D + i] = kk < a.r ? bf16_to_f32(U[uint64_t(i) * a.r + kk]) : 0.0f;
+  }
+  const int n_tiles = (a.n + TT - 1) / TT;
+  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const int t0 = tile * TT;
+    __syncthreads();                          // weights staged / previous tile consumed
+    for (int e = tid; e < TT * D; e += 256) {
+      const int tt = e / D, j = e % D, t = min(t0 + tt, a.n - 1);
+      ysT[j * TT + tt] = bf16_to_f32(y[uint64_t(t) * D + j]);
+    }
+    for (int e = tid; e < TT * RP; e += 256) {
+      const int tt = e / RP, kk = e % RP, t = min(t0 + tt, a.n - 1);
+      wsT[kk * TT + tt] = kk < a.r ? w[uint64_t(t) * a.r + kk] : 0.0f;
+    }
+    __syncthreads();
+    double acc[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[u][c] = 0.0;
+    auto step = [&](const float *ycol, const float *bcol) {
+      const float4 yv = *(const float4 *)(ycol + 4 * tg);
+      const float4 b0 = *(const float4 *)(bcol + 8 * ig), b1 = *(const float4 *)(bcol + 8 * ig + 4);
+      const double yd[4] = {double(yv.x), double(yv.y), double(yv.z), double(yv.w)};
+      const double bd[8] = {double(b0.x), double(b0.y), double(b0.z), double(b0.w),
+                            double(b1.x), double(b1.y), double(b1.z), double(b1.w)};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[u][c] = fma(bd[c], yd[u], acc[u][c]);
+    };
+#pragma unroll 4
+    for (int j = 0; j < D; ++j) step(ysT + j * TT, bsT + j * D);
+    for (int kk = 0; kk < a.r; ++kk) step(wsT + kk * TT, usT + kk * D);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + 4 * tg + u;
+      if (t >= a.n) continue;
+      float *pp = a.pred + (uint64_t(kv) * HD * a.n) + (uint64_t(h) * a.n + t) * D + 8 * ig;
+      *(float4 *)pp = make_float4(float(acc[u][0]), float(acc[u][1]), float(acc[u][2]), float(acc[u][3]));
+      *(float4 *)(pp + 4) = make_float4(float(acc[u][4]), float(acc[u][5]), float(acc[u][6]), float(acc[u][7]));
+    }
+  }
+}
+
 // chunk table after a rewind: blockIdx.x = stream of the range
 __global__ void k_set_header(uint8_t *arena, DevLayout L, int layer0, int n_chunks, int n_tokens) {
   if (threadIdx.x != 0) return;
@@ -1734,11 +1869,20 @@ void launch_attend(const AttnArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(k_attend_merge, dim3(cdiv(int64_t(a.n_q) * (a.L.D / 4), 256), a.L.H), dim3(256), 0, st, a);
 }
 void launch_xl_predict(const XlArgs &a, int kv0, int n_kv, hipStream_t st) {
-  int rp = 1;
-  while (rp < a.r) rp <<= 1;
-  const int tpb = 256 / rp;
-  hipLaunchKernelGGL(k_xl_project, dim3(cdiv(a.n, tpb), n_kv), dim3(256), 0, st, a, kv0);
-  hipLaunchKernelGGL(k_xl_predict, dim3(cdiv(int64_t(a.n) * a.D, 256), a.H, n_kv), dim3(256), 0, st, a, kv0);
+  // tiled kernels (fp32 LDS staging of the bf16 operands)
+  const int TT = 4 * (256 / xl_project_groups(a.r));
+  hipLaunchKernelGGL(k_xl_project2, dim3(cdiv(a.n, TT), n_kv), dim3(256), 0, st, a, kv0);
+  const int RP = (a.r + 7) & ~7;
+  const int IG = a.D / 8, TTp = 4 * (256 / IG);
+  const size_t lds = size_t(a.D * a.D + RP * a.D + a.D * TTp + RP * TTp) * 4;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_xl_predict2),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  // one block per CU fits (the staged weights); about 256 blocks in all,
+  // each walking every gx-th token tile of its (head, kv)
+  const int64_t n_tiles = cdiv(a.n, TTp);
+  const int64_t hk = int64_t(a.H) * n_kv;
+  const unsigned gx = unsigned(std::max<int64_t>(1, std::min<int64_t>(n_tiles, (256 + hk - 1) / hk)));
+  hipLaunchKernelGGL(k_xl_predict2, dim3(gx, a.H, n_kv), dim3(256), lds, st, a, kv0);
 }
 void launch_set_header(uint8_t *arena, const DevLayout &L, int layer0, int n_layers, int n_chunks,
                        int n_tokens, hipStream_t st) {
