@@ -1563,53 +1563,11 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttnArgs a) {
 
 // ------------------------------------------------------------ cross layer
 
-// p[t][k] = sum over m = 0..H*D-1 of V[m][k] * y[t][m] in fp64 (order m),
-// rounded once to bf16.  blockIdx.x = token tile, y = kv index (kv0 + y).
-__global__ __launch_bounds__(256) void k_xl_project(XlArgs a, int kv0) {
-  int rp = 1;
-  while (rp < a.r) rp <<= 1;
-  const int tpb = 256 / rp;
-  const int t = blockIdx.x * tpb + int(threadIdx.x) / rp;
-  const int k = int(threadIdx.x) % rp;
-  const int kv = kv0 + blockIdx.y;
-  if (t >= a.n || k >= a.r) return;
-  const uint64_t HD = uint64_t(a.H) * a.D;
-  const uint16_t *Vw = a.weights + uint64_t(kv) * a.kv_weight_stride + HD * a.D + HD * a.r;
-  const uint16_t *y = a.chain + uint64_t(kv) * HD * a.n;
-  double acc = 0.0;
-  for (int hh = 0; hh < a.H; ++hh) {
-    const uint16_t *yr = y + (uint64_t(hh) * a.n + t) * a.D;
-    for (int j = 0; j < a.D; ++j) {
-      const uint64_t m = uint64_t(hh) * a.D + j;
-      acc = acc + double(bf16_to_f32(yr[j])) * double(bf16_to_f32(Vw[m * a.r + k]));
-    }
-  }
-  a.proj[(uint64_t(kv) * a.n + t) * a.r + k] = bf16_to_f32(f64_to_bf16_bits(acc));
-}
-
-// pred[h][t][i] = sum_j B_h[i][j] y_h[t][j] (order j) then + sum_k U[h*D+i][k] w[t][k]
-// (order k), fp64, rounded once to fp32.  One thread per (t, i); y = head, z = kv.
-__global__ __launch_bounds__(256) void k_xl_predict(XlArgs a, int kv0) {
-  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (idx >= int64_t(a.n) * a.D) return;
-  const int t = int(idx / a.D), i = int(idx % a.D);
-  const int h = blockIdx.y, kv = kv0 + blockIdx.z;
-  const uint64_t HD = uint64_t(a.H) * a.D;
-  const uint16_t *W = a.weights + uint64_t(kv) * a.kv_weight_stride;
-  const uint16_t *B = W + uint64_t(h) * a.D * a.D + uint64_t(i) * a.D;
-  const uint16_t *U = W + HD * a.D + (uint64_t(h) * a.D + i) * a.r;
-  const uint16_t *y = a.chain + (uint64_t(kv) * HD * a.n) + (uint64_t(h) * a.n + t) * a.D;
-  const float *w = a.proj + (uint64_t(kv) * a.n + t) * a.r;
-  double acc = 0.0;
-  for (int j = 0; j < a.D; ++j) acc = acc + double(bf16_to_f32(B[j])) * double(bf16_to_f32(y[j]));
-  for (int k = 0; k < a.r; ++k) acc = acc + double(bf16_to_f32(U[k])) * double(w[k]);
-  a.pred[(uint64_t(kv) * HD * a.n) + (uint64_t(h) * a.n + t) * a.D + i] = float(acc);
-}
-
-// Tiled forms of the two kernels above, for r <= 64.  Every product is of two
-// bf16 values, hence exact in fp64, so fma(p, q, acc) equals acc + p*q rounded
-// once: each output is still the same sequence of fp64 additions in the same
-// order as the per-thread loops above (and the oracle).
+// Cross-layer prediction (r <= 64), in fp64 with a fixed summation order per
+// output: the projection sums over m = 0 .. H*D-1, the prediction over j, then
+// over k.  Every product is of two bf16 values, hence exact in fp64, so
+// fma(p, q, acc) equals acc + p*q rounded once: each output is exactly that
+// sequence of fp64 additions, however the work is tiled.
 
 // proj[t][k] = bf16(sum over m = 0 .. H*D-1 of y[t][m] V[m][k]).  Block = 256
 // threads = (token groups of 4) x (output groups of 8: 4 groups for r <= 32,
@@ -1617,7 +1575,7 @@ __global__ __launch_bounds__(256) void k_xl_predict(XlArgs a, int kv0) {
 // time (transposed, fp32; outputs past r read zero columns).
 constexpr int XL_MC = 32;
 __host__ __device__ constexpr int xl_project_groups(int r) { return r <= 32 ? 4 : 8; }
-__global__ __launch_bounds__(256) void k_xl_project2(XlArgs a, int kv0) {
+__global__ __launch_bounds__(256) void k_xl_project(XlArgs a, int kv0) {
   __shared__ float ys[XL_MC][256 + 4];    // [m][token]
   __shared__ float vs[XL_MC][64 + 4];     // [m][k]
   const int KG = xl_project_groups(a.r), KP = 8 * KG, TG = 256 / KG, TT = 4 * TG;
@@ -1674,7 +1632,7 @@ __global__ __launch_bounds__(256) void k_xl_project2(XlArgs a, int kv0) {
 // (token groups of 4) x (output groups of 8) over token tiles of 4*256/(D/8)
 // tokens; B_h and U_h are staged once per block (transposed, fp32) and the
 // block walks every gridDim.x-th token tile.
-__global__ __launch_bounds__(256) void k_xl_predict2(XlArgs a, int kv0) {
+__global__ __launch_bounds__(256) void k_xl_predict(XlArgs a, int kv0) {
   extern __shared__ float xs[];
   const int D = a.D, RP = (a.r + 7) & ~7;
   const int IG = D / 8, TG = 256 / IG, TT = 4 * TG;
@@ -1871,18 +1829,18 @@ void launch_attend(const AttnArgs &a, hipStream_t st) {
 void launch_xl_predict(const XlArgs &a, int kv0, int n_kv, hipStream_t st) {
   // tiled kernels (fp32 LDS staging of the bf16 operands)
   const int TT = 4 * (256 / xl_project_groups(a.r));
-  hipLaunchKernelGGL(k_xl_project2, dim3(cdiv(a.n, TT), n_kv), dim3(256), 0, st, a, kv0);
+  hipLaunchKernelGGL(k_xl_project, dim3(cdiv(a.n, TT), n_kv), dim3(256), 0, st, a, kv0);
   const int RP = (a.r + 7) & ~7;
   const int IG = a.D / 8, TTp = 4 * (256 / IG);
   const size_t lds = size_t(a.D * a.D + RP * a.D + a.D * TTp + RP * TTp) * 4;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_xl_predict2),
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_xl_predict),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   // one block per CU fits (the staged weights); about 256 blocks in all,
   // each walking every gx-th token tile of its (head, kv)
   const int64_t n_tiles = cdiv(a.n, TTp);
   const int64_t hk = int64_t(a.H) * n_kv;
   const unsigned gx = unsigned(std::max<int64_t>(1, std::min<int64_t>(n_tiles, (256 + hk - 1) / hk)));
-  hipLaunchKernelGGL(k_xl_predict2, dim3(gx, a.H, n_kv), dim3(256), lds, st, a, kv0);
+  hipLaunchKernelGGL(k_xl_predict, dim3(gx, a.H, n_kv), dim3(256), lds, st, a, kv0);
 }
 void launch_set_header(uint8_t *arena, const DevLayout &L, int layer0, int n_layers, int n_chunks,
                        int n_tokens, hipStream_t st) {
