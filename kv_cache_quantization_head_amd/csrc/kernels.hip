@@ -1630,16 +1630,16 @@ __global__ __launch_bounds__(256) void k_xl_project(XlArgs a, int kv0) {
 // pred[h][t][i] = sum_j B_h[i][j] y[t][j] (order j), then + sum_k U[h*D+i][k]
 // w[t][k] (order k), fp64, rounded once to fp32.  Block = 256 threads =
 // (token groups of 4) x (output groups of 8) over token tiles of 4*256/(D/8)
-// tokens; B_h and U_h are staged once per block (transposed, fp32) and the
-// block walks every gridDim.x-th token tile.
+// tokens; B_h and U_h are staged once per block (transposed, as bf16: two
+// blocks fit a CU) and the block walks every gridDim.x-th token tile.
 __global__ __launch_bounds__(256) void k_xl_predict(XlArgs a, int kv0) {
-  extern __shared__ float xs[];
+  extern __shared__ uint16_t xs16[];
   const int D = a.D, RP = (a.r + 7) & ~7;
   const int IG = D / 8, TG = 256 / IG, TT = 4 * TG;
-  float *bsT = xs;                            // [D j][D i]
-  float *usT = bsT + D * D;                   // [RP k][D i]
-  float *ysT = usT + RP * D;                  // [D j][TT]
-  float *wsT = ysT + D * TT;                  // [RP k][TT]
+  uint16_t *bsT = xs16;                       // [D j][D i] bf16
+  uint16_t *usT = bsT + D * D;                // [RP k][D i]
+  uint16_t *ysT = usT + RP * D;               // [D j][TT]
+  uint16_t *wsT = ysT + D * TT;               // [RP k][TT]
   const int tid = threadIdx.x, h = blockIdx.y, kv = kv0 + blockIdx.z;
   const int ig = tid % IG, tg = tid / IG;
   const uint64_t HD = uint64_t(a.H) * D;
@@ -1650,11 +1650,11 @@ __global__ __launch_bounds__(256) void k_xl_predict(XlArgs a, int kv0) {
   const float *w = a.proj + uint64_t(kv) * a.n * a.r;
   for (int e = tid; e < D * D; e += 256) {
     const int i = e / D, j = e % D;
-    bsT[j * D + i] = bf16_to_f32(B[e]);
+    bsT[j * D + i] = B[e];
   }
   for (int e = tid; e < D * RP; e += 256) {
     const int i = e / RP, kk = e % RP;
-    usT[kk * D + i] = kk < a.r ? bf16_to_f32(U[uint64_t(i) * a.r + kk]) : 0.0f;
+    usT[kk * D + i] = kk < a.r ? U[uint64_t(i) * a.r + kk] : uint16_t(0);
   }
   const int n_tiles = (a.n + TT - 1) / TT;
   for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
@@ -1662,11 +1662,12 @@ __global__ __launch_bounds__(256) void k_xl_predict(XlArgs a, int kv0) {
     __syncthreads();                          // weights staged / previous tile consumed
     for (int e = tid; e < TT * D; e += 256) {
       const int tt = e / D, j = e % D, t = min(t0 + tt, a.n - 1);
-      ysT[j * TT + tt] = bf16_to_f32(y[uint64_t(t) * D + j]);
+      ysT[j * TT + tt] = y[uint64_t(t) * D + j];
     }
     for (int e = tid; e < TT * RP; e += 256) {
       const int tt = e / RP, kk = e % RP, t = min(t0 + tt, a.n - 1);
-      wsT[kk * TT + tt] = kk < a.r ? w[uint64_t(t) * a.r + kk] : 0.0f;
+      // w holds bf16 values (rounded in the projection): exact in bf16
+      wsT[kk * TT + tt] = kk < a.r ? f32_to_bf16_bits(w[uint64_t(t) * a.r + kk]) : uint16_t(0);
     }
     __syncthreads();
     double acc[4][8];
@@ -1674,12 +1675,15 @@ __global__ __launch_bounds__(256) void k_xl_predict(XlArgs a, int kv0) {
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[u][c] = 0.0;
-    auto step = [&](const float *ycol, const float *bcol) {
-      const float4 yv = *(const float4 *)(ycol + 4 * tg);
-      const float4 b0 = *(const float4 *)(bcol + 8 * ig), b1 = *(const float4 *)(bcol + 8 * ig + 4);
-      const double yd[4] = {double(yv.x), double(yv.y), double(yv.z), double(yv.w)};
-      const double bd[8] = {double(b0.x), double(b0.y), double(b0.z), double(b0.w),
-                            double(b1.x), double(b1.y), double(b1.z), double(b1.w)};
+    auto step = [&](const uint16_t *ycol, const uint16_t *bcol) {
+      const uint2 yv = *(const uint2 *)(ycol + 4 * tg);
+      const uint4 bv = *(const uint4 *)(bcol + 8 * ig);
+      const double yd[4] = {double(__uint_as_float(yv.x << 16)), double(__uint_as_float(yv.x & 0xffff0000u)),
+                            double(__uint_as_float(yv.y << 16)), double(__uint_as_float(yv.y & 0xffff0000u))};
+      const double bd[8] = {double(__uint_as_float(bv.x << 16)), double(__uint_as_float(bv.x & 0xffff0000u)),
+                            double(__uint_as_float(bv.y << 16)), double(__uint_as_float(bv.y & 0xffff0000u)),
+                            double(__uint_as_float(bv.z << 16)), double(__uint_as_float(bv.z & 0xffff0000u)),
+                            double(__uint_as_float(bv.w << 16)), double(__uint_as_float(bv.w & 0xffff0000u))};
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -1832,14 +1836,14 @@ void launch_xl_predict(const XlArgs &a, int kv0, int n_kv, hipStream_t st) {
   hipLaunchKernelGGL(k_xl_project, dim3(cdiv(a.n, TT), n_kv), dim3(256), 0, st, a, kv0);
   const int RP = (a.r + 7) & ~7;
   const int IG = a.D / 8, TTp = 4 * (256 / IG);
-  const size_t lds = size_t(a.D * a.D + RP * a.D + a.D * TTp + RP * TTp) * 4;
+  const size_t lds = size_t(a.D * a.D + RP * a.D + a.D * TTp + RP * TTp) * 2;
   (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_xl_predict),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-  // one block per CU fits (the staged weights); about 256 blocks in all,
+  // two blocks per CU fit (the staged weights); about 512 blocks in all,
   // each walking every gx-th token tile of its (head, kv)
   const int64_t n_tiles = cdiv(a.n, TTp);
   const int64_t hk = int64_t(a.H) * n_kv;
-  const unsigned gx = unsigned(std::max<int64_t>(1, std::min<int64_t>(n_tiles, (256 + hk - 1) / hk)));
+  const unsigned gx = unsigned(std::max<int64_t>(1, std::min<int64_t>(n_tiles, (512 + hk - 1) / hk)));
   hipLaunchKernelGGL(k_xl_predict, dim3(gx, a.H, n_kv), dim3(256), lds, st, a, kv0);
 }
 void launch_set_header(uint8_t *arena, const DevLayout &L, int layer0, int n_layers, int n_chunks,
