@@ -31,6 +31,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--xlayer", action="store_true",
+                    help="instead of the default step: time the cross-layer encode of one "
+                         "wide-head layer (K and V [40, 62400, 128] bf16, rank 32, C = 512, "
+                         "2-stage INT2, G = 64), predicted from the previous layer")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (a known-size "
                          "reference for HBM byte counters)")
@@ -99,12 +103,67 @@ def recorded_traffic(kernel_source):
         return None
 
 
+def xlayer_main(args):
+    """Cross-layer residual mode on the wide-head shape.  A step rewinds both
+    layers, encodes layer 0 with SAS and then layer 1 from its prediction
+    (projection, prediction, PRQ of the residual); each call is timed with HIP
+    events on the current stream."""
+    import torch
+    import kv_cache_quantization_head_amd as qkv
+    import synth
+
+    dev = torch.device("cuda:0")
+    cfgs = synth.scaled(synth.WIDE_HEAD, n_layers=2)
+    H, T, d, C, r = cfgs.n_heads, cfgs.tokens, cfgs.head_dim, cfgs.n_clusters, cfgs.xlayer_rank
+    parts = []
+    for kv in (0, 1):
+        B, U, V = synth.predictor(cfgs, 0, kv, rank=r)
+        parts += [B.reshape(-1), U.reshape(-1), V.reshape(-1)]
+    cfg = qkv.config(2, H, d, C, cfgs.n_stages, cfgs.bits, cfgs.group, kmeans_iters=cfgs.iters,
+                     max_tokens=T, max_chunks=1, kv_dtype=qkv.QKV_BF16, max_query_tokens=0, xlayer=1,
+                     xlayer_rank=r)
+    codec = qkv.Codec(cfg, device=dev, predictor=torch.cat(parts).to(dev))
+    ks = torch.stack([synth.kv_tokens(cfgs, l, 0, 0, T, device=dev) for l in range(2)])
+    vs = torch.stack([synth.kv_tokens(cfgs, l, 1, 0, T, device=dev) for l in range(2)])
+    ev = []
+
+    def step(record):
+        codec.rewind(0, 2, 0)
+        m = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        m[0].record()
+        codec.encode_chunk(ks[:1], vs[:1], layer0=0)
+        m[1].record()
+        codec.encode_chunk(ks[1:], vs[1:], layer0=1)
+        m[2].record()
+        if record:
+            ev.append(m)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    sas = sum(m[0].elapsed_time(m[1]) for m in ev) / len(ev)
+    xl = sum(m[1].elapsed_time(m[2]) for m in ev) / len(ev)
+    print(json.dumps({
+        "metric": "cross-layer encode of one layer (K and V)", "value": round(xl, 4), "unit": "ms",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
+        "dtype": "bf16 in, fp64 prediction", "data": "synthetic (seeded prototype/drift/outlier generator)",
+        "config": {"workload": "wide_head layer: K,V bf16 [40, 62400, 128], C=512, 2-stage INT2 G=64, "
+                               "cross-layer rank 32", "heads": H, "tokens": T, "rank": r},
+        "sas_layer_ms": round(sas, 4)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; the path shards by heads/layers "
                           "with no exchange (see the design notes), but no multi-GPU run exists"}))
         sys.exit(2)
+    if args.xlayer:
+        xlayer_main(args)
+        return
     import torch
     import kv_cache_quantization_head_amd as qkv
     import synth
