@@ -155,3 +155,16 @@ def test_cross_layer_attend_unsupported_and_order():
 def test_status_strings():
     for s in (0, -1, -2, -3, -4, -5, -6, 99):
         assert isinstance(qkv.status_string(s), str)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asking for more exits with status 2 and a message."""
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    p = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert p.returncode == 2
+    msg = json.loads(p.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
