@@ -9,7 +9,7 @@
 //                 channels summed in order
 //   k_assign      the same decision with fp32 VALU screening (fp32 caches,
 //                 C > 512)
-//   k_tile_sort(_small), k_update_sorted
+//   k_tile_sort(_count), k_update_sorted
 //                 k-means update: stable per-tile sort of the ids, then fp64
 //                 member sums in token order -> mean -> one rounding
 //   k_update      the same update through in-LDS member lists (C > 4096)
@@ -743,12 +743,15 @@ __global__ __launch_bounds__(256) void k_tile_sort(EncodeArgs a) {
   }
 }
 
-// The same outputs as k_tile_sort for C <= 256, by a stable counting sort:
-// a token's rank among the equal ids of its wave comes from nine ballots (the
-// id's bits and a past-the-end flag); per-wave counts and a scan over the
-// ids give each cluster's start and each wave's offset inside it.
-__global__ __launch_bounds__(256) void k_tile_sort_small(EncodeArgs a) {
-  __shared__ uint32_t cnt[4][256];
+// The same outputs as k_tile_sort for C <= CMAX (256 or 1024), by a stable
+// counting sort: a token's rank among the equal ids of its wave comes from
+// ballots over the id's bits and a past-the-end flag; per-wave counts and a
+// scan over the ids give each cluster's start and each wave's offset in it.
+template <int CMAX>
+__global__ __launch_bounds__(256) void k_tile_sort_count(EncodeArgs a) {
+  constexpr int NB = CMAX == 256 ? 9 : 11;     // id bits + the past-the-end flag (id == CMAX)
+  constexpr int PER = CMAX / 256;              // clusters per thread in the scan
+  __shared__ uint32_t cnt[4][CMAX];
   __shared__ uint32_t wsum[4];
   const DevLayout &L = a.L;
   const int tile = blockIdx.x, h = blockIdx.y, z = blockIdx.z;
@@ -757,12 +760,14 @@ __global__ __launch_bounds__(256) void k_tile_sort_small(EncodeArgs a) {
   const int i = threadIdx.x, wave = i >> 6, lane = i & 63;
   const int t = tile * 256 + i;
   const bool valid = t < a.n;
-  const int id = valid ? load_id(ids, L.id_bytes, t) : 256;
+  const int id = valid ? load_id(ids, L.id_bytes, t) : CMAX;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) cnt[w][i] = 0;
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int p = 0; p < PER; ++p) cnt[w][p * 256 + i] = 0;
   uint64_t eq = ~uint64_t(0);                 // lanes of the wave with this lane's id
 #pragma unroll
-  for (int b = 0; b < 9; ++b) {
+  for (int b = 0; b < NB; ++b) {
     const uint64_t m = __ballot((id >> b) & 1);
     eq &= ((id >> b) & 1) ? m : ~m;
   }
@@ -770,10 +775,20 @@ __global__ __launch_bounds__(256) void k_tile_sort_small(EncodeArgs a) {
   __syncthreads();
   if (valid && rank == 0) cnt[wave][id] = uint32_t(__popcll(eq));
   __syncthreads();
-  // thread i now stands for cluster i
-  const uint32_t c0 = cnt[0][i], c1 = cnt[1][i], c2 = cnt[2][i], c3 = cnt[3][i];
-  const uint32_t tot = c0 + c1 + c2 + c3;
-  uint32_t incl = tot;
+  // thread i now stands for clusters PER*i .. PER*i + PER-1
+  uint32_t c[PER][4], tot[PER], sum = 0;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int kk = PER * i + p;
+    tot[p] = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      c[p][w] = cnt[w][kk];
+      tot[p] += c[p][w];
+    }
+    sum += tot[p];
+  }
+  uint32_t incl = sum;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const uint32_t v = __shfl_up(incl, d);
@@ -781,20 +796,27 @@ __global__ __launch_bounds__(256) void k_tile_sort_small(EncodeArgs a) {
   }
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  uint32_t start = incl - tot;
+  uint32_t start = incl - sum;
   for (int w = 0; w < wave; ++w) start += wsum[w];
-  cnt[0][i] = start;
-  cnt[1][i] = start + c0;
-  cnt[2][i] = start + c0 + c1;
-  cnt[3][i] = start + c0 + c1 + c2;
-  __syncthreads();
   const uint64_t unit = (uint64_t(z) * L.H + h) * uint64_t(a.sort_tiles) + tile;
+  uint16_t *off = a.sort_off + unit * uint64_t(L.C + 1);
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int kk = PER * i + p;
+    uint32_t o = start;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      cnt[w][kk] = o;
+      o += c[p][w];
+    }
+    if (kk <= L.C) off[kk] = uint16_t(start);
+    start += tot[p];
+  }
+  if (i == 0 && L.C == CMAX) off[CMAX] = uint16_t(min(256, a.n - tile * 256));
+  __syncthreads();
   // past-the-end tokens keep their place after the valid ones
   const int pos = valid ? int(cnt[wave][id]) + rank : i;
   a.sort_perm[unit * 256 + pos] = uint8_t(i);
-  uint16_t *off = a.sort_off + unit * uint64_t(L.C + 1);
-  if (i <= L.C) off[i] = uint16_t(start);
-  if (i == 0 && L.C == 256) off[256] = uint16_t(min(256, a.n - tile * 256));
 }
 
 // k-means update from the tile sort: one wave per cluster (blockIdx.x = group
@@ -1750,10 +1772,13 @@ static void launch_assign_t(const EncodeArgs &a, int streams, hipStream_t st) {
 template <int D, bool BF>
 static void launch_update_t(const EncodeArgs &a, int streams, hipStream_t st) {
   if (a.L.C <= kSortMaxClusters) {
+    const dim3 grid(cdiv(a.n, 256), a.L.H, streams);
     if (a.L.C <= 256)
-      hipLaunchKernelGGL(k_tile_sort_small, dim3(cdiv(a.n, 256), a.L.H, streams), dim3(256), 0, st, a);
+      hipLaunchKernelGGL(k_tile_sort_count<256>, grid, dim3(256), 0, st, a);
+    else if (a.L.C <= 1024)
+      hipLaunchKernelGGL(k_tile_sort_count<1024>, grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL(k_tile_sort, dim3(cdiv(a.n, 256), a.L.H, streams), dim3(256), 0, st, a);
+      hipLaunchKernelGGL(k_tile_sort, grid, dim3(256), 0, st, a);
     hipLaunchKernelGGL((k_update_sorted<D, BF>), dim3(cdiv(a.L.C, 4), a.L.H, streams), dim3(256), 0, st, a);
     return;
   }
