@@ -312,10 +312,14 @@ __global__ __launch_bounds__(256) void k_assign(EncodeArgs a) {
 // of D (acc <= 0 up to rounding), ties to the lowest index, and the three
 // smallest keys are kept with one v_min and two v_med3 per key.  The screening
 // error (MFMA accumulation over D+1 terms, rounding of the start value, the
-// 9 dropped bits) is below E; a token whose two best keys are within 2E goes
-// to the exact fp64 decision shared with k_assign.
+// 9 dropped bits) is below E; a token whose two best keys are within 2E (the
+// third clear) joins the block's pair list, decided exactly in fp64 (two lanes
+// per token) when the block moves to another head or ends; one whose best
+// three are within 2E is rescored exactly against every centroid at once.
+constexpr int kPairCap = 512;               // pair list entries per block
+constexpr uint32_t kNoToken = 0xffffffffu;  // empty pair list slot
 template <int D>
-__global__ __launch_bounds__(512) void k_assign_mfma(EncodeArgs a, int tiles_per_block, int streams) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_assign_mfma(EncodeArgs a, int tiles_per_block, int streams) {
   constexpr int KP = D + 8;                 // LDS row pitch (bf16 elements)
   constexpr int STEPS = D / 32;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -324,6 +328,9 @@ __global__ __launch_bounds__(512) void k_assign_mfma(EncodeArgs a, int tiles_per
   uint16_t *cbs = (uint16_t *)smem;                          // [C16][KP]
   float *cnh = (float *)(smem + size_t(C16) * KP * 2);       // [C16]
   __shared__ uint32_t cmax_bits;
+  // the block's list of pair tokens (within-call token index, two candidates)
+  __shared__ uint32_t pq_tok[kPairCap], pq_cand[kPairCap];
+  __shared__ int pq_n;
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g4 = lane >> 4, c16 = lane & 15;
@@ -333,12 +340,66 @@ __global__ __launch_bounds__(512) void k_assign_mfma(EncodeArgs a, int tiles_per
   const uint16_t *x = nullptr;
   uint8_t *ids = nullptr;
   float cmax = 0.0f;
+  // Exact decision for n pair tokens held in registers, entry j at lane j:
+  // token (etok, kNoToken for a skipped entry) and its two best candidates
+  // (ecand, low and high 16 bits).  Entry j is scored by lanes 2j (first
+  // candidate) and 2j+1 (second), the token row read in one go; the winner is
+  // written to ids.
+  auto decide_pairs = [&](uint32_t etok, uint32_t ecand, int n) {
+    const int j = lane >> 1;
+    const uint32_t tok = __shfl(etok, j), cc = __shfl(ecand, j);
+    const int cand = int((lane & 1) ? (cc >> 16) : (cc & 0xffffu));
+    const bool live = j < n && tok != kNoToken;
+    double dd = INFINITY;
+    if (live) {
+      const uint16_t *xrow = x + uint64_t(tok) * D;
+      const uint16_t *crow = cbs + cand * KP;
+      dd = 0.0;
+      uint4 xr[D / 8];
+#pragma unroll
+      for (int j8 = 0; j8 < D / 8; ++j8) xr[j8] = *(const uint4 *)(xrow + j8 * 8);
+#pragma unroll
+      for (int j8 = 0; j8 < D / 8; ++j8) {
+        const uint4 xv = xr[j8];
+        const uint4 cv = *(const uint4 *)(crow + j8 * 8);
+        const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, cw[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t xb = (xw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          const uint32_t cbb = (cw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+          const double diff = double(bf16_to_f32(xb)) - double(bf16_to_f32(cbb));
+          dd = dd + diff * diff;
+        }
+      }
+    }
+    const double od = __shfl_xor(dd, 1);
+    const int oc = __shfl_xor(cand, 1);
+    const int win = (dd < od || (dd == od && cand < oc)) ? cand : oc;
+    if (live && !(lane & 1)) {
+      const int64_t tt = int64_t(a.t0) + tok;
+      if (L.id_bytes == 1) ids[tt] = uint8_t(win);
+      else ((uint16_t *)ids)[tt] = uint16_t(win);
+    }
+  };
+  // Block-wide drain of the pair list (every thread calls it): wave w takes
+  // entries 32w, 32w + 256, ...; the list is empty afterwards.
+  auto drain_pairs = [&]() {
+    __syncthreads();
+    const int n = min(pq_n, kPairCap);
+    for (int e0 = wave * 32; e0 < n; e0 += 8 * 32) {
+      const int e = e0 + (lane & 31);
+      const uint32_t etok = e < n ? pq_tok[e] : kNoToken, ecand = e < n ? pq_cand[e] : 0u;
+      decide_pairs(etok, ecand, min(32, n - e0));
+    }
+  };
   for (int64_t f = int64_t(blockIdx.x) * tiles_per_block;
        f < min(total, int64_t(blockIdx.x + 1) * tiles_per_block); ++f) {
     const int tile = int(f % n_tiles);
     const int zh = int(f / n_tiles);
     if (zh != cur) {
-      // stage the codebook of (stream, head) zh
+      // decide the listed pairs of the previous (stream, head), then stage
+      // the codebook of (stream, head) zh
+      if (cur >= 0) drain_pairs();
       cur = zh;
       const int h = zh % L.H, z = zh / L.H, lrel = z >> 1, kv = z & 1;
       uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, kv);
@@ -346,8 +407,11 @@ __global__ __launch_bounds__(512) void k_assign_mfma(EncodeArgs a, int tiles_per
       const uint16_t *cb = (const uint16_t *)(st + L.cb_off + uint64_t(a.slot) * L.cb_chunk + uint64_t(h) * L.cb_head);
       const float *cn = (const float *)(st + L.cn_off + uint64_t(a.slot) * L.cn_chunk + uint64_t(h) * L.cn_head);
       ids = st + L.ids_off + uint64_t(h) * L.ids_head;
-      __syncthreads();  // previous codebook no longer read
-      if (threadIdx.x == 0) cmax_bits = 0;
+      __syncthreads();  // previous codebook and pair list no longer read
+      if (threadIdx.x == 0) {
+        cmax_bits = 0;
+        pq_n = 0;
+      }
       __syncthreads();
       for (int i = threadIdx.x; i < C16 * (D / 8); i += blockDim.x) {
         const int k = i / (D / 8), c8 = i % (D / 8);
@@ -456,62 +520,47 @@ __global__ __launch_bounds__(512) void k_assign_mfma(EncodeArgs a, int tiles_per
       full[nt] = valid && !(d2 - d1 > 2.0f * E) && !(d3 - d1 > 2.0f * E);
       kbest[nt] = k1v[nt];
     }
-    // Exact decisions between the two best, for the pair tokens of both
-    // column blocks in one pass: the j-th pair token (column block 0 first,
-    // then 1; each in lane order) is scored by lanes 2j (its best) and 2j+1
-    // (its second best).
+    // Pair tokens join the block's list (column block 0 first, then 1; each
+    // in lane order): the j-th new one of the wave goes to slot base + j.  A
+    // wave whose tokens do not all fit marks its slots below the capacity
+    // empty and sends its pair tokens to the full rescoring.
     const uint64_t pm0 = __ballot(pair[0]), pm1 = __ballot(pair[1]);
     if (pm0 | pm1) {
       const int np0 = __popcll(pm0), np = np0 + __popcll(pm1);
-      const int j = lane >> 1;
-      const bool worker = j < np;
-      const int jn = j < np0 ? 0 : 1;                         // column block of token j
-      // lane of token j: the (j - np0*jn)-th set bit of its block's mask
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&pq_n, np);
+      base = __shfl(base, 0);
+      const int j = lane;
+      const bool take = j < np;
+      const int jn = j < np0 ? 0 : 1;                         // column block of new token j
+      // lane of new token j: the (j - np0*jn)-th set bit of its block's mask
       uint64_t m = jn ? pm1 : pm0;
-      int rank = worker ? j - np0 * jn : 0, src = 0;
+      int rank = take ? j - np0 * jn : 0, src = 0;
 #pragma unroll
       for (int w = 32; w >= 1; w >>= 1) {
         const int c = __popcll((m >> src) & ((uint64_t(1) << w) - 1));
         if (rank >= c) { rank -= c; src += w; }
       }
-      // both shuffles of each block run on every lane (a shuffle under a
-      // divergent select would read the select taken by the source lane)
+      // all four shuffles run on every lane (a shuffle under a divergent
+      // select would read the select taken by the source lane)
       const int a1 = __shfl(k1v[0], src), a2 = __shfl(k2v[0], src);
       const int b1 = __shfl(k1v[1], src), b2 = __shfl(k2v[1], src);
-      const int cand = (lane & 1) ? (jn ? b2 : a2) : (jn ? b1 : a1);
-      double dd = INFINITY;
-      if (worker) {
-        const uint16_t *xrow = x + uint64_t(tb + jn * 16 + src) * D;
-        const uint16_t *crow = cbs + cand * KP;
-        dd = 0.0;
-        // the token row is read in one go (one memory latency, not D/8)
-        uint4 xr[D / 8];
+      const uint32_t etok = uint32_t(tb + jn * 16 + src);
+      const uint32_t ecand = jn ? (uint32_t(b1) | (uint32_t(b2) << 16)) : (uint32_t(a1) | (uint32_t(a2) << 16));
+      if (base + np <= kPairCap) {
+        if (take) {
+          pq_tok[base + j] = etok;
+          pq_cand[base + j] = ecand;
+        }
+      } else {
+        // rescored against every centroid below
+        if (take && base + j < kPairCap) pq_tok[base + j] = kNoToken;
 #pragma unroll
-        for (int j8 = 0; j8 < D / 8; ++j8) xr[j8] = *(const uint4 *)(xrow + j8 * 8);
-#pragma unroll
-        for (int j8 = 0; j8 < D / 8; ++j8) {
-          const uint4 xv = xr[j8];
-          const uint4 cv = *(const uint4 *)(crow + j8 * 8);
-          const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, cw[4] = {cv.x, cv.y, cv.z, cv.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t xb = (xw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-            const uint32_t cbb = (cw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-            const double diff = double(bf16_to_f32(xb)) - double(bf16_to_f32(cbb));
-            dd = dd + diff * diff;
-          }
+        for (int nt = 0; nt < 2; ++nt) {
+          full[nt] = full[nt] || pair[nt];
+          pair[nt] = false;
         }
       }
-      const double od = __shfl_xor(dd, 1);
-      const int oc = __shfl_xor(cand, 1);
-      const int win = (dd < od || (dd == od && cand < oc)) ? cand : oc;
-      // back to the owners: token of block nt at position p of its mask
-      const int p0 = __popcll(pm0 & ((uint64_t(1) << lane) - 1));
-      const int p1 = np0 + __popcll(pm1 & ((uint64_t(1) << lane) - 1));
-      const int got0 = __shfl(win, 2 * (pair[0] ? p0 : 0));
-      const int got1 = __shfl(win, 2 * (pair[1] ? p1 : 0));
-      if (pair[0]) kbest[0] = got0;
-      if (pair[1]) kbest[1] = got1;
     }
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -550,13 +599,14 @@ __global__ __launch_bounds__(512) void k_assign_mfma(EncodeArgs a, int tiles_per
         }
         if (lane == src) kbest[nt] = bk;
       }
-      if (valid) {
+      if (valid && !pair[nt]) {
         const int64_t tt = int64_t(a.t0) + t;
         if (L.id_bytes == 1) ids[tt] = uint8_t(kbest[nt]);
         else ((uint16_t *)ids)[tt] = uint16_t(kbest[nt]);
       }
     }
   }
+  if (cur >= 0) drain_pairs();
 }
 
 // One wave per 4 clusters; blockIdx.x = group of 16 clusters, y = head, z = stream.

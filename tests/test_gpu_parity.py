@@ -171,3 +171,53 @@ def test_encode_is_deterministic():
         torch.cuda.synchronize()
         arenas.append(codec.arena.cpu())
     assert torch.equal(arenas[0], arenas[1])
+
+
+def _near_tie_tokens(H, T, d, seed):
+    """bf16-exact tokens built so that most are near-ties for the nearest
+    centroid.  With no k-means iteration the codebook is the strided initial
+    one, rows floor(k T / 8) = +v, -v, +w, -w, 4v, -4v, 4w, -4w (v all ones,
+    w alternating +-1).  Other tokens: 80 % gamma (v + w) + delta (+v and +w
+    within a few 2^-8 of each other, the rest far: two-way near-ties), 10 %
+    delta alone (four-way near-ties; delta = 0 gives exact ties), 10 % random
+    normal rounded to bf16 (decided by the screen).  delta puts +-2^-8 on
+    eight random channels."""
+    rng = np.random.default_rng(seed)
+    v = np.ones(d, np.float32)
+    w = np.where(np.arange(d) % 2 == 0, 1.0, -1.0).astype(np.float32)
+    cents = np.stack([v, -v, w, -w, 4 * v, -4 * v, 4 * w, -4 * w])
+    x = np.zeros((H, T, d), np.float32)
+    for h in range(H):
+        kind = rng.random(T)
+        delta = np.zeros((T, d), np.float32)
+        ch = rng.integers(0, d, size=(T, 8))
+        sg = rng.choice(np.array([-1.0, 0.0, 1.0], np.float32), size=(T, 8)) * 2.0 ** -8
+        np.put_along_axis(delta, ch, sg, axis=1)
+        pair = 2.0 ** -5 * (v + w)[None, :] + delta
+        far = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).bfloat16().float().numpy()
+        x[h] = np.where((kind < 0.8)[:, None], pair, np.where((kind < 0.9)[:, None], delta, far))
+        x[h, (np.arange(8) * T) // 8] = cents
+    xb = torch.from_numpy(x).bfloat16()
+    assert torch.equal(xb.float(), torch.from_numpy(x))          # every value is bf16-exact
+    return xb
+
+
+def test_near_ties_pair_list_and_full_rescoring():
+    """Near-tie tokens in bulk: most tokens need the exact fp64 decision
+    between their two best centroids, some between four, some are exact ties
+    (lowest index wins).  96 227 tokens per head make each block of the
+    screening kernel take three 256-token tiles, so its pair list (512
+    entries) overflows and the overflow goes to the full rescoring."""
+    H, d, T, C = 2, 128, 3 * 32768 - 77, 8
+    k = _near_tie_tokens(H, T, d, 11)
+    v = _near_tie_tokens(H, T, d, 12)
+    codec = make_codec(H, d, C, 2, 2, 32, iters=0, max_tokens=T, max_chunks=1, max_q=0)
+    _say(f"near ties: {H} heads x {T} tokens, C={C}, no iterations")
+    codec.encode_chunk(k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    for kv, x in ((0, k), (1, v)):
+        o = oracle_stream(H, d, C, 0, 2, 2, 32, "bf16")
+        o.encode(x.float().numpy())
+        ids = o.chunks[0][0].ids
+        assert np.count_nonzero(ids == 0) > T // 20 and np.count_nonzero(ids == 2) > T // 20
+        assert_stream_equal(codec, 0, kv, o)
