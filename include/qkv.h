@@ -85,7 +85,8 @@ typedef struct {
   int32_t group_size;      /* G in {32, 64}, G divides d */
   int32_t kmeans_iters;    /* Lloyd iterations per call, in [0, 64] */
   int64_t max_tokens;      /* capacity of each (layer, K|V) stream, < 2^31 */
-  int64_t max_chunk_tokens;/* largest n of one encode call (0 = max_tokens) */
+  int64_t max_chunk_tokens;/* largest n of one encode call (0 = max_tokens);
+                              n * d * element bytes < 2^31 */
   int32_t max_chunks;      /* codebook snapshots per stream, in [1, 256] */
   int32_t kv_dtype;        /* QKV_F32 or QKV_BF16: the cache (and codebook) type */
   int64_t max_query_tokens;/* largest n_q of qkv_attend (0 = attention unused) */

@@ -646,6 +646,13 @@ __device__ __forceinline__ void finalize_centroid(uint8_t *cb, float *cn, int k,
 // summing the listed rows in list order with UPD_UNROLL (bf16 rows of 128
 // channels: UPD_UNROLL_BF, kept packed) row loads in flight, so every
 // centroid sum is the sequential fp64 sum in token order.
+// Raw (unformatted, stride 0) buffer resource over `bytes` bytes at p; the
+// fourth word is the gfx9 data-format field for 32-bit raw access.  Loads past
+// the end return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, int(bytes), 0x00020000);
+}
+
 constexpr int UPD_SEG = 16384;      // ids staged per pass
 constexpr int UPD_CAP = 512;        // list entries per cluster
 constexpr int UPD_UNROLL = 32;
@@ -653,16 +660,21 @@ constexpr int UPD_UNROLL_BF = 64;    // bf16 rows kept packed (one register per 
 
 template <int D, bool BF16>
 __device__ __forceinline__ void drain_list(const uint8_t *x, const int32_t *list, int count, double *acc,
-                                           int lane) {
+                                           int lane, __amdgpu_buffer_rsrc_t xr) {
   constexpr int EB = BF16 ? 2 : 4;
   constexpr int CPL = D / 64;
   if constexpr (BF16 && CPL == 2) {
+    static_assert(UPD_UNROLL_BF == 64, "one list entry per lane");
     for (int i = 0; i < count; i += UPD_UNROLL_BF) {
+      // lane e holds the e-th row index of the batch (tail: the last row,
+      // reloaded but not added); each row address is formed in scalar
+      // registers from the wave-uniform index
+      const int mine = list[min(i + lane, count - 1)];
       uint32_t v[UPD_UNROLL_BF];
 #pragma unroll
       for (int e = 0; e < UPD_UNROLL_BF; ++e) {
-        const int row = list[min(i + e, count - 1)];   // tail: reload the last row, not added
-        v[e] = *((const uint32_t *)(x + uint64_t(row) * D * EB) + lane);
+        const int row = __builtin_amdgcn_readlane(mine, e);
+        v[e] = __builtin_amdgcn_raw_buffer_load_b32(xr, 4 * lane, row * (D * EB), 0);
       }
 #pragma unroll
       for (int e = 0; e < UPD_UNROLL_BF; ++e) {
@@ -705,6 +717,7 @@ __global__ __launch_bounds__(1024) void k_update(EncodeArgs a) {
   const int k = blockIdx.x * 16 + wave;
   uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, kv);
   const uint8_t *x = (kv ? a.v_in : a.k_in) + (uint64_t(lrel) * L.H + h) * uint64_t(a.n) * D * EB;
+  const __amdgpu_buffer_rsrc_t xr = raw_rsrc(x, uint32_t(a.n) * D * EB);
   const uint8_t *ids = st + L.ids_off + uint64_t(h) * L.ids_head + uint64_t(a.t0) * L.id_bytes;
   uint8_t *cb = st + L.cb_off + uint64_t(a.slot) * L.cb_chunk + uint64_t(h) * L.cb_head;
   float *cn = (float *)(st + L.cn_off + uint64_t(a.slot) * L.cn_chunk + uint64_t(h) * L.cn_head);
@@ -740,7 +753,7 @@ __global__ __launch_bounds__(1024) void k_update(EncodeArgs a) {
         if (m == 0) continue;
         const int nm = __popcll(m);
         if (fill + nm > UPD_CAP) {
-          drain_list<D, BF16>(x, list, fill, acc, lane);
+          drain_list<D, BF16>(x, list, fill, acc, lane, xr);
           fill = 0;
         }
         if ((m >> lane) & 1) list[fill + __popcll(m & below)] = seg0 + t;
@@ -750,7 +763,7 @@ __global__ __launch_bounds__(1024) void k_update(EncodeArgs a) {
     }
   }
   if (k >= L.C) return;
-  if (fill) drain_list<D, BF16>(x, list, fill, acc, lane);
+  if (fill) drain_list<D, BF16>(x, list, fill, acc, lane, xr);
   finalize_centroid<D, BF16>(cb, cn, k, L.C, cnt, acc, lane);
 }
 
@@ -887,6 +900,7 @@ __global__ __launch_bounds__(256) void k_update_sorted(EncodeArgs a) {
   if (k >= L.C) return;  // whole wave; no block barrier below
   uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, kv);
   const uint8_t *x = (kv ? a.v_in : a.k_in) + (uint64_t(lrel) * L.H + h) * uint64_t(a.n) * D * EB;
+  const __amdgpu_buffer_rsrc_t xr = raw_rsrc(x, uint32_t(a.n) * D * EB);
   uint8_t *cb = st + L.cb_off + uint64_t(a.slot) * L.cb_chunk + uint64_t(h) * L.cb_head;
   float *cn = (float *)(st + L.cn_off + uint64_t(a.slot) * L.cn_chunk + uint64_t(h) * L.cn_head);
   const uint64_t unit0 = (uint64_t(z) * L.H + h) * uint64_t(a.sort_tiles);
@@ -918,7 +932,7 @@ __global__ __launch_bounds__(256) void k_update_sorted(EncodeArgs a) {
     int done = 0;
     while (done < total) {
       if (fill == UPD_CAP) {
-        drain_list<D, BF16>(x, list, fill, acc, lane);
+        drain_list<D, BF16>(x, list, fill, acc, lane, xr);
         fill = 0;
       }
       const int take = min(UPD_CAP - fill, total - done);
@@ -930,7 +944,7 @@ __global__ __launch_bounds__(256) void k_update_sorted(EncodeArgs a) {
       cnt += take;
     }
   }
-  if (fill) drain_list<D, BF16>(x, list, fill, acc, lane);
+  if (fill) drain_list<D, BF16>(x, list, fill, acc, lane, xr);
   finalize_centroid<D, BF16>(cb, cn, k, L.C, cnt, acc, lane);
 }
 

@@ -40,6 +40,9 @@ int make_plan(const qkv_config *cfg, Plan *plan) {
   const uint64_t H = c.n_heads, d = c.head_dim, T = c.max_tokens, S = c.n_stages;
   const uint64_t C = c.n_clusters, G = c.group_size, K = c.max_chunks;
   p.kv_elem_bytes = c.kv_dtype == QKV_BF16 ? 2 : 4;
+  // one head's slice of one call's input is addressed with 32-bit offsets
+  if (uint64_t(p.cfg.max_chunk_tokens) * uint64_t(c.head_dim) * p.kv_elem_bytes >= (uint64_t(1) << 31))
+    return QKV_E_INVAL;
 
   StreamLayout &s = p.s;
   uint64_t off = 0;

@@ -168,3 +168,13 @@ def test_bench_refuses_more_than_one_gpu():
     assert p.returncode == 2
     msg = json.loads(p.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"]
+
+
+def test_per_call_input_slice_must_stay_under_2gib():
+    """One head's slice of one encode call (n * d * element bytes) is
+    addressed with 32-bit offsets: 2^23 bf16 tokens of d = 128 are refused
+    unless the calls are capped below that."""
+    big = 1 << 23
+    assert qkv.workspace_bytes(_cfg(max_tokens=big, max_chunk_tokens=0, max_query_tokens=0)) == 0
+    assert qkv.workspace_bytes(_cfg(max_tokens=big, max_chunk_tokens=big - 1, max_query_tokens=0)) > 0
+    assert qkv.workspace_bytes(_cfg(max_tokens=big, max_chunk_tokens=4096, max_query_tokens=0)) > 0
