@@ -937,8 +937,16 @@ __global__ __launch_bounds__(256) void k_update_sorted(EncodeArgs a) {
       }
       const int take = min(UPD_CAP - fill, total - done);
       const int e0 = max(0, done - excl), e1 = min(num, done + take - excl);
-      for (int e = e0; e < e1; ++e)
-        list[fill + excl + e - done] = tile * 256 + int(perm[uint64_t(tile) * 256 + beg + e]);
+      // four member offsets read per round trip
+      const uint8_t *pt = perm + uint64_t(tile) * 256 + beg;
+      for (int e = e0; e < e1; e += 4) {
+        int pv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) pv[u] = e + u < e1 ? int(pt[e + u]) : 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (e + u < e1) list[fill + excl + e + u - done] = tile * 256 + pv[u];
+      }
       fill += take;
       done += take;
       cnt += take;
