@@ -35,6 +35,11 @@ def parse():
                     help="instead of the default step: time the cross-layer encode of one "
                          "wide-head layer (K and V [40, 62400, 128] bf16, rank 32, C = 512, "
                          "2-stage INT2, G = 64), predicted from the previous layer")
+    ap.add_argument("--fresh", action="store_true",
+                    help="instead of the default step: time a generated chunk on 4 wan_layer-shaped "
+                         "layers (attention over the packed cache plus the chunk's fresh bf16 K/V for "
+                         "every denoising step and layer, then the chunk's encode)")
+    ap.add_argument("--denoise", type=int, default=4, help="denoising steps per chunk (--fresh)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (a known-size "
                          "reference for HBM byte counters)")
@@ -155,6 +160,71 @@ def xlayer_main(args):
         "sas_layer_ms": round(sas, 4)}), flush=True)
 
 
+def fresh_main(args):
+    """The read as a generating model issues it, on the wan_layer shape with
+    4 layers: for each new 4680-token chunk, --denoise denoising steps each
+    attend every layer's 4680 queries over its packed 32760-token cache plus
+    the chunk's fresh bf16 K/V (qkv_attend_with_chunk), then the chunk is
+    encoded into every layer's cache.  A step is one chunk; the cache is
+    rewound to 32760 tokens before each step so every step sees the same
+    sizes."""
+    import torch
+    import kv_cache_quantization_head_amd as qkv
+    import synth
+
+    dev = torch.device("cuda:0")
+    L = 4
+    cfgs = synth.scaled(synth.WAN_LAYER, n_layers=L)
+    H, T, d, Tq, n_new = cfgs.n_heads, cfgs.tokens, cfgs.head_dim, cfgs.q_tokens, cfgs.q_tokens
+    cfg = qkv.config(L, H, d, cfgs.n_clusters, cfgs.n_stages, cfgs.bits, cfgs.group, kmeans_iters=cfgs.iters,
+                     max_tokens=T + n_new, max_chunk_tokens=T, max_chunks=2, kv_dtype=qkv.QKV_BF16,
+                     max_query_tokens=Tq)
+    codec = qkv.Codec(cfg, device=dev)
+    ks = torch.stack([synth.kv_tokens(cfgs, l, 0, 0, T + n_new, device=dev) for l in range(L)])
+    vs = torch.stack([synth.kv_tokens(cfgs, l, 1, 0, T + n_new, device=dev) for l in range(L)])
+    codec.encode_chunk(ks[:, :, :T].contiguous(), vs[:, :, :T].contiguous())
+    kn, vn = ks[:, :, T:].contiguous(), vs[:, :, T:].contiguous()
+    qs = [synth.queries(cfgs, l, Tq, device=dev) for l in range(L)]
+    out = torch.empty((H, Tq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((H, Tq), dtype=torch.float32, device=dev)
+    ev = []
+
+    def step(record):
+        codec.rewind(0, L, T)
+        m = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        m[0].record()
+        for _ in range(args.denoise):
+            for l in range(L):
+                codec.attend_with_chunk(l, qs[l], kn[l], vn[l], out=out, lse=lse)
+        m[1].record()
+        codec.encode_chunk(kn, vn)
+        m[2].record()
+        if record:
+            ev.append(m)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    att = sum(m[0].elapsed_time(m[1]) for m in ev) / len(ev)
+    enc = sum(m[1].elapsed_time(m[2]) for m in ev) / len(ev)
+    per_call = att / (args.denoise * L)
+    flops = 4.0 * d * H * Tq * (T + n_new)
+    print(json.dumps({
+        "metric": "generated chunk: attention over packed cache + fresh chunk for every denoising step and "
+                  "layer, then the chunk's encode", "value": round(att + enc, 4), "unit": "ms per chunk",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False, "dtype": "bf16",
+        "data": "synthetic (seeded prototype/drift/outlier generator)",
+        "config": {"workload": f"wan_layer x {L} layers: packed cache 32760 + fresh 4680 tokens, 4680 bf16 "
+                               f"queries, {args.denoise} denoising steps",
+                   "layers": L, "heads": H, "cache_tokens": T, "fresh_tokens": n_new, "q_tokens": Tq,
+                   "denoise_steps": args.denoise},
+        "attend_with_chunk_ms": round(per_call, 4), "attend_with_chunk_TFLOPs": round(flops / per_call / 1e9, 1),
+        "encode_chunk_ms": round(enc, 4)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -163,6 +233,9 @@ def main():
         sys.exit(2)
     if args.xlayer:
         xlayer_main(args)
+        return
+    if args.fresh:
+        fresh_main(args)
         return
     import torch
     import kv_cache_quantization_head_amd as qkv

@@ -152,6 +152,22 @@ int qkv_encode_chunk(qkv_ctx *ctx, int32_t layer0, int32_t n_layers,
 int qkv_attend(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t n_q, int32_t q_dtype,
                void *d_out, int32_t out_dtype, float *d_lse, void *stream);
 
+/* The read as a generating model issues it: attention of n_q queries over
+ * every token encoded in `layer` followed by n_new fresh tokens of the chunk
+ * being generated, which are not in the cache yet (QVG explainer, "Sommario
+ * tecnico" 2.B and 3: the cached tokens are dequantized inside the attention
+ * kernels; the 33-method study, abstract: no bf16 copy of the cache is made).
+ * d_k_new, d_v_new: device [H][n_new][d] bf16, read as they are.  The result
+ * is softmax over the concatenated keys (cache first, then the fresh keys):
+ * the two parts are computed separately and combined by their log-sum-exps.
+ * n_new = 0 is qkv_attend; an empty cache with n_new > 0 attends to the
+ * fresh tokens alone.  Other arguments as qkv_attend.  Errors: QKV_E_INVAL,
+ * QKV_E_CAPACITY (n_q > max_query_tokens), QKV_E_STATE (empty cache and
+ * n_new = 0), QKV_E_UNSUPPORTED (cross-layer coded layer >= 1). */
+int qkv_attend_with_chunk(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t n_q, int32_t q_dtype,
+                          const void *d_k_new, const void *d_v_new, int64_t n_new, void *d_out,
+                          int32_t out_dtype, float *d_lse, void *stream);
+
 /* Rebuild tokens [t0, t1) of tensor kv (0 = K, 1 = V) for layers
  * [layer0, layer0+n_layers) into d_out: device [n_layers][H][t1-t0][d] in
  * out_dtype (QKV_F32 is the exact reconstruction; QKV_BF16 its nearest-even

@@ -66,6 +66,8 @@ def lib():
     L.qkv_encode_chunk.restype = ctypes.c_int
     L.qkv_attend.argtypes = [vp, i32, vp, i64, i32, vp, i32, vp, vp]
     L.qkv_attend.restype = ctypes.c_int
+    L.qkv_attend_with_chunk.argtypes = [vp, i32, vp, i64, i32, vp, vp, i64, vp, i32, vp, vp]
+    L.qkv_attend_with_chunk.restype = ctypes.c_int
     L.qkv_reconstruct.argtypes = [vp, i32, i32, i32, i64, i64, vp, i32, vp]
     L.qkv_reconstruct.restype = ctypes.c_int
     L.qkv_rewind.argtypes = [vp, i32, i32, i64, vp]
@@ -175,6 +177,33 @@ class Codec:
         _check(lib().qkv_attend(self.ctx, layer, ctypes.c_void_p(q.data_ptr()), n_q,
                                 _dtype_code(q.dtype), ctypes.c_void_p(out.data_ptr()),
                                 _dtype_code(out.dtype), lse_ptr, _stream()), self.ctx)
+        return out, lse
+
+    def attend_with_chunk(self, layer, q, k_new, v_new, out_dtype=torch.float32, with_lse=True, out=None,
+                          lse=None):
+        """Attention over the packed cache of `layer` followed by the fresh
+        chunk k_new, v_new ([H, n_new, d] bf16 device tensors).  Returns
+        (out, lse)."""
+        H, n_q, d = q.shape
+        if H != self.cfg.n_heads or d != self.cfg.head_dim:
+            raise ValueError("q shape does not match the configuration")
+        if k_new.shape != v_new.shape or k_new.dim() != 3 or k_new.shape[0] != H or k_new.shape[2] != d:
+            raise ValueError("fresh K/V shape does not match the configuration")
+        if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+            raise ValueError("fresh K/V must be bf16")
+        q, k_new, v_new = q.contiguous(), k_new.contiguous(), v_new.contiguous()
+        n_new = k_new.shape[1]
+        if out is None:
+            out = torch.empty((H, n_q, d), dtype=out_dtype, device=q.device)
+        if with_lse and lse is None:
+            lse = torch.empty((H, n_q), dtype=torch.float32, device=q.device)
+        lse_ptr = ctypes.c_void_p(lse.data_ptr()) if with_lse else None
+        kp = ctypes.c_void_p(k_new.data_ptr()) if n_new else None
+        vp = ctypes.c_void_p(v_new.data_ptr()) if n_new else None
+        _check(lib().qkv_attend_with_chunk(self.ctx, layer, ctypes.c_void_p(q.data_ptr()), n_q,
+                                           _dtype_code(q.dtype), kp, vp, n_new,
+                                           ctypes.c_void_p(out.data_ptr()), _dtype_code(out.dtype), lse_ptr,
+                                           _stream()), self.ctx)
         return out, lse
 
     def reconstruct(self, layer0, n_layers, kv, t0, t1, out_dtype=torch.float32, out=None):

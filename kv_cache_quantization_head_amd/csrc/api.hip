@@ -172,6 +172,89 @@ extern "C" int qkv_attend(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t 
   return hip_status(ctx);
 }
 
+extern "C" int qkv_attend_with_chunk(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t n_q, int32_t q_dtype,
+                                     const void *d_k_new, const void *d_v_new, int64_t n_new, void *d_out,
+                                     int32_t out_dtype, float *d_lse, void *stream) {
+  const int rc = check_attend_with_chunk(ctx, layer, d_q, n_q, q_dtype, d_k_new, d_v_new, n_new, d_out, out_dtype);
+  if (rc != QKV_OK) return rc;
+  if (n_q == 0) return QKV_OK;
+  const int64_t n_cache = ctx->layers[layer].n_tokens;
+  if (n_new == 0) return qkv_attend(ctx, layer, d_q, n_q, q_dtype, d_out, out_dtype, d_lse, stream);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Plan &p = ctx->plan;
+  const qkv_config &c = p.cfg;
+  if (ctx->n_cu <= 0) {
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n_cu > 0)
+      ctx->n_cu = n_cu;
+    else
+      ctx->n_cu = 256;
+  }
+  // Each part may split a query block over at most kMaxSplits - 2 blocks;
+  // the last two partial slots hold the two complete parts for the merge.
+  const uint64_t HQ = uint64_t(c.n_heads) * uint64_t(n_q);
+  float *part_o = reinterpret_cast<float *>(scratch(ctx, p.attn_part_o_off));
+  float *part_lse = reinterpret_cast<float *>(scratch(ctx, p.attn_part_lse_off));
+  float *o_part[2] = {part_o + (kMaxSplits - 2) * HQ * c.head_dim, part_o + (kMaxSplits - 1) * HQ * c.head_dim};
+  float *l_part[2] = {part_lse + (kMaxSplits - 2) * HQ, part_lse + (kMaxSplits - 1) * HQ};
+  auto args_for = [&](int64_t n_keys) {
+    const AttnSplit w = attention_split(p, n_keys, n_q, ctx->n_cu, kMaxSplits - 2);
+    AttnArgs a{};
+    a.L = dev_layout(p);
+    a.q = d_q;
+    a.q_bf16 = q_dtype == QKV_BF16;
+    a.n_q = int32_t(n_q);
+    a.n_keys = int32_t(n_keys);
+    a.n_qblocks = int32_t(w.n_qblocks);
+    a.n_ktiles = int32_t(w.n_ktiles);
+    a.units_per_block = int32_t(w.units_per_block);
+    a.max_segments = int32_t(w.max_segments);
+    a.xcd_remap = w.n_blocks % 8 == 0;
+    a.part_o = part_o;
+    a.part_lse = part_lse;
+    return a;
+  };
+  (void)hipGetLastError();
+  // fresh part: straight into the output when the cache holds nothing
+  AttnArgs f = args_for(n_new);
+  f.k_new = static_cast<const uint16_t *>(d_k_new);
+  f.v_new = static_cast<const uint16_t *>(d_v_new);
+  if (n_cache == 0) {
+    f.out = d_out;
+    f.out_bf16 = out_dtype == QKV_BF16;
+    f.lse = d_lse;
+    launch_attend_fresh(f, st);
+    ctx->chain_layer = -1;  // scratch reused
+    return hip_status(ctx);
+  }
+  AttnArgs a = args_for(n_cache);
+  a.stream_k = ctx->arena + stream_offset(p, layer, 0);
+  a.stream_v = ctx->arena + stream_offset(p, layer, 1);
+  a.out = o_part[0];
+  a.out_bf16 = 0;
+  a.lse = l_part[0];
+  launch_attend(a, st);
+  f.out = o_part[1];
+  f.out_bf16 = 0;
+  f.lse = l_part[1];
+  launch_attend_fresh(f, st);
+  MergeArgs m{};
+  m.H = c.n_heads;
+  m.D = c.head_dim;
+  m.n_q = int32_t(n_q);
+  m.o1 = o_part[0];
+  m.lse1 = l_part[0];
+  m.o2 = o_part[1];
+  m.lse2 = l_part[1];
+  m.out = d_out;
+  m.out_bf16 = out_dtype == QKV_BF16;
+  m.lse = d_lse;
+  launch_attend_merge2(m, st);
+  ctx->chain_layer = -1;  // scratch reused
+  return hip_status(ctx);
+}
+
 extern "C" int qkv_reconstruct(qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int32_t kv, int64_t t0,
                                int64_t t1, void *d_out, int32_t out_dtype, void *stream) {
   const int rc = check_reconstruct(ctx, layer0, n_layers, kv, t0, t1, d_out, out_dtype);

@@ -87,6 +87,16 @@ struct AttnArgs {
   float *lse;                           // final [H][n_q] or null
   float *part_o;                        // [max_segments][H][n_q][D] partials
   float *part_lse;                      // [max_segments][H][n_q]
+  const uint16_t *k_new, *v_new;        // fresh keys/values [H][n_keys][D] bf16 (uncoded read)
+};
+
+// LSE merge of two complete attention results over disjoint key sets.
+struct MergeArgs {
+  int32_t H, D, n_q;
+  const float *o1, *lse1, *o2, *lse2;   // [H][n_q][D], [H][n_q]
+  void *out;                            // [H][n_q][D]
+  int32_t out_bf16;
+  float *lse;                           // [H][n_q] or null
 };
 
 struct XlArgs {

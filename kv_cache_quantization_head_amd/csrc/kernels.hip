@@ -1277,10 +1277,12 @@ __device__ __forceinline__ int chunk_of_lds(const int32_t *starts, int n_chunks,
 
 constexpr float AT3_TAU = 8.0f;
 
-template <int D, int G, int BITS, bool CB_BF16, int SMAX>
+template <int D, int G, int BITS, bool CB_BF16, int SMAX, bool FRESH = false>
 __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   // SMAX = the number of PRQ stages (a template parameter so that the staging
-  // registers are sized exactly)
+  // registers are sized exactly).  FRESH: the keys and values are the
+  // uncoded bf16 rows a.k_new / a.v_new ([H][n_keys][D]) of the chunk being
+  // generated; an item is then copied to LDS as read.
   constexpr int IC = 32;                   // channels of one rebuild item
   constexpr int NI = D / IC;               // items per key and tensor
   constexpr int KP = D + 8;                // bf16 elements per K row in LDS
@@ -1317,10 +1319,14 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   const int it_ch = (it_rem % NI) * IC, it_g = it_ch / G;
   const uint8_t *st = it_kv ? a.stream_v : a.stream_k;
 
-  if (tid == 0) nch_s = ((const StreamHeader *)(a.stream_k + L.header_off))->n_chunks;
-  __syncthreads();
-  for (int i = tid; i < nch_s; i += blockDim.x)
-    starts_s[i] = ((const StreamHeader *)(a.stream_k + L.header_off))->start[i];
+  if constexpr (FRESH) {
+    if (tid == 0) nch_s = 1;
+  } else {
+    if (tid == 0) nch_s = ((const StreamHeader *)(a.stream_k + L.header_off))->n_chunks;
+    __syncthreads();
+    for (int i = tid; i < nch_s; i += blockDim.x)
+      starts_s[i] = ((const StreamHeader *)(a.stream_k + L.header_off))->start[i];
+  }
 
   // Stream-K work split: the (head, query block, key tile) units are dealt
   // out in equal consecutive runs, one run per block; a block walks its run
@@ -1343,7 +1349,7 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     const int t1 = int(min(T, t0 + (u_end - u)));
     const int slot = (t0 == 0 && t1 == T) ? -1 : int(lb - (seg * T) / U);
     u += t1 - t0;
-    const uint8_t *idp = st + L.ids_off + uint64_t(h) * L.ids_head;
+    const uint8_t *idp = FRESH ? nullptr : st + L.ids_off + uint64_t(h) * L.ids_head;
     const int ks = t0 * AT_BK;
     const int ke = min(a.n_keys, t1 * AT_BK);
     const int n_tiles = ke > ks ? (ke - ks + AT_BK - 1) / AT_BK : 0;
@@ -1385,6 +1391,7 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
       if (!has_item || tile >= n_tiles) return -1;
       const int t = ks + tile * AT_BK + it_key;
       if (t >= ke) return -1;
+      if constexpr (FRESH) return 0;
       return L.id_bytes == 1 ? int(idp[t]) : int(((const uint16_t *)idp)[t]);
     };
     struct Regs {
@@ -1394,11 +1401,14 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     } R;
     // per-item pointers of the segment (key t = ks + AT_BK * tile + it_key)
     const int t_first = ks + it_key;
-    const uint8_t *code_p = st + L.codes_off + uint64_t(h) * L.codes_head + uint64_t(t_first) * L.codes_token +
-                            it_ch * BITS / 8;
-    const uint8_t *meta_p = st + L.meta_off + uint64_t(h) * L.meta_head + uint64_t(t_first) * L.meta_token +
-                            4 * it_g;
-    const uint8_t *cb_p = st + L.cb_off + uint64_t(h) * L.cb_head + uint64_t(it_ch) * EB;
+    const uint8_t *code_p = FRESH ? nullptr : st + L.codes_off + uint64_t(h) * L.codes_head +
+                                              uint64_t(t_first) * L.codes_token + it_ch * BITS / 8;
+    const uint8_t *meta_p = FRESH ? nullptr : st + L.meta_off + uint64_t(h) * L.meta_head +
+                                              uint64_t(t_first) * L.meta_token + 4 * it_g;
+    const uint8_t *cb_p = FRESH ? nullptr : st + L.cb_off + uint64_t(h) * L.cb_head + uint64_t(it_ch) * EB;
+    // fresh rows: channels it_ch .. it_ch+31 of key t_first of head h
+    const uint16_t *fresh_p = FRESH ? (it_kv ? a.v_new : a.k_new) + (uint64_t(h) * a.n_keys + t_first) * D + it_ch
+                                    : nullptr;
     const uint64_t tile_codes = uint64_t(AT_BK) * L.codes_token, tile_meta = uint64_t(AT_BK) * L.meta_token;
     // packed data of the item's key: centroid slice, codes, (sigma, z); all
     // zero when there is no key, which rebuilds to zero
@@ -1412,6 +1422,12 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   #pragma unroll
           for (int w = 0; w < KW; ++w) R.codes[s2][w] = 0u;
         }
+        return;
+      }
+      if constexpr (FRESH) {
+        const uint16_t *row = fresh_p + uint64_t(tile) * AT_BK * D;
+  #pragma unroll
+        for (int i = 0; i < KC; ++i) R.cent[i] = *(const uint4 *)(row + 8 * i);
         return;
       }
       const int cslot = nch_s > 1 ? chunk_of_lds(starts_s, nch_s, ks + tile * AT_BK + it_key) : 0;
@@ -1467,6 +1483,12 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     // ulps of a bf16 rounding boundary.
     auto dequant_store = [&](int buf) {
       if (!has_item) return;
+      if constexpr (FRESH) {
+        uint16_t *dst = it_kv ? &Vs[buf][it_key * VP + it_ch] : &Ks[buf][it_key * KP + it_ch];
+  #pragma unroll
+        for (int i = 0; i < KC; ++i) *(uint4 *)(dst + 8 * i) = R.cent[i];
+        return;
+      }
       float xh[IC];
       float zs = 0.0f;
   #pragma unroll
@@ -1653,6 +1675,35 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttnArgs a) {
     *(float4 *)((float *)a.out + off) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   }
   if (a.lse && d4 == 0) a.lse[uint64_t(h) * a.n_q + q] = wsum > 0.0f ? mx + logf(wsum) : -INFINITY;
+}
+
+// Two complete results over disjoint key sets (the packed cache and the fresh
+// chunk) combined by their log-sum-exps: O = (w1 O1 + w2 O2) / (w1 + w2),
+// w_i = exp(lse_i - max), LSE = max + log(w1 + w2); an empty side has
+// lse = -inf and weight 0.  One thread per (query, 4 channels); blockIdx.y =
+// head.
+__global__ __launch_bounds__(256) void k_attend_merge2(MergeArgs m) {
+  const int D4 = m.D / 4;
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= int64_t(m.n_q) * D4) return;
+  const int q = int(idx / D4), d4 = int(idx % D4), h = blockIdx.y;
+  const uint64_t r = uint64_t(h) * m.n_q + q;
+  const float l1 = m.lse1[r], l2 = m.lse2[r];
+  const float mx = fmaxf(l1, l2);
+  const float w1 = l1 == -INFINITY ? 0.0f : expf(l1 - mx);
+  const float w2 = l2 == -INFINITY ? 0.0f : expf(l2 - mx);
+  const float ws = w1 + w2;
+  const float inv = ws > 0.0f ? 1.0f / ws : 0.0f;
+  const float4 a = *(const float4 *)(m.o1 + r * m.D + 4 * d4);
+  const float4 b = *(const float4 *)(m.o2 + r * m.D + 4 * d4);
+  const float4 o = make_float4(fmaf(w1, a.x, w2 * b.x) * inv, fmaf(w1, a.y, w2 * b.y) * inv,
+                               fmaf(w1, a.z, w2 * b.z) * inv, fmaf(w1, a.w, w2 * b.w) * inv);
+  const uint64_t off = r * m.D + 4 * d4;
+  if (m.out_bf16)
+    *(uint2 *)((uint16_t *)m.out + off) = make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+  else
+    *(float4 *)((float *)m.out + off) = o;
+  if (m.lse && d4 == 0) m.lse[r] = ws > 0.0f ? mx + logf(ws) : -INFINITY;
 }
 
 // ------------------------------------------------------------ cross layer
@@ -1921,6 +1972,19 @@ void launch_quantize(const EncodeArgs &a, int streams, hipStream_t st) {
 }
 void launch_reconstruct(const ReconArgs &a, int n_layers, int64_t out_tokens, int out_t_off, hipStream_t st) {
   QKV_DISPATCH_CODEC(a.L, launch_recon_t, a, n_layers, out_tokens, out_t_off, st);
+}
+void launch_attend_fresh(const AttnArgs &a, hipStream_t st) {
+  const int64_t total = int64_t(a.n_ktiles) * a.n_qblocks * a.L.H;
+  const dim3 grid(unsigned(cdiv(total, a.units_per_block)));
+  if (a.L.D == 64)
+    hipLaunchKernelGGL((k_attend3<64, 32, 2, true, 1, true>), grid, dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_attend3<128, 32, 2, true, 1, true>), grid, dim3(512), 0, st, a);
+  if (a.max_segments > 1)
+    hipLaunchKernelGGL(k_attend_merge, dim3(cdiv(int64_t(a.n_q) * (a.L.D / 4), 256), a.L.H), dim3(256), 0, st, a);
+}
+void launch_attend_merge2(const MergeArgs &m, hipStream_t st) {
+  hipLaunchKernelGGL(k_attend_merge2, dim3(cdiv(int64_t(m.n_q) * (m.D / 4), 256), m.H), dim3(256), 0, st, m);
 }
 void launch_attend(const AttnArgs &a, hipStream_t st) {
   QKV_DISPATCH_CODEC(a.L, launch_attend_t, a, st);

@@ -142,6 +142,21 @@ int check_attend(const qkv_ctx *ctx, int32_t layer, const void *q, int64_t n_q, 
   return QKV_OK;
 }
 
+int check_attend_with_chunk(const qkv_ctx *ctx, int32_t layer, const void *q, int64_t n_q, int32_t q_dtype,
+                            const void *k_new, const void *v_new, int64_t n_new, const void *out,
+                            int32_t out_dtype) {
+  if (!ctx) return QKV_E_INVAL;
+  if (layer < 0 || layer >= ctx->plan.cfg.n_layers) return QKV_E_INVAL;
+  if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype) || n_q < 0) return QKV_E_INVAL;
+  if (n_new < 0 || n_new >= (int64_t(1) << 31)) return QKV_E_INVAL;
+  if (n_q > 0 && (!q || !out)) return QKV_E_INVAL;
+  if (n_new > 0 && (!k_new || !v_new)) return QKV_E_INVAL;
+  if (n_q > ctx->plan.cfg.max_query_tokens) return QKV_E_CAPACITY;
+  if (ctx->plan.cfg.xlayer && layer >= 1) return QKV_E_UNSUPPORTED;
+  if (ctx->layers[layer].n_tokens == 0 && n_new == 0) return QKV_E_STATE;
+  return QKV_OK;
+}
+
 int check_reconstruct(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int32_t kv, int64_t t0,
                       int64_t t1, const void *out, int32_t out_dtype) {
   if (!ctx) return QKV_E_INVAL;
@@ -172,18 +187,19 @@ int check_rewind(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int64_t n
   return QKV_OK;
 }
 
-AttnSplit attention_split(const Plan &p, int64_t n_keys, int64_t n_q, int n_cu) {
+AttnSplit attention_split(const Plan &p, int64_t n_keys, int64_t n_q, int n_cu, int max_splits) {
   AttnSplit w{};
   w.n_qblocks = (n_q + 255) / 256;
   w.n_ktiles = std::max<int64_t>(1, (n_keys + 63) / 64);
   const int64_t total = w.n_qblocks * w.n_ktiles * p.cfg.n_heads;
   const int64_t cus = std::max(n_cu, 1);
   // one run per compute unit, but no query block shared by more than
-  // kMaxSplits blocks (the partial slots of the scratch region)
-  w.units_per_block = std::max((total + cus - 1) / cus, (w.n_ktiles + kMaxSplits - 2) / (kMaxSplits - 1));
+  // max_splits blocks (partial slots of the scratch region)
+  const int64_t ms = std::max(2, std::min(max_splits, kMaxSplits));
+  w.units_per_block = std::max((total + cus - 1) / cus, (w.n_ktiles + ms - 2) / (ms - 1));
   w.n_blocks = (total + w.units_per_block - 1) / w.units_per_block;
   // blocks meeting one query block: at most ceil((T - 1) / U) + 1
-  w.max_segments = std::min<int64_t>(kMaxSplits, (w.n_ktiles - 1 + w.units_per_block - 1) / w.units_per_block + 1);
+  w.max_segments = std::min<int64_t>(ms, (w.n_ktiles - 1 + w.units_per_block - 1) / w.units_per_block + 1);
   return w;
 }
 

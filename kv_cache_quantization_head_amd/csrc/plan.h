@@ -89,6 +89,9 @@ int check_attend(const qkv_ctx *ctx, int32_t layer, const void *q, int64_t n_q, 
 int check_reconstruct(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int32_t kv, int64_t t0,
                       int64_t t1, const void *out, int32_t out_dtype);
 int check_rewind(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int64_t n_tokens);
+int check_attend_with_chunk(const qkv_ctx *ctx, int32_t layer, const void *q, int64_t n_q, int32_t q_dtype,
+                            const void *k_new, const void *v_new, int64_t n_new, const void *out,
+                            int32_t out_dtype);
 
 // Work split of an attention call (stream-K): the (head, query block of
 // 256, key tile of 64) units are dealt out in runs of units_per_block
@@ -96,7 +99,8 @@ int check_rewind(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int64_t n
 struct AttnSplit {
   int64_t n_qblocks, n_ktiles, units_per_block, n_blocks, max_segments;
 };
-AttnSplit attention_split(const Plan &p, int64_t n_keys, int64_t n_q, int n_cu);
+// max_splits bounds the blocks sharing one query block (partial slots used).
+AttnSplit attention_split(const Plan &p, int64_t n_keys, int64_t n_q, int n_cu, int max_splits = kMaxSplits);
 
 // Byte offset of stream (layer, kv) from the arena base.
 inline uint64_t stream_offset(const Plan &p, int layer, int kv) {

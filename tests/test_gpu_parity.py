@@ -157,6 +157,16 @@ def test_wan_layer_full_size_sampled_heads():
     err = attention_tolerance_check(out.cpu().numpy()[heads][:, sample], lse.cpu().numpy()[heads][:, sample],
                                     o_ref, lse_ref)
     _say(f"wan layer attention (sampled) max abs err {err:.3e}")
+    # the same read with the next 4680-token chunk still in bf16
+    kn = synth.kv_tokens(cfgs, 0, 0, 32760, 4680)
+    vn = synth.kv_tokens(cfgs, 0, 1, 32760, 4680)
+    out, lse = codec.attend_with_chunk(0, q.to(DEV), kn.to(DEV), vn.to(DEV))
+    khat = np.concatenate([ost[0].xhat(), kn.float().numpy()[heads]], axis=1)
+    vhat = np.concatenate([ost[1].xhat(), vn.float().numpy()[heads]], axis=1)
+    o_ref, lse_ref = o_attend.attend(q.float().numpy()[heads][:, sample], khat, vhat)
+    err = attention_tolerance_check(out.cpu().numpy()[heads][:, sample], lse.cpu().numpy()[heads][:, sample],
+                                    o_ref, lse_ref)
+    _say(f"wan layer attention with a fresh 4680-token chunk (sampled) max abs err {err:.3e}")
 
 
 def test_encode_is_deterministic():
@@ -221,3 +231,42 @@ def test_near_ties_pair_list_and_full_rescoring():
         ids = o.chunks[0][0].ids
         assert np.count_nonzero(ids == 0) > T // 20 and np.count_nonzero(ids == 2) > T // 20
         assert_stream_equal(codec, 0, kv, o)
+
+
+@pytest.mark.parametrize("n_new,out_dtype", [(4680, torch.float32), (77, torch.bfloat16), (1, torch.float32)],
+                         ids=["chunk4680_f32", "ragged77_bf16", "one_token_f32"])
+def test_attend_with_fresh_chunk(n_new, out_dtype):
+    """Attention over the packed cache followed by a fresh bf16 chunk equals
+    the oracle's attention over the concatenated keys (cache rebuilt by the
+    oracle, fresh rows as given), within the attention tolerance."""
+    cfgs = synth.scaled(synth.WAN_LAYER, n_heads=2, tokens=3000 + n_new)
+    _say(f"fresh chunk: cache 3000 + fresh {n_new}, out {out_dtype}")
+    codec, ost, _ = _encode_and_oracle(cfgs, [3000], "bf16", max_q=512)
+    kn = synth.kv_tokens(cfgs, 0, 0, 3000, n_new)
+    vn = synth.kv_tokens(cfgs, 0, 1, 3000, n_new)
+    q = synth.queries(cfgs, 0, 300)
+    out, lse = codec.attend_with_chunk(0, q.to(DEV), kn.to(DEV), vn.to(DEV), out_dtype=out_dtype)
+    khat = np.concatenate([ost[0].xhat(), kn.float().numpy()], axis=1)
+    vhat = np.concatenate([ost[1].xhat(), vn.float().numpy()], axis=1)
+    o_ref, lse_ref = o_attend.attend(q.float().numpy(), khat, vhat)
+    err = attention_tolerance_check(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+    _say(f"fresh chunk {n_new}: max abs err {err:.3e}")
+
+
+def test_attend_with_fresh_chunk_edges():
+    """No fresh tokens: the same bytes as qkv_attend.  Empty cache: attention
+    over the fresh tokens alone, against the oracle."""
+    cfgs = synth.scaled(synth.WAN_LAYER, n_heads=2, tokens=2000)
+    codec, ost, _ = _encode_and_oracle(cfgs, [1500], "bf16", max_q=512)
+    q = synth.queries(cfgs, 0, 257).to(DEV)
+    empty = torch.empty((2, 0, 128), dtype=torch.bfloat16, device=DEV)
+    o1, l1 = codec.attend(0, q)
+    o2, l2 = codec.attend_with_chunk(0, q, empty, empty)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    fresh = make_codec(2, 128, 256, 2, 2, 32, max_tokens=2000, max_chunks=1, max_q=512)
+    kn = synth.kv_tokens(cfgs, 0, 0, 0, 500)
+    vn = synth.kv_tokens(cfgs, 0, 1, 0, 500)
+    out, lse = fresh.attend_with_chunk(0, q, kn.to(DEV), vn.to(DEV))
+    o_ref, lse_ref = o_attend.attend(q.float().cpu().numpy(), kn.float().numpy(), vn.float().numpy())
+    attention_tolerance_check(out.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)

@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     L = qkv.lib()
     names = _declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(L, n), n
     assert "qkv_encode_chunk" in names and "qkv_attend" in names
@@ -124,6 +124,17 @@ def test_call_validation_before_enqueue(ctx):
     assert L.qkv_attend(ctx, 2, p, 16, B.QKV_BF16, p, B.QKV_F32, None, None) == B.QKV_E_INVAL
     assert L.qkv_attend(ctx, 0, p, 16, 5, p, B.QKV_F32, None, None) == B.QKV_E_INVAL
     assert L.qkv_attend(ctx, 0, None, 16, B.QKV_BF16, p, B.QKV_F32, None, None) == B.QKV_E_INVAL
+    # attention with a fresh chunk: nothing to attend to, capacity, arguments
+    A = L.qkv_attend_with_chunk
+    assert A(ctx, 0, p, 16, B.QKV_BF16, None, None, 0, p, B.QKV_F32, None, None) == B.QKV_E_STATE
+    assert A(ctx, 0, p, 4681, B.QKV_BF16, p, p, 8, p, B.QKV_F32, None, None) == B.QKV_E_CAPACITY
+    assert A(ctx, 2, p, 16, B.QKV_BF16, p, p, 8, p, B.QKV_F32, None, None) == B.QKV_E_INVAL
+    assert A(ctx, 0, p, 16, B.QKV_BF16, None, p, 8, p, B.QKV_F32, None, None) == B.QKV_E_INVAL
+    assert A(ctx, 0, p, 16, B.QKV_BF16, p, None, 8, p, B.QKV_F32, None, None) == B.QKV_E_INVAL
+    assert A(ctx, 0, p, 16, B.QKV_BF16, p, p, -1, p, B.QKV_F32, None, None) == B.QKV_E_INVAL
+    assert A(ctx, 0, None, 16, B.QKV_BF16, p, p, 8, p, B.QKV_F32, None, None) == B.QKV_E_INVAL
+    assert A(ctx, 0, p, 16, B.QKV_BF16, p, p, 8, None, B.QKV_F32, None, None) == B.QKV_E_INVAL
+    assert A(ctx, 0, p, 16, 9, p, p, 8, p, B.QKV_F32, None, None) == B.QKV_E_INVAL
     assert L.qkv_reconstruct(ctx, 0, 1, 0, 0, 10, p, B.QKV_F32, None) == B.QKV_E_STATE
     assert L.qkv_reconstruct(ctx, 0, 1, 2, 0, 10, p, B.QKV_F32, None) == B.QKV_E_INVAL
     assert L.qkv_reconstruct(ctx, 0, 1, 0, 5, 4, p, B.QKV_F32, None) == B.QKV_E_INVAL
@@ -147,6 +158,8 @@ def test_cross_layer_attend_unsupported_and_order():
     L = qkv.lib()
     p = ctypes.c_void_p(FAKE)
     assert L.qkv_attend(c, 1, p, 16, B.QKV_BF16, p, B.QKV_F32, None, None) == B.QKV_E_UNSUPPORTED
+    assert L.qkv_attend_with_chunk(c, 1, p, 16, B.QKV_BF16, p, p, 8, p, B.QKV_F32, None,
+                                   None) == B.QKV_E_UNSUPPORTED
     # layer 1 before layer 0 (no chain) is a state error
     assert L.qkv_encode_chunk(c, 1, 1, p, p, 100, None) == B.QKV_E_STATE
     L.qkv_destroy(c)
