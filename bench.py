@@ -40,6 +40,10 @@ def parse():
                          "layers (attention over the packed cache plus the chunk's fresh bf16 K/V for "
                          "every denoising step and layer, then the chunk's encode)")
     ap.add_argument("--denoise", type=int, default=4, help="denoising steps per chunk (--fresh)")
+    ap.add_argument("--reuse", action="store_true",
+                    help="instead of the default step: encode a long-rollout layer (187200 tokens in 40 "
+                         "calls) with codebook reuse and with per-call snapshots; time, reconstruction "
+                         "error and storage cost of each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (a known-size "
                          "reference for HBM byte counters)")
@@ -225,6 +229,77 @@ def fresh_main(args):
         "encode_chunk_ms": round(enc, 4)}), flush=True)
 
 
+def reuse_main(args):
+    """Codebook reuse against per-call snapshots on one long-rollout layer
+    (12 heads, 187 200 tokens arriving as 40 calls of 4680, 3 INT2 stages,
+    C = 256): a step encodes the whole layer from empty in each mode; after
+    the timed steps the reconstruction error of each mode is measured over
+    the layer, with the storage cost of each."""
+    import torch
+    import kv_cache_quantization_head_amd as qkv
+    import synth
+    from fractions import Fraction
+
+    dev = torch.device("cuda:0")
+    cfgs = synth.LONG_ROLLOUT
+    H, T, d, C, S, b, G = (cfgs.n_heads, cfgs.tokens, cfgs.head_dim, cfgs.n_clusters, cfgs.n_stages,
+                           cfgs.bits, cfgs.group)
+    n_call = 4680
+    n_calls = T // n_call
+    k = synth.kv_tokens(cfgs, 0, 0, 0, T, device=dev)
+    v = synth.kv_tokens(cfgs, 0, 1, 0, T, device=dev)
+    codecs = {}
+    for reuse in (0, 1):
+        cfg = qkv.config(1, H, d, C, S, b, G, kmeans_iters=cfgs.iters, max_tokens=T, max_chunk_tokens=n_call,
+                         max_chunks=n_calls, kv_dtype=qkv.QKV_BF16, max_query_tokens=0, codebook_reuse=reuse)
+        codecs[reuse] = qkv.Codec(cfg, device=dev)
+    ks = [k[:, i * n_call:(i + 1) * n_call].contiguous() for i in range(n_calls)]
+    vs = [v[:, i * n_call:(i + 1) * n_call].contiguous() for i in range(n_calls)]
+    times = {0: [], 1: []}
+
+    def step(record):
+        for reuse, codec in codecs.items():
+            codec.rewind(0, 1, 0)
+            m = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            m[0].record()
+            for i in range(n_calls):
+                codec.encode_chunk(ks[i], vs[i])
+            m[1].record()
+            if record:
+                times[reuse].append(m)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    res = {}
+    for reuse, codec in codecs.items():
+        ms = sum(m[0].elapsed_time(m[1]) for m in times[reuse]) / len(times[reuse])
+        err = []
+        for kv, x in ((0, k), (1, v)):
+            xf = x.float()
+            rec = codec.reconstruct(0, 1, kv, 0, T)[0]
+            err.append(float(((rec - xf) ** 2).sum() / (xf ** 2).sum()))
+            del rec
+        cb_tokens = T if reuse else n_call
+        fixed = Fraction(S * b) + Fraction(S * 32, G) + Fraction(8, d)
+        bits = float(fixed + Fraction(8 * 2 * C, cb_tokens))
+        res["reuse" if reuse else "per_call"] = {
+            "layer_ms": round(ms, 4), "call_ms": round(ms / n_calls, 4),
+            "rel_sq_error_k": round(err[0], 6), "rel_sq_error_v": round(err[1], 6),
+            "bits_per_element": round(bits, 4)}
+    print(json.dumps({
+        "metric": "codebook reuse vs per-call snapshots: encode time of a long-rollout layer",
+        "value": res["reuse"]["layer_ms"], "unit": "ms per layer (40 calls of 4680 tokens)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False, "dtype": "bf16",
+        "data": "synthetic (seeded prototype/drift/outlier generator)",
+        "config": {"workload": "long_rollout layer: K,V bf16 [12, 187200, 128] in 40 calls of 4680, C=256, "
+                               "5 iterations, 3-stage INT2, G=32", "heads": H, "tokens": T, "calls": n_calls},
+        "modes": res}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -236,6 +311,9 @@ def main():
         return
     if args.fresh:
         fresh_main(args)
+        return
+    if args.reuse:
+        reuse_main(args)
         return
     import torch
     import kv_cache_quantization_head_amd as qkv

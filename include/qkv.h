@@ -93,6 +93,13 @@ typedef struct {
   int32_t xlayer;          /* 0: SAS + PRQ on every layer; 1: cross-layer residual
                               coding for layers >= 1 (requires QKV_BF16) */
   int32_t xlayer_rank;     /* r of the low-rank term, in [1, 64] when xlayer = 1 */
+  int32_t codebook_reuse;  /* 0: every encode call runs the k-means (warm start from the
+                              previous snapshot) and stores its own snapshot; 1: only a
+                              stream's first call (after a rewind to 0: the next call)
+                              runs the k-means; later calls assign their tokens to that
+                              codebook, which is the one snapshot of the stream (the
+                              codebook-reuse reading of centroid caching, QVG explainer,
+                              "Sommario tecnico" 3) */
 } qkv_config;
 
 /* Offsets (bytes from the arena base) and strides of one (layer, K|V) stream,
@@ -103,7 +110,9 @@ typedef struct {
  *   ids      u8|u16 [H][max_tokens]            cluster id of each token
  *   codebook kv_dtype [max_chunks][H][C][d]    snapshot of each encode call
  *   cnorm    f32 [max_chunks][H][C]            ||c||^2 of each snapshot row
- * The codebook of a token is the snapshot of the chunk that encoded it. */
+ * The codebook of a token is the snapshot of the chunk that encoded it.  With
+ * codebook_reuse = 1 there is one snapshot ([1][H][C][d], [1][H][C]) and the
+ * chunk strides are 0. */
 typedef struct {
   uint64_t codes_off, codes_stage_stride, codes_head_stride, codes_token_stride;
   uint64_t meta_off, meta_stage_stride, meta_head_stride, meta_token_stride;

@@ -27,7 +27,7 @@ class qkv_config(ctypes.Structure):
                 ("max_tokens", ctypes.c_int64), ("max_chunk_tokens", ctypes.c_int64),
                 ("max_chunks", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("max_query_tokens", ctypes.c_int64), ("xlayer", ctypes.c_int32),
-                ("xlayer_rank", ctypes.c_int32)]
+                ("xlayer_rank", ctypes.c_int32), ("codebook_reuse", ctypes.c_int32)]
 
 
 class qkv_layout_desc(ctypes.Structure):
@@ -96,10 +96,10 @@ def status_string(status, ctx=None):
 
 def config(n_layers, n_heads, head_dim, n_clusters, n_stages, bits, group_size, kmeans_iters=5,
            max_tokens=0, max_chunk_tokens=0, max_chunks=1, kv_dtype=QKV_BF16,
-           max_query_tokens=0, xlayer=0, xlayer_rank=0):
+           max_query_tokens=0, xlayer=0, xlayer_rank=0, codebook_reuse=0):
     return qkv_config(n_layers, n_heads, head_dim, n_clusters, n_stages, bits, group_size,
                       kmeans_iters, max_tokens, max_chunk_tokens, max_chunks, kv_dtype,
-                      max_query_tokens, xlayer, xlayer_rank)
+                      max_query_tokens, xlayer, xlayer_rank, codebook_reuse)
 
 
 def workspace_bytes(cfg):

@@ -46,8 +46,14 @@ extern "C" int qkv_init(const qkv_config *cfg, void *d_arena, size_t arena_bytes
 }
 
 // SAS + PRQ for the 2*n_layers streams of `a` (k-means loop, then codes).
+// iters < 0: assign to the stream's codebook as it stands (codebook reuse).
 static void enqueue_sas(const EncodeArgs &a, int streams, int iters, hipStream_t st) {
   launch_header(a, streams, st);
+  if (iters < 0) {
+    launch_assign(a, streams, st);
+    launch_quantize(a, streams, st);
+    return;
+  }
   launch_init(a, streams, st);
   for (int it = 0; it < iters; ++it) {
     launch_assign(a, streams, st);
@@ -81,12 +87,14 @@ extern "C" int qkv_encode_chunk(qkv_ctx *ctx, int32_t layer0, int32_t n_layers, 
   const uint8_t *kin = static_cast<const uint8_t *>(d_k);
   const uint8_t *vin = static_cast<const uint8_t *>(d_v);
 
+  // codebook reuse: calls after a stream's first only assign
+  const int iters = c.codebook_reuse && slot > 0 ? -1 : c.kmeans_iters;
   (void)hipGetLastError();
   if (!c.xlayer) {
     a.layer0 = layer0;
     a.k_in = kin;
     a.v_in = vin;
-    enqueue_sas(a, 2 * n_layers, c.kmeans_iters, st);
+    enqueue_sas(a, 2 * n_layers, iters, st);
   } else {
     const uint64_t HD = uint64_t(c.n_heads) * c.head_dim;
     const uint64_t kv_stride = HD * c.head_dim + 2 * HD * uint64_t(c.xlayer_rank);
@@ -100,7 +108,7 @@ extern "C" int qkv_encode_chunk(qkv_ctx *ctx, int32_t layer0, int32_t n_layers, 
       a.chain = chain;
       if (l == 0) {
         a.pred = nullptr;
-        enqueue_sas(a, 2, c.kmeans_iters, st);
+        enqueue_sas(a, 2, iters, st);
       } else {
         XlArgs x{};
         x.H = c.n_heads; x.D = c.head_dim; x.r = c.xlayer_rank; x.n = int32_t(n);

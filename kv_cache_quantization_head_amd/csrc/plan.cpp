@@ -27,6 +27,7 @@ int make_plan(const qkv_config *cfg, Plan *plan) {
   if (!valid_dtype(c.kv_dtype)) return QKV_E_INVAL;
   if (c.max_query_tokens < 0 || c.max_query_tokens >= (int64_t(1) << 31)) return QKV_E_INVAL;
   if (c.xlayer != 0 && c.xlayer != 1) return QKV_E_INVAL;
+  if (c.codebook_reuse != 0 && c.codebook_reuse != 1) return QKV_E_INVAL;
   if (c.xlayer) {
     if (c.xlayer_rank < 1 || c.xlayer_rank > 64) return QKV_E_INVAL;
     if (c.kv_dtype != QKV_BF16) return QKV_E_INVAL;
@@ -62,15 +63,17 @@ int make_plan(const qkv_config *cfg, Plan *plan) {
   s.ids_head = T * s.id_bytes;
   s.ids_off = off;
   off = align_up(off + H * s.ids_head);
+  // one snapshot per chunk, or one per stream (codebook reuse: stride 0)
+  const uint64_t snaps = c.codebook_reuse ? 1 : K;
   s.cb_row = d * p.kv_elem_bytes;
   s.cb_head = C * s.cb_row;
-  s.cb_chunk = H * s.cb_head;
+  s.cb_chunk = c.codebook_reuse ? 0 : H * s.cb_head;
   s.cb_off = off;
-  off = align_up(off + K * s.cb_chunk);
+  off = align_up(off + snaps * H * s.cb_head);
   s.cn_head = C * 4;
-  s.cn_chunk = H * s.cn_head;
+  s.cn_chunk = c.codebook_reuse ? 0 : H * s.cn_head;
   s.cn_off = off;
-  off = align_up(off + K * s.cn_chunk);
+  off = align_up(off + snaps * H * s.cn_head);
   s.bytes = off;
 
   p.streams_bytes = 2 * uint64_t(c.n_layers) * s.bytes;

@@ -12,6 +12,8 @@ element are
   + 8*cb_bytes*C/n_call         the call's codebook, amortised over its tokens
 
 with id_bytes = 1 for C <= 256, else 2, and cb_bytes the cache dtype's size.
+With codebook reuse the stream keeps one codebook, so n_call is replaced by
+every token the stream holds.
 """
 from fractions import Fraction
 

@@ -10,6 +10,11 @@ that encoded it; earlier chunks are never re-encoded.
 
 In cross-layer mode a layer >= 1 has no clustering: its base is the
 prediction from the previous layer's reconstruction (see ``xlayer``).
+
+Codebook reuse (the other reading of centroid caching, "Sommario tecnico"
+3, offered as an option): only a stream's first call runs the k-means; a
+later call assigns its tokens to that first codebook, with no iterations,
+and keeps it as its snapshot.
 """
 import numpy as np
 
@@ -54,11 +59,12 @@ def encode_residual_head(x, pred, n_stages, bits, group):
 class Stream:
     """Cache stream of one layer and tensor: all heads, all chunks so far."""
 
-    def __init__(self, n_heads, head_dim, n_clusters, iters, n_stages, bits, group, dtype):
+    def __init__(self, n_heads, head_dim, n_clusters, iters, n_stages, bits, group, dtype, reuse=False):
         self.H, self.d = n_heads, head_dim
         self.C, self.iters = n_clusters, iters
         self.S, self.b, self.G = n_stages, bits, group
         self.dtype = dtype
+        self.reuse = reuse
         self.chunks = []          # list of per-head Chunk lists
         self.starts = []          # first token of each chunk
 
@@ -67,12 +73,14 @@ class Stream:
         return sum(ch[0].xhat.shape[0] for ch in self.chunks) if self.chunks else 0
 
     def encode(self, x):
-        """Append x [H, n, d]; the k-means warm-starts from the last snapshot."""
+        """Append x [H, n, d]; the k-means warm-starts from the last snapshot
+        (with reuse, a later call only assigns to the first codebook)."""
         prev = self.chunks[-1] if self.chunks else None
         per_head = []
         for h in range(self.H):
             init = None if prev is None else prev[h].codebook
-            per_head.append(encode_head(x[h], self.C, self.iters, self.S, self.b,
+            iters = 0 if (self.reuse and prev is not None) else self.iters
+            per_head.append(encode_head(x[h], self.C, iters, self.S, self.b,
                                         self.G, self.dtype, init=init))
         self.starts.append(self.n_tokens)
         self.chunks.append(per_head)

@@ -270,3 +270,45 @@ def test_attend_with_fresh_chunk_edges():
     out, lse = fresh.attend_with_chunk(0, q, kn.to(DEV), vn.to(DEV))
     o_ref, lse_ref = o_attend.attend(q.float().cpu().numpy(), kn.float().numpy(), vn.float().numpy())
     attention_tolerance_check(out.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_codebook_reuse_matches_oracle(dtype):
+    """Codebook reuse: the first call runs the k-means, later calls only
+    assign their tokens to its codebook (one snapshot per stream); after a
+    rewind to 0 the next call runs the k-means again."""
+    base = synth.WAN_LAYER if dtype == "bf16" else synth.scaled(synth.TINY, per_token_labels=False, drift=0.02)
+    cfgs = synth.scaled(base, n_heads=2, head_dim=128, n_clusters=64, group=32, tokens=4000)
+    n_list = [1560, 1560, 880]
+    S, b, it = cfgs.n_stages, cfgs.bits, cfgs.iters
+    codec = make_codec(2, 128, 64, S, b, 32, iters=it, max_tokens=4000, max_chunks=3, dtype=dtype, max_q=256,
+                       reuse=1)
+    ost = [oracle_stream(2, 128, 64, it, S, b, 32, dtype, reuse=True) for _ in range(2)]
+    t0 = 0
+    _say(f"codebook reuse {dtype}: chunks {n_list}")
+    for n in n_list:
+        k = synth.kv_tokens(cfgs, 0, 0, t0, n)
+        v = synth.kv_tokens(cfgs, 0, 1, t0, n)
+        codec.encode_chunk(k.to(DEV), v.to(DEV))
+        ost[0].encode(k.float().numpy())
+        ost[1].encode(v.float().numpy())
+        t0 += n
+    torch.cuda.synchronize()
+    for kv in (0, 1):
+        assert_stream_equal(codec, 0, kv, ost[kv])
+        rec = codec.reconstruct(0, 1, kv, 0, t0)[0].cpu().numpy()
+        np.testing.assert_array_equal(f32_bits(rec), f32_bits(ost[kv].xhat()))
+    q = synth.queries(synth.scaled(cfgs, q_dtype=dtype), 0, 256)
+    out, lse = codec.attend(0, q.to(DEV))
+    o_ref, lse_ref = o_attend.attend(q.float().numpy(), ost[0].xhat(), ost[1].xhat())
+    attention_tolerance_check(out.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+    # rewind to 0: the next call clusters afresh
+    codec.rewind(0, 1, 0)
+    k = synth.kv_tokens(cfgs, 0, 0, 1560, 1560)
+    v = synth.kv_tokens(cfgs, 0, 1, 1560, 1560)
+    codec.encode_chunk(k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    for kv, x in ((0, k), (1, v)):
+        o = oracle_stream(2, 128, 64, it, S, b, 32, dtype, reuse=True)
+        o.encode(x.float().numpy())
+        assert_stream_equal(codec, 0, kv, o)

@@ -64,6 +64,7 @@ def test_workspace_bytes_matches_layout_closed_form():
     ("n_stages", 0), ("n_stages", 5), ("bits", 3), ("group_size", 16), ("group_size", 128),
     ("kmeans_iters", -1), ("max_tokens", 0), ("max_tokens", 1 << 31), ("max_chunks", 0),
     ("max_chunks", 257), ("kv_dtype", 7), ("max_chunk_tokens", 40000), ("xlayer", 2),
+    ("codebook_reuse", 2),
 ])
 def test_invalid_config_rejected(field, value):
     cfg = _cfg(**{field: value})
@@ -191,3 +192,20 @@ def test_per_call_input_slice_must_stay_under_2gib():
     assert qkv.workspace_bytes(_cfg(max_tokens=big, max_chunk_tokens=0, max_query_tokens=0)) == 0
     assert qkv.workspace_bytes(_cfg(max_tokens=big, max_chunk_tokens=big - 1, max_query_tokens=0)) > 0
     assert qkv.workspace_bytes(_cfg(max_tokens=big, max_chunk_tokens=4096, max_query_tokens=0)) > 0
+
+
+def test_codebook_reuse_keeps_one_snapshot():
+    """With codebook reuse each stream holds one codebook snapshot: the
+    snapshot strides are 0 and the arena shrinks by the other max_chunks - 1
+    snapshots of every stream."""
+    per_call, reused = _cfg(max_chunks=8), _cfg(max_chunks=8, codebook_reuse=1)
+    H, C, d = 12, 256, 128
+    saved = qkv.workspace_bytes(per_call) - qkv.workspace_bytes(reused)
+    one = H * C * d * 2 + H * C * 4
+    assert 2 * 2 * 7 * one <= saved <= 2 * 2 * (7 * one + 2 * 256)
+    rc, c = _init(reused)
+    assert rc == B.QKV_OK
+    d_ = B.qkv_layout_desc()
+    assert qkv.lib().qkv_layout(c, 1, 1, ctypes.byref(d_)) == B.QKV_OK
+    assert d_.codebook_chunk_stride == 0 and d_.cnorm_chunk_stride == 0
+    qkv.lib().qkv_destroy(c)
