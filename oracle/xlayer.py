@@ -22,6 +22,16 @@ Readings:
   + U[h*d+i, k] * w[k] for k = 0..r-1; pred is rounded once to fp32.
 * r0 = fl32(x_{l+1} - pred); the residual then goes through the same PRQ
   stages as the smoothed residual, and decode adds the stages to pred.
+
+Adapted configuration (the same page, on its two modes: the reusable one
+applies predictors calibrated in advance; the adapted one recomputes the
+light block-diagonal predictors for the video at hand).  Readings: the block
+B_h of each head is re-fitted once per video, on the tokens of the stream's
+first encode call, by least squares with the low-rank term held fixed:
+B_h = argmin over B of sum_t |B y_h[t] + (U w[t])_h - x_{l+1,h}[t]|^2,
+regularised by lam * I with lam = 2^-20 * trace(G_h) / d (G_h = sum_t y y^T)
+so the normal equations stay definite; solved in fp64, rounded to bf16
+(nearest even) like the given weights; later calls and the decoder use it.
 """
 import numpy as np
 
@@ -53,3 +63,24 @@ def predict(xhat_prev, B, U, V):
 def residual(x_next, pred):
     """r0 = fl32(x_{l+1} - pred)."""
     return np.asarray(x_next, dtype=np.float32) - np.asarray(pred, dtype=np.float32)
+
+
+REFIT_RIDGE = 2.0 ** -20
+
+
+def refit_block(xhat_prev, x_next, U, V):
+    """Adapted block-diagonal predictor: B [H, d, d] fp64 (before rounding)
+    and its bf16 rounding, from xhat_prev, x_next [H, T, d] and the fixed
+    low-rank factors U, V [H*d, r]."""
+    H, T, d = xhat_prev.shape
+    zeros = np.zeros((H, d, d), dtype=np.float32)
+    low_rank = predict(xhat_prev, zeros, U, V).astype(np.float64)      # U w, rounded to fp32
+    y = round_to_bf16(xhat_prev).astype(np.float64)
+    target = np.asarray(x_next, dtype=np.float64) - low_rank
+    B = np.empty((H, d, d), dtype=np.float64)
+    for h in range(H):
+        G = y[h].T @ y[h]
+        R = y[h].T @ target[h]
+        A = G + (REFIT_RIDGE * np.trace(G) / d) * np.eye(d)
+        B[h] = np.linalg.solve(A, R).T
+    return B, round_to_bf16(B)

@@ -124,3 +124,40 @@ def test_stored_sizes_match_closed_form_on_encoded_head():
     nbytes = sum(p.nbytes for p in ch.packed) + sum(s.nbytes + z.nbytes for s, z in zip(ch.sigmas, ch.zs)) \
         + 1024 * 1 + ch.codebook.astype(np.float32).nbytes
     assert Fraction(8 * nbytes, 1024 * 64) == bits.bits_per_element(2, 2, 64, 64, 16, 4, 1024)
+
+
+def test_refit_recovers_an_exact_block_predictor():
+    """Adapted mode: when x_{l+1} is exactly B_true y + U w (computed in fp64
+    from bf16 factors), the least-squares re-fit returns B_true up to the tiny
+    ridge bias, and its bf16 rounding is B_true itself."""
+    rng = np.random.default_rng(5)
+    H, T, d, r = 2, 600, 16, 3
+    xprev = rng.standard_normal((H, T, d)).astype(np.float32)
+    Btrue = numerics.round_to_bf16(0.3 * rng.standard_normal((H, d, d)))
+    U = numerics.round_to_bf16(0.2 * rng.standard_normal((H * d, r)))
+    V = numerics.round_to_bf16(0.2 * rng.standard_normal((H * d, r)))
+    y = numerics.round_to_bf16(xprev).astype(np.float64)
+    w = numerics.round_to_bf16(np.transpose(y, (1, 0, 2)).reshape(T, H * d) @ V.astype(np.float64))
+    lowrank = (w @ U.astype(np.float64).T).reshape(T, H, d).transpose(1, 0, 2)
+    xnext = np.einsum("hij,htj->hti", Btrue.astype(np.float64), y) + lowrank
+    B, Bb = xlayer.refit_block(xprev, xnext, U, V)
+    np.testing.assert_allclose(B, Btrue, rtol=0, atol=1e-4)
+    np.testing.assert_array_equal(Bb, Btrue)
+
+
+def test_refit_without_low_rank_is_ridge_least_squares():
+    """With U = 0 the re-fit is the ridge solution of min |Y B^T - X|, which
+    numpy's lstsq of the augmented system [Y; sqrt(lam) I] gives as well."""
+    rng = np.random.default_rng(6)
+    H, T, d = 1, 300, 8
+    xprev = rng.standard_normal((H, T, d)).astype(np.float32)
+    xnext = rng.standard_normal((H, T, d))
+    U = np.zeros((d, 1), np.float32)
+    V = np.zeros((d, 1), np.float32)
+    B, _ = xlayer.refit_block(xprev, xnext, U, V)
+    y = numerics.round_to_bf16(xprev).astype(np.float64)[0]
+    lam = xlayer.REFIT_RIDGE * np.trace(y.T @ y) / d
+    Ya = np.vstack([y, np.sqrt(lam) * np.eye(d)])
+    Xa = np.vstack([xnext[0], np.zeros((d, d))])
+    ref = np.linalg.lstsq(Ya, Xa, rcond=None)[0].T
+    np.testing.assert_allclose(B[0], ref, rtol=1e-10, atol=1e-12)
