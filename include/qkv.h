@@ -100,6 +100,12 @@ typedef struct {
                               codebook, which is the one snapshot of the stream (the
                               codebook-reuse reading of centroid caching, QVG explainer,
                               "Sommario tecnico" 3) */
+  int32_t xlayer_adapt;    /* with xlayer = 1: 0 uses the caller's block-diagonal B_h as
+                              given; 1 re-fits every B_h of layers >= 1 once per video, on
+                              the first encode call of the layer (ridge least squares with
+                              the low-rank term fixed, fp64, rounded to bf16), and uses the
+                              re-fitted blocks for that and every later call and for
+                              decoding (Coral-KV's adapted configuration) */
 } qkv_config;
 
 /* Offsets (bytes from the arena base) and strides of one (layer, K|V) stream,
@@ -196,6 +202,13 @@ int qkv_layout(const qkv_ctx *ctx, int32_t layer, int32_t kv, qkv_layout_desc *o
 /* First token of each chunk of `layer` (up to max entries); returns the
  * number of chunks, or a negative status. */
 int qkv_chunk_starts(const qkv_ctx *ctx, int32_t layer, int64_t *starts, int32_t max);
+
+/* Cross-layer mode with xlayer_adapt = 1: byte offset from the arena base of
+ * the re-fitted blocks of the transition into `layer` (1 <= layer <
+ * n_layers), bf16 [2 (K, V)][H][d][d] (row i of B_h maps head h's channels
+ * to output channel i), valid once that layer has been encoded since its
+ * stream was last empty.  Errors: QKV_E_INVAL (not adapted mode, bad layer). */
+int qkv_adapted_blocks(const qkv_ctx *ctx, int32_t layer, uint64_t *offset);
 
 /* Release the context (not the caller's device memory). */
 void qkv_destroy(qkv_ctx *ctx);

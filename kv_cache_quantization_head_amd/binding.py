@@ -27,7 +27,8 @@ class qkv_config(ctypes.Structure):
                 ("max_tokens", ctypes.c_int64), ("max_chunk_tokens", ctypes.c_int64),
                 ("max_chunks", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("max_query_tokens", ctypes.c_int64), ("xlayer", ctypes.c_int32),
-                ("xlayer_rank", ctypes.c_int32), ("codebook_reuse", ctypes.c_int32)]
+                ("xlayer_rank", ctypes.c_int32), ("codebook_reuse", ctypes.c_int32),
+                ("xlayer_adapt", ctypes.c_int32)]
 
 
 class qkv_layout_desc(ctypes.Structure):
@@ -76,6 +77,8 @@ def lib():
     L.qkv_layout.restype = ctypes.c_int
     L.qkv_chunk_starts.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_int64), i32]
     L.qkv_chunk_starts.restype = ctypes.c_int
+    L.qkv_adapted_blocks.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_uint64)]
+    L.qkv_adapted_blocks.restype = ctypes.c_int
     L.qkv_destroy.argtypes = [vp]
     L.qkv_destroy.restype = None
     L.qkv_status_string.argtypes = [vp, ctypes.c_int]
@@ -96,10 +99,10 @@ def status_string(status, ctx=None):
 
 def config(n_layers, n_heads, head_dim, n_clusters, n_stages, bits, group_size, kmeans_iters=5,
            max_tokens=0, max_chunk_tokens=0, max_chunks=1, kv_dtype=QKV_BF16,
-           max_query_tokens=0, xlayer=0, xlayer_rank=0, codebook_reuse=0):
+           max_query_tokens=0, xlayer=0, xlayer_rank=0, codebook_reuse=0, xlayer_adapt=0):
     return qkv_config(n_layers, n_heads, head_dim, n_clusters, n_stages, bits, group_size,
                       kmeans_iters, max_tokens, max_chunk_tokens, max_chunks, kv_dtype,
-                      max_query_tokens, xlayer, xlayer_rank, codebook_reuse)
+                      max_query_tokens, xlayer, xlayer_rank, codebook_reuse, xlayer_adapt)
 
 
 def workspace_bytes(cfg):
@@ -230,6 +233,13 @@ class Codec:
         buf = (ctypes.c_int64 * max(n, 1))()
         lib().qkv_chunk_starts(self.ctx, layer, buf, n)
         return [int(buf[i]) for i in range(n)]
+
+    def adapted_blocks(self, layer):
+        """Re-fitted predictor blocks of the transition into `layer`: [2, H, d, d] bf16 view."""
+        off = ctypes.c_uint64()
+        _check(lib().qkv_adapted_blocks(self.ctx, layer, ctypes.byref(off)), self.ctx)
+        H, d = self.cfg.n_heads, self.cfg.head_dim
+        return self.arena[off.value:off.value + 2 * H * d * d * 2].view(torch.bfloat16).view(2, H, d, d)
 
     # ---- read-back views of the arena (for tests and inspection) ----
     def _view(self, off, nbytes):

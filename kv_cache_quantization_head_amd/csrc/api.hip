@@ -45,6 +45,21 @@ extern "C" int qkv_init(const qkv_config *cfg, void *d_arena, size_t arena_bytes
   return QKV_OK;
 }
 
+// re-fitted blocks of the transition into layer l (adapted cross-layer mode)
+static uint16_t *refit_blocks(qkv_ctx *ctx, int l) {
+  const qkv_config &c = ctx->plan.cfg;
+  return reinterpret_cast<uint16_t *>(ctx->arena + ctx->plan.xl_refit_off +
+                                      uint64_t(l) * 2 * c.n_heads * c.head_dim * c.head_dim * 2);
+}
+
+extern "C" int qkv_adapted_blocks(const qkv_ctx *ctx, int32_t layer, uint64_t *offset) {
+  if (!ctx || !offset) return QKV_E_INVAL;
+  const qkv_config &c = ctx->plan.cfg;
+  if (!c.xlayer_adapt || layer < 1 || layer >= c.n_layers) return QKV_E_INVAL;
+  *offset = ctx->plan.xl_refit_off + uint64_t(layer) * 2 * c.n_heads * c.head_dim * c.head_dim * 2;
+  return QKV_OK;
+}
+
 // SAS + PRQ for the 2*n_layers streams of `a` (k-means loop, then codes).
 // iters < 0: assign to the stream's codebook as it stands (codebook reuse).
 static void enqueue_sas(const EncodeArgs &a, int streams, int iters, hipStream_t st) {
@@ -117,6 +132,27 @@ extern "C" int qkv_encode_chunk(qkv_ctx *ctx, int32_t layer0, int32_t n_layers, 
         x.kv_weight_stride = kv_stride;
         x.proj = proj;
         x.pred = pred;
+        if (c.xlayer_adapt) {
+          uint16_t *blocks = refit_blocks(ctx, l);
+          if (ctx->layers[l].starts.empty()) {
+            // first call of the video for this layer: re-fit the blocks on
+            // its tokens against the low-rank part of the prediction
+            x.lowrank_only = 1;
+            launch_xl_predict(x, 0, 2, st);
+            RefitArgs f{};
+            f.H = c.n_heads; f.D = c.head_dim; f.n = int32_t(n);
+            f.chain = chain;
+            f.k_in = a.k_in;
+            f.v_in = a.v_in;
+            f.low_rank = pred;
+            f.gram = reinterpret_cast<double *>(scratch(ctx, p.xl_gram_off));
+            f.b_out = blocks;
+            launch_xl_refit(f, st);
+            x.lowrank_only = 0;
+            x.skip_project = 1;
+          }
+          x.b_weights = blocks;
+        }
         launch_xl_predict(x, 0, 2, st);
         a.pred = pred;
         launch_header(a, 2, st);
@@ -313,6 +349,7 @@ extern "C" int qkv_reconstruct(qkv_ctx *ctx, int32_t layer0, int32_t n_layers, i
         x.kv_weight_stride = kv_stride;
         x.proj = proj;
         x.pred = pred;
+        x.b_weights = c.xlayer_adapt ? refit_blocks(ctx, l + 1) : nullptr;
         launch_xl_predict(x, kv, 1, st);
       }
     }

@@ -106,6 +106,21 @@ struct XlArgs {
   uint64_t kv_weight_stride;   // elements between the K and V blocks
   float *proj;                 // [2][n][r] bf16-rounded projections (as f32)
   float *pred;                 // [2][H][n][D]
+  // adapted predictor: when set, B of head h of tensor kv is read from
+  // b_weights + (kv*H + h)*D*D instead of the caller's block
+  const uint16_t *b_weights;
+  int32_t lowrank_only;        // pred = U w only (the block term left out)
+  int32_t skip_project;        // proj already holds this call's projections
+};
+
+// Adapted-predictor re-fit of one target layer (all heads, K and V).
+struct RefitArgs {
+  int32_t H, D, n;
+  const uint16_t *chain;       // [2][H][n][D] bf16 y (source layer reconstruction)
+  const uint8_t *k_in, *v_in;  // [H][n][D] bf16 target layer tokens
+  const float *low_rank;       // [2][H][n][D] U w (the pred buffer of a low-rank-only prediction)
+  double *gram;                // [kRefitParts][2 kv][2 mats][H][D][D]: y y^T and y (x - U w)^T
+  uint16_t *b_out;             // [2][H][D][D] bf16 re-fitted blocks
 };
 
 }  // namespace qkv

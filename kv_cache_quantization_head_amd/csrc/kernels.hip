@@ -1789,7 +1789,7 @@ __global__ __launch_bounds__(256) void k_xl_predict(XlArgs a, int kv0) {
   const int ig = tid % IG, tg = tid / IG;
   const uint64_t HD = uint64_t(a.H) * D;
   const uint16_t *W = a.weights + uint64_t(kv) * a.kv_weight_stride;
-  const uint16_t *B = W + uint64_t(h) * D * D;
+  const uint16_t *B = a.b_weights ? a.b_weights + (uint64_t(kv) * a.H + h) * D * D : W + uint64_t(h) * D * D;
   const uint16_t *U = W + HD * D + uint64_t(h) * D * a.r;
   const uint16_t *y = a.chain + uint64_t(kv) * HD * a.n + uint64_t(h) * a.n * D;
   const float *w = a.proj + uint64_t(kv) * a.n * a.r;
@@ -1834,8 +1834,10 @@ __global__ __launch_bounds__(256) void k_xl_predict(XlArgs a, int kv0) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[u][c] = fma(bd[c], yd[u], acc[u][c]);
     };
+    if (!a.lowrank_only) {
 #pragma unroll 4
-    for (int j = 0; j < D; ++j) step(ysT + j * TT, bsT + j * D);
+      for (int j = 0; j < D; ++j) step(ysT + j * TT, bsT + j * D);
+    }
     for (int kk = 0; kk < a.r; ++kk) step(wsT + kk * TT, usT + kk * D);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -1845,6 +1847,146 @@ __global__ __launch_bounds__(256) void k_xl_predict(XlArgs a, int kv0) {
       *(float4 *)pp = make_float4(float(acc[u][0]), float(acc[u][1]), float(acc[u][2]), float(acc[u][3]));
       *(float4 *)(pp + 4) = make_float4(float(acc[u][4]), float(acc[u][5]), float(acc[u][6]), float(acc[u][7]));
     }
+  }
+}
+
+// Adapted predictor, step 1: per (token range p, head, kv, matrix) the fp64
+// sums over the range's tokens of y y^T (matrix 0) and y (x - U w)^T
+// (matrix 1), in token order.  Block = 16 x 16 threads, thread (ti, tj)
+// owns entries [8 ti .. 8 ti + 7][8 tj .. 8 tj + 7]; tokens are staged
+// through LDS 32 at a time (y as fp32, the second factor as fp64).
+constexpr int RF_TC = 32;
+__global__ __launch_bounds__(256) void k_xl_gram(RefitArgs a) {
+  __shared__ float ys[RF_TC][128];
+  __shared__ double zs[RF_TC][128];
+  const int D = a.D, part = blockIdx.x, h = blockIdx.y, kv = blockIdx.z >> 1, mat = blockIdx.z & 1;
+  const int tid = threadIdx.x, ti = tid / 16, tj = tid % 16;
+  const int64_t t_beg = int64_t(a.n) * part / kRefitParts, t_end = int64_t(a.n) * (part + 1) / kRefitParts;
+  const uint16_t *y = a.chain + (uint64_t(kv) * a.H + h) * uint64_t(a.n) * D;
+  const uint16_t *x = (const uint16_t *)(kv ? a.v_in : a.k_in) + uint64_t(h) * a.n * D;
+  const float *lr = a.low_rank + (uint64_t(kv) * a.H + h) * uint64_t(a.n) * D;
+  const bool active = 8 * ti < D && 8 * tj < D;
+  double acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
+  for (int64_t c0 = t_beg; c0 < t_end; c0 += RF_TC) {
+    const int nc = int(min<int64_t>(RF_TC, t_end - c0));
+    __syncthreads();
+    for (int e = tid; e < RF_TC * D; e += 256) {
+      const int tt = e / D, j = e % D;
+      float yv = 0.0f;
+      double zv = 0.0;
+      if (tt < nc) {
+        const uint64_t off = uint64_t(c0 + tt) * D + j;
+        yv = bf16_to_f32(y[off]);
+        zv = mat == 0 ? double(yv) : double(bf16_to_f32(x[off])) - double(lr[off]);
+      }
+      ys[tt][j] = yv;
+      zs[tt][j] = zv;
+    }
+    __syncthreads();
+    if (active) {
+      for (int tt = 0; tt < nc; ++tt) {
+        double yi[8], zj[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) yi[i] = double(ys[tt][8 * ti + i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) zj[j] = zs[tt][8 * tj + j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[i][j] = fma(yi[i], zj[j], acc[i][j]);
+      }
+    }
+  }
+  if (active) {
+    double *g = a.gram + (((uint64_t(part) * 2 + kv) * 2 + mat) * a.H + h) * uint64_t(D) * D;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) g[uint64_t(8 * ti + i) * D + 8 * tj + j] = acc[i][j];
+  }
+}
+
+// Adapted predictor, step 2: one block per (head, kv).  A = sum of the parts
+// of y y^T (in part order) + lam I, lam = 2^-20 trace(A) / D; Cholesky
+// factor L (left-looking, in LDS); then, 16 right-hand sides at a time, the
+// columns c of R = sum of the parts of y (x - U w)^T are solved through
+// L z' = r and L^T z = z', and row c of the block is z, rounded to bf16.
+__global__ __launch_bounds__(256) void k_xl_solve(RefitArgs a) {
+  extern __shared__ double lds64[];
+  const int D = a.D, h = blockIdx.x, kv = blockIdx.y, tid = threadIdx.x;
+  double *Lm = lds64;                 // [D][D]
+  double *Z = lds64 + D * D;          // [16][D]
+  __shared__ double lam_s;
+  const uint64_t DD = uint64_t(D) * D;
+  auto part_ptr = [&](int p, int mat) {
+    return a.gram + (((uint64_t(p) * 2 + kv) * 2 + mat) * a.H + h) * DD;
+  };
+  for (int e = tid; e < D * D; e += 256) {
+    double v = 0.0;
+    for (int p = 0; p < kRefitParts; ++p) v += part_ptr(p, 0)[e];
+    Lm[e] = v;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double tr = 0.0;
+    for (int i = 0; i < D; ++i) tr += Lm[i * D + i];
+    lam_s = 0x1p-20 * tr / D;
+  }
+  __syncthreads();
+  if (tid < D) Lm[tid * D + tid] += lam_s;
+  __syncthreads();
+  // left-looking Cholesky: column j from the columns before it
+  for (int j = 0; j < D; ++j) {
+    if (tid == 0) {
+      double s = Lm[j * D + j];
+      for (int k = 0; k < j; ++k) s -= Lm[j * D + k] * Lm[j * D + k];
+      Lm[j * D + j] = sqrt(s > 0.0 ? s : 0x1p-1000);
+    }
+    __syncthreads();
+    const int i = j + 1 + tid;
+    if (i < D) {
+      double s = Lm[i * D + j];
+      for (int k = 0; k < j; ++k) s -= Lm[i * D + k] * Lm[j * D + k];
+      Lm[i * D + j] = s / Lm[j * D + j];
+    }
+    __syncthreads();
+  }
+  // 16 right-hand sides at a time: thread (cc, q) = column c0 + cc, terms k = q mod 16
+  const int cc = tid / 16, q = tid % 16;
+  for (int c0 = 0; c0 < D; c0 += 16) {
+    for (int e = tid; e < 16 * D; e += 256) {
+      const int col = e / D, row = e % D;
+      double v = 0.0;
+      for (int p = 0; p < kRefitParts; ++p) v += part_ptr(p, 1)[uint64_t(row) * D + c0 + col];
+      Z[col * D + row] = v;
+    }
+    __syncthreads();
+    for (int i = 0; i < D; ++i) {              // forward: L z' = r
+      double s = 0.0;
+      for (int k = q; k < i; k += 16) s += Lm[i * D + k] * Z[cc * D + k];
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 16);
+      if (q == 0) Z[cc * D + i] = (Z[cc * D + i] - s) / Lm[i * D + i];
+      __syncthreads();
+    }
+    for (int i = D - 1; i >= 0; --i) {         // backward: L^T z = z'
+      double s = 0.0;
+      for (int k = i + 1 + q; k < D; k += 16) s += Lm[k * D + i] * Z[cc * D + k];
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 16);
+      if (q == 0) Z[cc * D + i] = (Z[cc * D + i] - s) / Lm[i * D + i];
+      __syncthreads();
+    }
+    uint16_t *bo = a.b_out + (uint64_t(kv) * a.H + h) * DD;
+    for (int e = tid; e < 16 * D; e += 256) {
+      const int col = e / D, j = e % D;
+      bo[uint64_t(c0 + col) * D + j] = f64_to_bf16_bits(Z[col * D + j]);
+    }
+    __syncthreads();
   }
 }
 
@@ -1991,10 +2133,17 @@ void launch_attend(const AttnArgs &a, hipStream_t st) {
   if (a.max_segments > 1)
     hipLaunchKernelGGL(k_attend_merge, dim3(cdiv(int64_t(a.n_q) * (a.L.D / 4), 256), a.L.H), dim3(256), 0, st, a);
 }
+void launch_xl_refit(const RefitArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL(k_xl_gram, dim3(kRefitParts, a.H, 4), dim3(256), 0, st, a);
+  const size_t lds = (size_t(a.D) * a.D + 16 * size_t(a.D)) * sizeof(double);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_xl_solve),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  hipLaunchKernelGGL(k_xl_solve, dim3(a.H, 2), dim3(256), lds, st, a);
+}
 void launch_xl_predict(const XlArgs &a, int kv0, int n_kv, hipStream_t st) {
   // tiled kernels (fp32 LDS staging of the bf16 operands)
   const int TT = 4 * (256 / xl_project_groups(a.r));
-  hipLaunchKernelGGL(k_xl_project, dim3(cdiv(a.n, TT), n_kv), dim3(256), 0, st, a, kv0);
+  if (!a.skip_project) hipLaunchKernelGGL(k_xl_project, dim3(cdiv(a.n, TT), n_kv), dim3(256), 0, st, a, kv0);
   const int RP = (a.r + 7) & ~7;
   const int IG = a.D / 8, TTp = 4 * (256 / IG);
   const size_t lds = size_t(a.D * a.D + RP * a.D + a.D * TTp + RP * TTp) * 2;

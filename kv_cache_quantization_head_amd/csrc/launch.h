@@ -18,6 +18,7 @@ void launch_attend(const AttnArgs &a, hipStream_t st);
 void launch_attend_fresh(const AttnArgs &a, hipStream_t st);
 void launch_attend_merge2(const MergeArgs &m, hipStream_t st);
 void launch_xl_predict(const XlArgs &a, int kv0, int n_kv, hipStream_t st);
+void launch_xl_refit(const RefitArgs &a, hipStream_t st);
 void launch_set_header(uint8_t *arena, const DevLayout &L, int layer0, int n_layers, int n_chunks,
                        int n_tokens, hipStream_t st);
 

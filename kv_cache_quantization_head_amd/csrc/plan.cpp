@@ -28,6 +28,7 @@ int make_plan(const qkv_config *cfg, Plan *plan) {
   if (c.max_query_tokens < 0 || c.max_query_tokens >= (int64_t(1) << 31)) return QKV_E_INVAL;
   if (c.xlayer != 0 && c.xlayer != 1) return QKV_E_INVAL;
   if (c.codebook_reuse != 0 && c.codebook_reuse != 1) return QKV_E_INVAL;
+  if (c.xlayer_adapt != 0 && (c.xlayer_adapt != 1 || !c.xlayer)) return QKV_E_INVAL;
   if (c.xlayer) {
     if (c.xlayer_rank < 1 || c.xlayer_rank > 64) return QKV_E_INVAL;
     if (c.kv_dtype != QKV_BF16) return QKV_E_INVAL;
@@ -77,7 +78,10 @@ int make_plan(const qkv_config *cfg, Plan *plan) {
   s.bytes = off;
 
   p.streams_bytes = 2 * uint64_t(c.n_layers) * s.bytes;
-  p.scratch_off = p.streams_bytes;
+  // re-fitted predictor blocks (adapted cross-layer mode), kept between calls
+  p.xl_refit_off = p.streams_bytes;
+  const uint64_t refit_bytes = c.xlayer_adapt ? align_up(uint64_t(c.n_layers) * 2 * H * d * d * 2) : 0;
+  p.scratch_off = p.streams_bytes + refit_bytes;
   uint64_t attn = 0;
   if (c.max_query_tokens > 0) {
     const uint64_t Q = c.max_query_tokens;
@@ -101,7 +105,10 @@ int make_plan(const qkv_config *cfg, Plan *plan) {
   const uint64_t units = C <= uint64_t(kSortMaxClusters) ? 2 * uint64_t(c.n_layers) * H * p.sort_tiles : 0;
   p.sort_perm_off = xl;
   p.sort_off_off = align_up(p.sort_perm_off + units * 256);
-  const uint64_t enc = align_up(p.sort_off_off + units * (C + 1) * 2);
+  uint64_t enc = align_up(p.sort_off_off + units * (C + 1) * 2);
+  // re-fit sums: [parts][2 kv][2 matrices][H][d][d] fp64 (adapted mode)
+  p.xl_gram_off = enc;
+  if (c.xlayer_adapt) enc = align_up(enc + uint64_t(kRefitParts) * 4 * H * d * d * 8);
   p.scratch_bytes = std::max(attn, enc);
   p.total_bytes = p.scratch_off + p.scratch_bytes;
   *plan = p;

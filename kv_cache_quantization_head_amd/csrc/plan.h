@@ -14,6 +14,7 @@ namespace qkv {
 
 constexpr int kMaxChunks = 256;      // snapshot slots per stream (header size)
 constexpr int kMaxSplits = 8;        // split-KV partitions of one attention call
+constexpr int kRefitParts = 8;       // adapted-predictor re-fit: token ranges summed apart, then in order
 constexpr int kSortMaxClusters = 4096;  // k-means update through per-tile sorts up to this C
 constexpr uint64_t kAlign = 256;
 
@@ -47,6 +48,8 @@ struct Plan {
   uint64_t scratch_off, scratch_bytes;
   uint64_t attn_part_o_off, attn_part_lse_off;     // relative to scratch
   uint64_t xl_pred_off, xl_chain_off, xl_proj_off; // relative to scratch
+  uint64_t xl_refit_off;                           // absolute: [L][2][H][d][d] bf16 (adapted mode)
+  uint64_t xl_gram_off;                            // relative to scratch (adapted mode re-fit)
   uint64_t sort_perm_off, sort_off_off;            // relative to scratch (encode)
   uint64_t sort_tiles;                             // 256-token tiles per call, max
   uint64_t total_bytes;

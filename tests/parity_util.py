@@ -12,11 +12,13 @@ import kv_cache_quantization_head_amd as qkv
 
 
 def make_codec(H, d, C, S, bits, G, iters=5, max_tokens=4096, max_chunks=4, dtype="bf16",
-               max_q=256, n_layers=1, max_chunk_tokens=0, xlayer=0, rank=0, predictor=None, reuse=0):
+               max_q=256, n_layers=1, max_chunk_tokens=0, xlayer=0, rank=0, predictor=None, reuse=0,
+               adapt=0):
     cfg = qkv.config(n_layers, H, d, C, S, bits, G, kmeans_iters=iters, max_tokens=max_tokens,
                      max_chunk_tokens=max_chunk_tokens, max_chunks=max_chunks,
                      kv_dtype=qkv.QKV_BF16 if dtype == "bf16" else qkv.QKV_F32,
-                     max_query_tokens=max_q, xlayer=xlayer, xlayer_rank=rank, codebook_reuse=reuse)
+                     max_query_tokens=max_q, xlayer=xlayer, xlayer_rank=rank, codebook_reuse=reuse,
+                     xlayer_adapt=adapt)
     return qkv.Codec(cfg, device="cuda", predictor=predictor)
 
 

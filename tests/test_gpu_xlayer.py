@@ -58,3 +58,58 @@ def test_cross_layer_chain(G, S, bits):
         # a later window through the chain: layers 1..2 only, tokens [50, 250)
         part = codec.reconstruct(1, 2, kv, 50, 250).cpu().numpy()
         np.testing.assert_array_equal(f32_bits(part), f32_bits(rec[1:, :, 50:250]))
+
+
+def _bf16_step(v):
+    """Spacing of bf16 values around v (v a bf16 value, not zero)."""
+    e = np.floor(np.log2(np.abs(v)))
+    return 2.0 ** (e - 7)
+
+
+def test_adapted_predictor_refit_and_chain():
+    """Adapted mode: the blocks of layers 1 and 2 are re-fitted on the first
+    call's tokens (600), then used for that call and the next (200).  The
+    re-fitted bf16 blocks equal the oracle's (the fp64 solves differ only in
+    rounding order: a block element may differ by one bf16 step only where
+    the fp64 value sits on a rounding midpoint to 1e-8); given the device's
+    blocks, codes and reconstructions of every layer are bit-exact."""
+    L, H, r, C, S, bits, G = 3, 4, 8, 16, 2, 2, 64
+    n1, n2 = 600, 200
+    n = n1 + n2
+    cfgs = synth.scaled(synth.WIDE_HEAD, n_layers=L, n_heads=H, tokens=n, n_clusters=C,
+                        n_stages=S, bits=bits, group=G, xlayer_rank=r)
+    blob = _predictor_blob(cfgs, L, r)
+    codec = make_codec(H, 128, C, S, bits, G, max_tokens=n, max_chunks=2, n_layers=L, max_q=0,
+                       xlayer=1, rank=r, predictor=blob.to(DEV), adapt=1)
+    xs = {kv: torch.stack([synth.kv_tokens(cfgs, l, kv, 0, n) for l in range(L)]) for kv in (0, 1)}
+    print(f"adapted xlayer: {L} layers, calls of {n1} and {n2} tokens", flush=True)
+    codec.encode_chunk(xs[0][:, :, :n1].contiguous().to(DEV), xs[1][:, :, :n1].contiguous().to(DEV))
+    codec.encode_chunk(xs[0][:, :, n1:].contiguous().to(DEV), xs[1][:, :, n1:].contiguous().to(DEV))
+    torch.cuda.synchronize()
+    blocks = {l: codec.adapted_blocks(l).float().cpu().numpy() for l in range(1, L)}
+    for kv in (0, 1):
+        rec = codec.reconstruct(0, L, kv, 0, n).cpu().numpy()
+        o0 = oracle_stream(H, 128, C, 5, S, bits, G, "bf16")
+        o0.encode(xs[kv][0, :, :n1].float().numpy())
+        o0.encode(xs[kv][0, :, n1:].float().numpy())
+        assert_stream_equal(codec, 0, kv, o0)
+        prev = o0.xhat()
+        for l in range(1, L):
+            _, U, V = synth.predictor(cfgs, l - 1, kv, rank=r)
+            U, V = U.float().numpy(), V.float().numpy()
+            x_l = xs[kv][l].float().numpy()
+            Bfit, Bb = o_xlayer.refit_block(prev[:, :n1], x_l[:, :n1], U, V)
+            dev_b = blocks[l][kv]
+            bad = np.argwhere(dev_b != Bb)
+            assert len(bad) <= dev_b.size // 1000, f"layer {l} kv {kv}: {len(bad)} block elements differ"
+            for h, i, j in bad:
+                g, o, f = dev_b[h, i, j], Bb[h, i, j], Bfit[h, i, j]
+                assert abs(g - o) == _bf16_step(max(abs(g), abs(o)))
+                assert abs(f - (g + o) / 2) <= 1e-8 * abs(f)
+            pred = o_xlayer.predict(prev, dev_b, U, V)
+            ol = oracle_stream(H, 128, C, 5, S, bits, G, "bf16")
+            ol.encode_residual(x_l[:, :n1], pred[:, :n1])
+            ol.encode_residual(x_l[:, n1:], pred[:, n1:])
+            assert_stream_equal(codec, l, kv, ol, check_ids=False)
+            np.testing.assert_array_equal(f32_bits(rec[l]), f32_bits(ol.xhat()), err_msg=f"layer {l} kv {kv}")
+            prev = ol.xhat()

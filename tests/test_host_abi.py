@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     L = qkv.lib()
     names = _declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
     assert "qkv_encode_chunk" in names and "qkv_attend" in names
@@ -64,7 +64,7 @@ def test_workspace_bytes_matches_layout_closed_form():
     ("n_stages", 0), ("n_stages", 5), ("bits", 3), ("group_size", 16), ("group_size", 128),
     ("kmeans_iters", -1), ("max_tokens", 0), ("max_tokens", 1 << 31), ("max_chunks", 0),
     ("max_chunks", 257), ("kv_dtype", 7), ("max_chunk_tokens", 40000), ("xlayer", 2),
-    ("codebook_reuse", 2),
+    ("codebook_reuse", 2), ("xlayer_adapt", 1),
 ])
 def test_invalid_config_rejected(field, value):
     cfg = _cfg(**{field: value})
@@ -209,3 +209,25 @@ def test_codebook_reuse_keeps_one_snapshot():
     assert qkv.lib().qkv_layout(c, 1, 1, ctypes.byref(d_)) == B.QKV_OK
     assert d_.codebook_chunk_stride == 0 and d_.cnorm_chunk_stride == 0
     qkv.lib().qkv_destroy(c)
+
+
+def test_adapted_mode_layout_and_readback():
+    """xlayer_adapt needs the cross-layer mode; its re-fitted blocks live in
+    the arena between the streams and the scratch region."""
+    assert qkv.workspace_bytes(_cfg(xlayer_adapt=1)) == 0
+    plain, adapted = _cfg(xlayer=1, xlayer_rank=8), _cfg(xlayer=1, xlayer_rank=8, xlayer_adapt=1)
+    assert qkv.workspace_bytes(adapted) > qkv.workspace_bytes(plain) + 2 * 2 * 12 * 128 * 128 * 2
+    rc, c = _init(adapted, predictor=FAKE)
+    assert rc == B.QKV_OK
+    L = qkv.lib()
+    off1, off0 = ctypes.c_uint64(), ctypes.c_uint64()
+    assert L.qkv_adapted_blocks(c, 1, ctypes.byref(off1)) == B.QKV_OK
+    assert L.qkv_adapted_blocks(c, 0, ctypes.byref(off0)) == B.QKV_E_INVAL
+    assert L.qkv_adapted_blocks(c, 2, ctypes.byref(off0)) == B.QKV_E_INVAL
+    d = B.qkv_layout_desc()
+    assert L.qkv_layout(c, 1, 1, ctypes.byref(d)) == B.QKV_OK
+    assert off1.value % 256 >= 0 and off1.value > d.cnorm_off
+    L.qkv_destroy(c)
+    rc, c = _init(plain, predictor=FAKE)
+    assert L.qkv_adapted_blocks(c, 1, ctypes.byref(off1)) == B.QKV_E_INVAL
+    L.qkv_destroy(c)
