@@ -131,21 +131,27 @@ def xlayer_main(args):
     cfg = qkv.config(2, H, d, C, cfgs.n_stages, cfgs.bits, cfgs.group, kmeans_iters=cfgs.iters,
                      max_tokens=T, max_chunks=1, kv_dtype=qkv.QKV_BF16, max_query_tokens=0, xlayer=1,
                      xlayer_rank=r)
-    codec = qkv.Codec(cfg, device=dev, predictor=torch.cat(parts).to(dev))
+    blob = torch.cat(parts).to(dev)
+    codec = qkv.Codec(cfg, device=dev, predictor=blob)
+    cfg_a = qkv.config(2, H, d, C, cfgs.n_stages, cfgs.bits, cfgs.group, kmeans_iters=cfgs.iters,
+                       max_tokens=T, max_chunks=1, kv_dtype=qkv.QKV_BF16, max_query_tokens=0, xlayer=1,
+                       xlayer_rank=r, xlayer_adapt=1)
+    codec_a = qkv.Codec(cfg_a, device=dev, predictor=blob)
     ks = torch.stack([synth.kv_tokens(cfgs, l, 0, 0, T, device=dev) for l in range(2)])
     vs = torch.stack([synth.kv_tokens(cfgs, l, 1, 0, T, device=dev) for l in range(2)])
-    ev = []
+    ev, ev_a = [], []
 
     def step(record):
-        codec.rewind(0, 2, 0)
-        m = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        m[0].record()
-        codec.encode_chunk(ks[:1], vs[:1], layer0=0)
-        m[1].record()
-        codec.encode_chunk(ks[1:], vs[1:], layer0=1)
-        m[2].record()
-        if record:
-            ev.append(m)
+        for c, sink in ((codec, ev), (codec_a, ev_a)):
+            c.rewind(0, 2, 0)
+            m = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            m[0].record()
+            c.encode_chunk(ks[:1], vs[:1], layer0=0)
+            m[1].record()
+            c.encode_chunk(ks[1:], vs[1:], layer0=1)
+            m[2].record()
+            if record:
+                sink.append(m)
 
     for _ in range(args.warmup):
         step(False)
@@ -155,13 +161,25 @@ def xlayer_main(args):
     torch.cuda.synchronize()
     sas = sum(m[0].elapsed_time(m[1]) for m in ev) / len(ev)
     xl = sum(m[1].elapsed_time(m[2]) for m in ev) / len(ev)
+    xl_a = sum(m[1].elapsed_time(m[2]) for m in ev_a) / len(ev_a)
+
+    def layer1_error(c):
+        err = []
+        for kv, x in ((0, ks[1]), (1, vs[1])):
+            xf = x.float()
+            rec = c.reconstruct(1, 1, kv, 0, T)[0]
+            err.append(round(float(((rec - xf) ** 2).sum() / (xf ** 2).sum()), 6))
+            del rec
+        return err
     print(json.dumps({
         "metric": "cross-layer encode of one layer (K and V)", "value": round(xl, 4), "unit": "ms",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
         "dtype": "bf16 in, fp64 prediction", "data": "synthetic (seeded prototype/drift/outlier generator)",
         "config": {"workload": "wide_head layer: K,V bf16 [40, 62400, 128], C=512, 2-stage INT2 G=64, "
                                "cross-layer rank 32", "heads": H, "tokens": T, "rank": r},
-        "sas_layer_ms": round(sas, 4)}), flush=True)
+        "sas_layer_ms": round(sas, 4), "layer1_rel_sq_error_kv": layer1_error(codec),
+        "adapted_layer_ms_with_refit": round(xl_a, 4),
+        "adapted_layer1_rel_sq_error_kv": layer1_error(codec_a)}), flush=True)
 
 
 def fresh_main(args):

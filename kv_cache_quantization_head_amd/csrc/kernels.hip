@@ -1873,18 +1873,41 @@ __global__ __launch_bounds__(256) void k_xl_gram(RefitArgs a) {
     for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
   for (int64_t c0 = t_beg; c0 < t_end; c0 += RF_TC) {
     const int nc = int(min<int64_t>(RF_TC, t_end - c0));
-    __syncthreads();
-    for (int e = tid; e < RF_TC * D; e += 256) {
-      const int tt = e / D, j = e % D;
-      float yv = 0.0f;
-      double zv = 0.0;
-      if (tt < nc) {
+    // eight channels per thread and step, every load of the chunk issued
+    // before any is used (past the range: zeros)
+    constexpr int NU = RF_TC * 128 / 8 / 256;
+    uint4 yv[NU], xv[NU];
+    float4 lv[NU][2];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int e8 = tid + 256 * u, tt = e8 / (D / 8), j = 8 * (e8 % (D / 8));
+      yv[u] = xv[u] = make_uint4(0, 0, 0, 0);
+      lv[u][0] = lv[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (tt < nc && e8 < RF_TC * D / 8) {
         const uint64_t off = uint64_t(c0 + tt) * D + j;
-        yv = bf16_to_f32(y[off]);
-        zv = mat == 0 ? double(yv) : double(bf16_to_f32(x[off])) - double(lr[off]);
+        yv[u] = *(const uint4 *)(y + off);
+        if (mat) {
+          xv[u] = *(const uint4 *)(x + off);
+          lv[u][0] = *(const float4 *)(lr + off);
+          lv[u][1] = *(const float4 *)(lr + off + 4);
+        }
       }
-      ys[tt][j] = yv;
-      zs[tt][j] = zv;
+    }
+    __syncthreads();                          // previous chunk consumed
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int e8 = tid + 256 * u, tt = e8 / (D / 8), j = 8 * (e8 % (D / 8));
+      if (e8 >= RF_TC * D / 8) continue;
+      const uint32_t yw[4] = {yv[u].x, yv[u].y, yv[u].z, yv[u].w}, xw[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+      const float lf[8] = {lv[u][0].x, lv[u][0].y, lv[u][0].z, lv[u][0].w,
+                           lv[u][1].x, lv[u][1].y, lv[u][1].z, lv[u][1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float yf = __uint_as_float((e & 1) ? (yw[e >> 1] & 0xffff0000u) : (yw[e >> 1] << 16));
+        const float xf = __uint_as_float((e & 1) ? (xw[e >> 1] & 0xffff0000u) : (xw[e >> 1] << 16));
+        ys[tt][j + e] = yf;
+        zs[tt][j + e] = mat == 0 ? double(yf) : double(xf) - double(lf[e]);
+      }
     }
     __syncthreads();
     if (active) {
