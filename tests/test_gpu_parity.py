@@ -312,3 +312,20 @@ def test_codebook_reuse_matches_oracle(dtype):
         o = oracle_stream(2, 128, 64, it, S, b, 32, dtype, reuse=True)
         o.encode(x.float().numpy())
         assert_stream_equal(codec, 0, kv, o)
+
+
+def test_attend_with_fresh_chunk_d64_fp32_queries():
+    """The fresh-chunk read at d = 64 with fp32 queries, a 3-chunk cache
+    (several codebook snapshots) and a ragged fresh chunk."""
+    cfgs = synth.scaled(synth.WAN_LAYER, n_heads=3, head_dim=64, n_clusters=32, group=32, tokens=2600,
+                        q_dtype="f32")
+    codec, ost, _ = _encode_and_oracle(cfgs, [700, 900, 400], "bf16", max_q=300)
+    kn = synth.kv_tokens(cfgs, 0, 0, 2000, 333)
+    vn = synth.kv_tokens(cfgs, 0, 1, 2000, 333)
+    q = synth.queries(cfgs, 0, 199)
+    assert q.dtype == torch.float32
+    out, lse = codec.attend_with_chunk(0, q.to(DEV), kn.to(DEV), vn.to(DEV), out_dtype=torch.bfloat16)
+    khat = np.concatenate([ost[0].xhat(), kn.float().numpy()], axis=1)
+    vhat = np.concatenate([ost[1].xhat(), vn.float().numpy()], axis=1)
+    o_ref, lse_ref = o_attend.attend(q.numpy(), khat, vhat)
+    attention_tolerance_check(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
