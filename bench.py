@@ -40,6 +40,8 @@ def parse():
                          "layers (attention over the packed cache plus the chunk's fresh bf16 K/V for "
                          "every denoising step and layer, then the chunk's encode)")
     ap.add_argument("--denoise", type=int, default=4, help="denoising steps per chunk (--fresh)")
+    ap.add_argument("--layers", type=int, default=4,
+                    help="layers of the model (--fresh; Wan2.1-1.3B has 30)")
     ap.add_argument("--reuse", action="store_true",
                     help="instead of the default step: encode a long-rollout layer (187200 tokens in 40 "
                          "calls) with codebook reuse and with per-call snapshots; time, reconstruction "
@@ -184,7 +186,7 @@ def xlayer_main(args):
 
 def fresh_main(args):
     """The read as a generating model issues it, on the wan_layer shape with
-    4 layers: for each new 4680-token chunk, --denoise denoising steps each
+    --layers layers (4 by default): for each new 4680-token chunk, --denoise denoising steps each
     attend every layer's 4680 queries over its packed 32760-token cache plus
     the chunk's fresh bf16 K/V (qkv_attend_with_chunk), then the chunk is
     encoded into every layer's cache.  A step is one chunk; the cache is
@@ -195,7 +197,7 @@ def fresh_main(args):
     import synth
 
     dev = torch.device("cuda:0")
-    L = 4
+    L = args.layers
     cfgs = synth.scaled(synth.WAN_LAYER, n_layers=L)
     H, T, d, Tq, n_new = cfgs.n_heads, cfgs.tokens, cfgs.head_dim, cfgs.q_tokens, cfgs.q_tokens
     cfg = qkv.config(L, H, d, cfgs.n_clusters, cfgs.n_stages, cfgs.bits, cfgs.group, kmeans_iters=cfgs.iters,
