@@ -329,3 +329,22 @@ def test_attend_with_fresh_chunk_d64_fp32_queries():
     vhat = np.concatenate([ost[1].xhat(), vn.float().numpy()], axis=1)
     o_ref, lse_ref = o_attend.attend(q.numpy(), khat, vhat)
     attention_tolerance_check(out.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("index,dtype", [(101, "bf16"), (102, "bf16"), (103, "f32")])
+def test_other_seeds_bit_exact(index, dtype):
+    """The bit-exact bar on data drawn from other seeds (a wan_layer-shaped
+    stream with 2 heads, two warm-started calls; one fp32 cache that takes
+    the non-MFMA assignment)."""
+    base = synth.WAN_LAYER if dtype == "bf16" else synth.scaled(synth.TINY, per_token_labels=False, drift=0.02)
+    cfgs = synth.scaled(base, index=index, n_heads=2, head_dim=128, n_clusters=256, group=32, tokens=8000)
+    _say(f"seed index {index} ({dtype}): 2 heads x (5000 + 3000) tokens")
+    codec, ost, _ = _encode_and_oracle(cfgs, [5000, 3000], dtype, max_q=128)
+    for kv in (0, 1):
+        assert_stream_equal(codec, 0, kv, ost[kv])
+        rec = codec.reconstruct(0, 1, kv, 0, 8000)[0].cpu().numpy()
+        np.testing.assert_array_equal(f32_bits(rec), f32_bits(ost[kv].xhat()))
+    q = synth.queries(synth.scaled(cfgs, q_dtype=dtype), 0, 128)
+    out, lse = codec.attend(0, q.to(DEV))
+    o_ref, lse_ref = o_attend.attend(q.float().numpy(), ost[0].xhat(), ost[1].xhat())
+    attention_tolerance_check(out.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
