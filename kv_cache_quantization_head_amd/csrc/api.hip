@@ -45,6 +45,18 @@ extern "C" int qkv_init(const qkv_config *cfg, void *d_arena, size_t arena_bytes
   return QKV_OK;
 }
 
+// compute units of the current device, looked up once per context (the
+// attention's work split deals one run per compute unit)
+static void ensure_cu_count(qkv_ctx *ctx) {
+  if (ctx->n_cu > 0) return;
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n_cu > 0)
+    ctx->n_cu = n_cu;
+  else
+    ctx->n_cu = 256;
+}
+
 // re-fitted blocks of the transition into layer l (adapted cross-layer mode)
 static uint16_t *refit_blocks(qkv_ctx *ctx, int l) {
   const qkv_config &c = ctx->plan.cfg;
@@ -182,14 +194,7 @@ extern "C" int qkv_attend(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Plan &p = ctx->plan;
   const int64_t n_keys = ctx->layers[layer].n_tokens;
-  if (ctx->n_cu <= 0) {
-    int dev = 0, n_cu = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n_cu > 0)
-      ctx->n_cu = n_cu;
-    else
-      ctx->n_cu = 256;
-  }
+  ensure_cu_count(ctx);
   const AttnSplit w = attention_split(p, n_keys, n_q, ctx->n_cu);
 
   AttnArgs a{};
@@ -227,14 +232,7 @@ extern "C" int qkv_attend_with_chunk(qkv_ctx *ctx, int32_t layer, const void *d_
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Plan &p = ctx->plan;
   const qkv_config &c = p.cfg;
-  if (ctx->n_cu <= 0) {
-    int dev = 0, n_cu = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n_cu > 0)
-      ctx->n_cu = n_cu;
-    else
-      ctx->n_cu = 256;
-  }
+  ensure_cu_count(ctx);
   // Each part may split a query block over at most kMaxSplits - 2 blocks;
   // the last two partial slots hold the two complete parts for the merge.
   const uint64_t HQ = uint64_t(c.n_heads) * uint64_t(n_q);
