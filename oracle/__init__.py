@@ -21,6 +21,10 @@ Sources, cited by page title and section throughout:
   Portuguese copy /pt/news/13833), section on cross-layer prediction: predict
   the next layer's K/V from one layer's cache with a block-diagonal plus
   low-rank ("block-DPLR") matrix and quantize only the prediction residual.
+* "Q-ARVD: Quantizing Autoregressive Video Diffusion Models" (explainer,
+  gist.science), section on outlier-aware adaptive dual-scale quantization:
+  channels whose L2 norm a MAD-based modified z-score flags get a quantizer
+  of their own (stated for weights; carried over to the KV residual).
 * "KV Cache Quantization for Self-Forcing Video Generation: A 33-Method
   Empirical Study" (abstract, fugumt.com/fugumt/paper_check/2603.27469v1):
   reconstructing BF16 buffers during attention defeats the compression.
@@ -36,6 +40,7 @@ Modules:
   prq       -- progressive residual stages, bit packing, reconstruction
   attend    -- attention over the reconstructed cache (fp64)
   xlayer    -- cross-layer block-diagonal + low-rank prediction
+  outlier   -- outlier-channel flags and the dual-scale stages
   stream    -- one (layer, K|V) stream encoded chunk by chunk
   bits      -- closed-form storage cost per element
 

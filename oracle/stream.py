@@ -15,16 +15,20 @@ Codebook reuse (the other reading of centroid caching, "Sommario tecnico"
 3, offered as an option): only a stream's first call runs the k-means; a
 later call assigns its tokens to that first codebook, with no iterations,
 and keeps it as its snapshot.
+
+Outlier channels (option, see ``outlier``): a call flags the channels of
+each head whose residual norm stands out and codes them as one extra group
+per token and stage; the flags are kept with the call's snapshot.
 """
 import numpy as np
 
-from . import prq, sas
+from . import outlier, prq, sas
 
 
 class Chunk:
     """Encoded content of one call for one head: what the decoder needs."""
 
-    def __init__(self, ids, codebook, packed, sigmas, zs, base, xhat, r_final, rhats):
+    def __init__(self, ids, codebook, packed, sigmas, zs, base, xhat, r_final, rhats, flags=None):
         self.ids = ids            # [n] cluster ids (None in cross-layer mode)
         self.codebook = codebook  # [C, d] snapshot (None in cross-layer mode)
         self.packed = packed      # S x [n, d*b/8] uint8
@@ -34,17 +38,24 @@ class Chunk:
         self.xhat = xhat          # [n, d] fp32 reconstruction
         self.r_final = r_final    # [n, d] fp32 residual after the last stage
         self.rhats = rhats        # S x [n, d] fp32 dequantized stages
+        self.flags = flags        # [d] bool outlier channels of the call (None: option off)
 
 
-def encode_head(x, n_clusters, iters, n_stages, bits, group, dtype, init=None):
-    """Encode one head's new tokens x [n, d] with SAS + PRQ."""
+def encode_head(x, n_clusters, iters, n_stages, bits, group, dtype, init=None, outliers=False):
+    """Encode one head's new tokens x [n, d] with SAS + PRQ (optionally with
+    the outlier-channel group)."""
     ids, cb = sas.kmeans(x, n_clusters, iters, dtype, init=init)
     base = cb[ids]
     r0 = sas.centroid_residual(x, cb, ids)
-    codes, sig, zs, rhats, r_fin = prq.quantize(r0, n_stages, bits, group)
+    flags = None
+    if outliers:
+        flags = outlier.channel_flags(r0)
+        codes, sig, zs, rhats, r_fin = outlier.quantize_dual(r0, n_stages, bits, group, flags)
+    else:
+        codes, sig, zs, rhats, r_fin = prq.quantize(r0, n_stages, bits, group)
     packed = [prq.pack(q, bits) for q in codes]
     xhat = prq.reconstruct(base, rhats)
-    return Chunk(ids, cb, packed, sig, zs, base, xhat, r_fin, rhats)
+    return Chunk(ids, cb, packed, sig, zs, base, xhat, r_fin, rhats, flags)
 
 
 def encode_residual_head(x, pred, n_stages, bits, group):
@@ -59,12 +70,14 @@ def encode_residual_head(x, pred, n_stages, bits, group):
 class Stream:
     """Cache stream of one layer and tensor: all heads, all chunks so far."""
 
-    def __init__(self, n_heads, head_dim, n_clusters, iters, n_stages, bits, group, dtype, reuse=False):
+    def __init__(self, n_heads, head_dim, n_clusters, iters, n_stages, bits, group, dtype, reuse=False,
+                 outliers=False):
         self.H, self.d = n_heads, head_dim
         self.C, self.iters = n_clusters, iters
         self.S, self.b, self.G = n_stages, bits, group
         self.dtype = dtype
         self.reuse = reuse
+        self.outliers = outliers
         self.chunks = []          # list of per-head Chunk lists
         self.starts = []          # first token of each chunk
 
@@ -81,7 +94,7 @@ class Stream:
             init = None if prev is None else prev[h].codebook
             iters = 0 if (self.reuse and prev is not None) else self.iters
             per_head.append(encode_head(x[h], self.C, iters, self.S, self.b,
-                                        self.G, self.dtype, init=init))
+                                        self.G, self.dtype, init=init, outliers=self.outliers))
         self.starts.append(self.n_tokens)
         self.chunks.append(per_head)
         return per_head
