@@ -106,16 +106,29 @@ typedef struct {
                               the low-rank term fixed, fp64, rounded to bf16), and uses the
                               re-fitted blocks for that and every later call and for
                               decoding (Coral-KV's adapted configuration) */
+  int32_t outlier_channels;/* 0: plain groups; 1: every encode call flags, per head, the
+                              channels whose residual L2 norm stands out (modified z-score
+                              on the median absolute deviation: 0.6745 (n_j - med) > 3.5 MAD,
+                              and n_j > 2 med, medians over the d channels) and quantizes
+                              them as one extra group per token and stage with its own
+                              fp16 (sigma, z); the normal groups leave them out (Q-ARVD
+                              explainer, outlier-aware adaptive dual-scale quantization,
+                              carried over from weights to the KV residual).  SAS mode only
+                              (xlayer = 0) */
 } qkv_config;
 
 /* Offsets (bytes from the arena base) and strides of one (layer, K|V) stream,
  * for read-back and tests.  Layouts:
  *   codes    u8  [S][H][max_tokens][d*bits/8]  element j of a token at byte
  *                j*bits/8, bit (j*bits)%8 (least significant first)
- *   meta     u16 [S][H][max_tokens][d/G][2]    fp16 bit patterns (sigma, z)
+ *   meta     u16 [S][H][max_tokens][d/G][2]    fp16 bit patterns (sigma, z); with
+ *                outlier_channels = 1 [d/G + 1][2], the last entry the outlier group's
+ *                ((0, 0) when a group has no channel)
  *   ids      u8|u16 [H][max_tokens]            cluster id of each token
  *   codebook kv_dtype [max_chunks][H][C][d]    snapshot of each encode call
  *   cnorm    f32 [max_chunks][H][C]            ||c||^2 of each snapshot row
+ *   chmask   u32 [max_chunks][H][d/32]         outlier channels of each call (bit j%32
+ *                of word j/32 = channel j); only with outlier_channels = 1
  * The codebook of a token is the snapshot of the chunk that encoded it.  With
  * codebook_reuse = 1 there is one snapshot ([1][H][C][d], [1][H][C]) and the
  * chunk strides are 0. */
@@ -128,6 +141,7 @@ typedef struct {
   int64_t n_tokens;        /* tokens encoded so far in this layer */
   int32_t n_chunks;        /* encode calls so far in this layer */
   int32_t reserved;
+  uint64_t chmask_off, chmask_chunk_stride, chmask_head_stride;  /* 0 when outlier_channels = 0 */
 } qkv_layout_desc;
 
 /* Device bytes the arena must provide for `cfg` (0 if cfg is invalid). */

@@ -28,7 +28,7 @@ class qkv_config(ctypes.Structure):
                 ("max_chunks", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
                 ("max_query_tokens", ctypes.c_int64), ("xlayer", ctypes.c_int32),
                 ("xlayer_rank", ctypes.c_int32), ("codebook_reuse", ctypes.c_int32),
-                ("xlayer_adapt", ctypes.c_int32)]
+                ("xlayer_adapt", ctypes.c_int32), ("outlier_channels", ctypes.c_int32)]
 
 
 class qkv_layout_desc(ctypes.Structure):
@@ -38,7 +38,8 @@ class qkv_layout_desc(ctypes.Structure):
         "ids_off", "ids_head_stride", "id_bytes",
         "codebook_off", "codebook_chunk_stride", "codebook_head_stride",
         "cnorm_off", "cnorm_chunk_stride", "cnorm_head_stride")] + [
-        ("n_tokens", ctypes.c_int64), ("n_chunks", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+        ("n_tokens", ctypes.c_int64), ("n_chunks", ctypes.c_int32), ("reserved", ctypes.c_int32)] + [
+        (n, ctypes.c_uint64) for n in ("chmask_off", "chmask_chunk_stride", "chmask_head_stride")]
 
 
 _lib = None
@@ -99,10 +100,12 @@ def status_string(status, ctx=None):
 
 def config(n_layers, n_heads, head_dim, n_clusters, n_stages, bits, group_size, kmeans_iters=5,
            max_tokens=0, max_chunk_tokens=0, max_chunks=1, kv_dtype=QKV_BF16,
-           max_query_tokens=0, xlayer=0, xlayer_rank=0, codebook_reuse=0, xlayer_adapt=0):
+           max_query_tokens=0, xlayer=0, xlayer_rank=0, codebook_reuse=0, xlayer_adapt=0,
+           outlier_channels=0):
     return qkv_config(n_layers, n_heads, head_dim, n_clusters, n_stages, bits, group_size,
                       kmeans_iters, max_tokens, max_chunk_tokens, max_chunks, kv_dtype,
-                      max_query_tokens, xlayer, xlayer_rank, codebook_reuse, xlayer_adapt)
+                      max_query_tokens, xlayer, xlayer_rank, codebook_reuse, xlayer_adapt,
+                      outlier_channels)
 
 
 def workspace_bytes(cfg):
@@ -255,10 +258,10 @@ class Codec:
         return v[:, :lay["n_tokens"]]
 
     def meta(self, layer, kv, stage):
-        """[H, n_tokens, d/G, 2] uint16 fp16 bit patterns (sigma, z)."""
+        """[H, n_tokens, d/G (+1 with outlier channels), 2] uint16 fp16 bit patterns (sigma, z)."""
         lay = self.layout(layer, kv)
         H, T = self.cfg.n_heads, self.cfg.max_tokens
-        ng = self.cfg.head_dim // self.cfg.group_size
+        ng = lay["meta_token_stride"] // 4
         base = lay["meta_off"] + stage * lay["meta_stage_stride"]
         v = self._view(base, H * T * ng * 4).view(torch.int16).view(H, T, ng, 2)
         return v[:, :lay["n_tokens"]]
@@ -270,6 +273,15 @@ class Codec:
         v = self._view(lay["ids_off"], H * T * nb)
         v = v.view(H, T) if nb == 1 else v.view(torch.int16).view(H, T)
         return v[:, :lay["n_tokens"]]
+
+    def channel_mask(self, layer, kv, chunk):
+        """[H, d/32] int32 outlier-channel flags of one chunk (bit j%32 of word j/32)."""
+        lay = self.layout(layer, kv)
+        if not lay["chmask_off"]:
+            raise ValueError("outlier_channels is off")
+        H, d = self.cfg.n_heads, self.cfg.head_dim
+        base = lay["chmask_off"] + chunk * lay["chmask_chunk_stride"]
+        return self._view(base, H * d // 8).view(torch.int32).view(H, d // 32)
 
     def codebook(self, layer, kv, chunk):
         """[H, C, d] snapshot of one chunk, in the cache dtype."""

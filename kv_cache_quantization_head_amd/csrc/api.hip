@@ -74,19 +74,19 @@ extern "C" int qkv_adapted_blocks(const qkv_ctx *ctx, int32_t layer, uint64_t *o
 
 // SAS + PRQ for the 2*n_layers streams of `a` (k-means loop, then codes).
 // iters < 0: assign to the stream's codebook as it stands (codebook reuse).
+// With outlier channels the call's flags are found between the final
+// assignment and the stages.
 static void enqueue_sas(const EncodeArgs &a, int streams, int iters, hipStream_t st) {
   launch_header(a, streams, st);
-  if (iters < 0) {
-    launch_assign(a, streams, st);
-    launch_quantize(a, streams, st);
-    return;
-  }
-  launch_init(a, streams, st);
-  for (int it = 0; it < iters; ++it) {
-    launch_assign(a, streams, st);
-    launch_update(a, streams, st);
+  if (iters >= 0) {
+    launch_init(a, streams, st);
+    for (int it = 0; it < iters; ++it) {
+      launch_assign(a, streams, st);
+      launch_update(a, streams, st);
+    }
   }
   launch_assign(a, streams, st);
+  if (a.L.mask_off) launch_chan_flags(a, streams, st);
   launch_quantize(a, streams, st);
 }
 
@@ -110,6 +110,7 @@ extern "C" int qkv_encode_chunk(qkv_ctx *ctx, int32_t layer0, int32_t n_layers, 
   a.sort_perm = scratch(ctx, p.sort_perm_off);
   a.sort_off = reinterpret_cast<uint16_t *>(scratch(ctx, p.sort_off_off));
   a.sort_tiles = int32_t(p.sort_tiles);
+  a.chan_part = reinterpret_cast<double *>(scratch(ctx, p.chan_part_off));
   const uint64_t layer_bytes = uint64_t(c.n_heads) * uint64_t(n) * c.head_dim * p.kv_elem_bytes;
   const uint8_t *kin = static_cast<const uint8_t *>(d_k);
   const uint8_t *vin = static_cast<const uint8_t *>(d_v);

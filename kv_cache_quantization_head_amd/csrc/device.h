@@ -16,6 +16,7 @@ struct DevLayout {
   uint64_t ids_off, ids_head;
   uint64_t cb_off, cb_chunk, cb_head, cb_row;
   uint64_t cn_off, cn_chunk, cn_head;
+  uint64_t mask_off, mask_chunk, mask_head;   // outlier channel flags (mask_off 0: option off)
   int32_t H, D, C, S, bits, G, id_bytes, kv_bf16;
 };
 
@@ -31,6 +32,7 @@ inline DevLayout dev_layout(const Plan &p) {
   d.ids_off = s.ids_off; d.ids_head = s.ids_head;
   d.cb_off = s.cb_off; d.cb_chunk = s.cb_chunk; d.cb_head = s.cb_head; d.cb_row = s.cb_row;
   d.cn_off = s.cn_off; d.cn_chunk = s.cn_chunk; d.cn_head = s.cn_head;
+  d.mask_off = s.mask_off; d.mask_chunk = s.mask_chunk; d.mask_head = s.mask_head;
   d.H = p.cfg.n_heads; d.D = p.cfg.head_dim; d.C = p.cfg.n_clusters; d.S = p.cfg.n_stages;
   d.bits = p.cfg.bits; d.G = p.cfg.group_size; d.id_bytes = int32_t(s.id_bytes);
   d.kv_bf16 = p.cfg.kv_dtype == QKV_BF16;
@@ -57,6 +59,7 @@ struct EncodeArgs {
   uint8_t *sort_perm;           // [streams][H][tiles][256] u8 token offsets sorted by (id, t)
   uint16_t *sort_off;           // [streams][H][tiles][C+1] start of each cluster in the tile
   int32_t sort_tiles;           // tile stride of the two arrays
+  double *chan_part;            // outlier flags: [streams][H][kChanParts][D] sums of r^2
 };
 
 struct ReconArgs {

@@ -956,12 +956,130 @@ __global__ __launch_bounds__(256) void k_update_sorted(EncodeArgs a) {
   finalize_centroid<D, BF16>(cb, cn, k, L.C, cnt, acc, lane);
 }
 
+// Outlier channels, step 1: per (stream, head, token range p) the sums over
+// the range's tokens of r^2 for every channel, r = fl32(x - c_id) the
+// residual the stages will code, squared and summed in fp64.  Block = 4
+// waves; a lane holds 8 consecutive channels of one token per step (16-byte
+// loads; a wave covers 64 * 8 / D tokens per step), the waves' and slots'
+// sums are added in a fixed order, so the result does not depend on timing.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_chan_stats(EncodeArgs a) {
+  constexpr int EB = BF16 ? 2 : 4;
+  constexpr int LPT = D / 8;            // lanes per token
+  constexpr int TPW = 64 / LPT;         // tokens per wave step
+  __shared__ double part[4 * TPW][D];
+  const DevLayout &L = a.L;
+  const int p = blockIdx.x, h = blockIdx.y, z = blockIdx.z, lrel = z >> 1, kv = z & 1;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ts = lane / LPT, c0 = (lane % LPT) * 8;
+  const int tb = int(int64_t(a.n) * p / kChanParts), te = int(int64_t(a.n) * (p + 1) / kChanParts);
+  const uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, kv);
+  const uint8_t *xb = (kv ? a.v_in : a.k_in) + (uint64_t(lrel) * L.H + h) * uint64_t(a.n) * (D * EB) + c0 * EB;
+  const uint8_t *ids = st + L.ids_off + uint64_t(h) * L.ids_head;
+  const uint8_t *cb = st + L.cb_off + uint64_t(a.slot) * L.cb_chunk + uint64_t(h) * L.cb_head + c0 * EB;
+  double acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0;
+  for (int t = tb + wave * TPW + ts; t < te; t += 4 * TPW) {
+    const int id = load_id(ids, L.id_bytes, int64_t(a.t0) + t);
+    const uint8_t *xr = xb + uint64_t(t) * (D * EB);
+    const uint8_t *cr = cb + uint64_t(id) * (D * EB);
+    float xv[8], cv[8];
+    if constexpr (BF16) {
+      const uint4 u = *(const uint4 *)xr, c = *(const uint4 *)cr;
+      const uint32_t uw[4] = {u.x, u.y, u.z, u.w}, cw[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xv[2 * i] = __uint_as_float(uw[i] << 16); xv[2 * i + 1] = __uint_as_float(uw[i] & 0xffff0000u);
+        cv[2 * i] = __uint_as_float(cw[i] << 16); cv[2 * i + 1] = __uint_as_float(cw[i] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float4 u = ((const float4 *)xr)[i], c = ((const float4 *)cr)[i];
+        xv[4 * i] = u.x; xv[4 * i + 1] = u.y; xv[4 * i + 2] = u.z; xv[4 * i + 3] = u.w;
+        cv[4 * i] = c.x; cv[4 * i + 1] = c.y; cv[4 * i + 2] = c.z; cv[4 * i + 3] = c.w;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const double r = double(xv[e] - cv[e]);
+      acc[e] = fma(r, r, acc[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[wave * TPW + ts][c0 + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    double sum = 0.0;
+    for (int i = 0; i < 4 * TPW; ++i) sum += part[i][threadIdx.x];
+    a.chan_part[((uint64_t(z) * L.H + h) * kChanParts + p) * D + threadIdx.x] = sum;
+  }
+}
+
+// Outlier channels, step 2: one block of 128 threads per (head, stream);
+// thread j owns channel j.  n_j = sqrt(sum of the ranges' sums, in range
+// order); med and MAD are the means of the two middle values of the sorted
+// norms and of the sorted |n_j - med| (rank sort in LDS, ties by channel).
+// Channel j is flagged when 0.6745 (n_j - med) > 3.5 MAD and n_j > 2 med; the
+// flags are stored as the d-bit mask of this call's slot.
+template <int D>
+__global__ __launch_bounds__(128) void k_chan_flags(EncodeArgs a) {
+  __shared__ double vals[D], sorted[D];
+  __shared__ double stat_s;
+  const DevLayout &L = a.L;
+  const int j = threadIdx.x, h = blockIdx.x, z = blockIdx.y, lrel = z >> 1, kv = z & 1;
+  const bool own = j < D;
+  double nj = 0.0;
+  if (own) {
+    const double *pp = a.chan_part + (uint64_t(z) * L.H + h) * kChanParts * D + j;
+    double sum = 0.0;
+    for (int p = 0; p < kChanParts; ++p) sum += pp[p * D];
+    nj = sqrt(sum);
+    vals[j] = nj;
+  }
+  __syncthreads();
+  auto rank_store = [&](double v) {
+    int rank = 0;
+    for (int i = 0; i < D; ++i) {
+      const double o = vals[i];
+      rank += (o < v) || (o == v && i < j);
+    }
+    sorted[rank] = v;
+  };
+  if (own) rank_store(nj);
+  __syncthreads();
+  if (j == 0) stat_s = (sorted[D / 2 - 1] + sorted[D / 2]) * 0.5;
+  __syncthreads();
+  const double med = stat_s;
+  const double dev = fabs(nj - med);
+  if (own) vals[j] = dev;
+  __syncthreads();
+  if (own) rank_store(dev);
+  __syncthreads();
+  if (j == 0) stat_s = (sorted[D / 2 - 1] + sorted[D / 2]) * 0.5;
+  __syncthreads();
+  const double mad = stat_s;
+  const bool flag = own && (0.6745 * (nj - med) > 3.5 * mad) && (nj > 2.0 * med);
+  const uint64_t bits = __ballot(flag);
+  if (own && (j & 63) == 0) {
+    uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, kv);
+    uint32_t *mw = (uint32_t *)(st + L.mask_off + uint64_t(a.slot) * L.mask_chunk + uint64_t(h) * L.mask_head) +
+                   (j >> 5);
+    mw[0] = uint32_t(bits);
+    mw[1] = uint32_t(bits >> 32);
+  }
+}
+
 // One thread per (token, group).  blockIdx.x = tile of 256 (token, group)
 // items, y = head, z = stream.  Base = centroid of the token's cluster, or the
 // cross-layer prediction when a.pred is set (then the reconstruction is also
 // written to a.chain in bf16).
 // CHAIN: also accumulate the reconstruction and write it to a.chain in bf16.
-template <int D, int G, int BITS, bool BF16, bool CHAIN>
+// OUTL: the call's flagged channels (mask of its slot) form one more group
+// per token and stage, spread over the token's D/G threads (min and max
+// combined across them); meta entry D/G holds its (sigma, z).
+template <int D, int G, int BITS, bool BF16, bool CHAIN, bool OUTL = false>
 __global__ __launch_bounds__(256) void k_quantize(EncodeArgs a) {
   constexpr int EB = BF16 ? 2 : 4;
   constexpr int NG = D / G;
@@ -997,7 +1115,81 @@ __global__ __launch_bounds__(256) void k_quantize(EncodeArgs a) {
       r[j] = load_elem<BF16>(xrow, g * G + j) - c;
     }
   }
+  constexpr int FW = (G + 31) / 32;
+  uint32_t fm[FW];
+  if constexpr (OUTL) {
+    const uint32_t *mw = (const uint32_t *)(st + L.mask_off + uint64_t(a.slot) * L.mask_chunk +
+                                            uint64_t(h) * L.mask_head);
+#pragma unroll
+    for (int i = 0; i < FW; ++i) fm[i] = mw[g * FW + i];
+  }
   for (int s = 0; s < L.S; ++s) {
+    if constexpr (OUTL) {
+      float mn = INFINITY, mx = -INFINITY, omn = INFINITY, omx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < G; ++j) {
+        const bool f = (fm[j >> 5] >> (j & 31)) & 1u;
+        mn = fminf(mn, f ? INFINITY : r[j]);
+        mx = fmaxf(mx, f ? -INFINITY : r[j]);
+        omn = fminf(omn, f ? r[j] : INFINITY);
+        omx = fmaxf(omx, f ? r[j] : -INFINITY);
+      }
+      // the token's threads are NG consecutive lanes
+#pragma unroll
+      for (int m = 1; m < NG; m <<= 1) {
+        omn = fminf(omn, __shfl_xor(omn, m));
+        omx = fmaxf(omx, __shfl_xor(omx, m));
+      }
+      // a group without channels stores (0, 0)
+      const bool hn = mn <= mx, ho = omn <= omx;
+      const uint16_t zb = hn ? f32_to_f16_bits(mn) : uint16_t(0);
+      const float zf = f16_bits_to_f32(zb);
+      const uint16_t sb = hn ? f32_to_f16_bits((mx - zf) / LEVELS) : uint16_t(0);
+      const float sf = f16_bits_to_f32(sb);
+      const uint16_t zbo = ho ? f32_to_f16_bits(omn) : uint16_t(0);
+      const float zfo = f16_bits_to_f32(zbo);
+      const uint16_t sbo = ho ? f32_to_f16_bits((omx - zfo) / LEVELS) : uint16_t(0);
+      const float sfo = f16_bits_to_f32(sbo);
+      const float inv = 1.0f / sf, invo = 1.0f / sfo;
+      constexpr int PER_BYTE = 8 / BITS;
+      uint32_t w[WORDS];
+#pragma unroll
+      for (int i = 0; i < WORDS; ++i) w[i] = 0;
+#pragma unroll
+      for (int j0 = 0; j0 < G; j0 += PER_BYTE) {
+        float q[PER_BYTE];
+#pragma unroll
+        for (int e = 0; e < PER_BYTE; ++e) {
+          const int j = j0 + e;
+          const bool f = (fm[j >> 5] >> (j & 31)) & 1u;
+          const float zj = f ? zfo : zf, sj = f ? sfo : sf, ij = f ? invo : inv;
+          // sigma 0 (degenerate group): code 0, r^ = z
+          const float qq = fminf(fmaxf(rintf((r[j] - zj) * ij), 0.0f), LEVELS);
+          q[e] = sj != 0.0f ? qq : 0.0f;
+          const float rh = fmaf(q[e], sj, zj);
+          r[j] = r[j] - rh;
+          if constexpr (CHAIN) xh[j] = xh[j] + rh;
+        }
+        float byte = q[PER_BYTE - 1];
+#pragma unroll
+        for (int e = PER_BYTE - 2; e >= 0; --e) byte = fmaf(byte, float(1 << BITS), q[e]);
+        const int bi = j0 / PER_BYTE;
+        w[bi / 4] = __builtin_amdgcn_cvt_pk_u8_f32(byte, bi % 4, w[bi / 4]);
+      }
+      uint8_t *cp = st + L.codes_off + uint64_t(s) * L.codes_stage + uint64_t(h) * L.codes_head +
+                    uint64_t(tt) * L.codes_token + uint64_t(g) * (G * BITS / 8);
+      if constexpr (WORDS == 2) {
+        *(uint2 *)cp = make_uint2(w[0], w[1]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < WORDS; i += 4) *(uint4 *)(cp + 4 * i) = make_uint4(w[i], w[i + 1], w[i + 2], w[i + 3]);
+      }
+      uint32_t *mp = (uint32_t *)(st + L.meta_off + uint64_t(s) * L.meta_stage + uint64_t(h) * L.meta_head +
+                                  uint64_t(tt) * L.meta_token);
+      mp[g] = uint32_t(sb) | (uint32_t(zb) << 16);
+      if (g == 0) mp[NG] = uint32_t(sbo) | (uint32_t(zbo) << 16);
+      continue;
+    }
     float mn = r[0], mx = r[0];
 #pragma unroll
     for (int j = 1; j < G; ++j) {
@@ -1101,6 +1293,47 @@ __device__ __forceinline__ void add_stages(const uint8_t *st, const DevLayout &L
   }
 }
 
+// add_stages with the outlier group: channel j of the group is dequantized
+// with meta entry D/G when bit j of fm (the token's chunk's mask words for
+// the group's channels) is set.
+template <int D, int G, int BITS>
+__device__ __forceinline__ void add_stages_outl(const uint8_t *st, const DevLayout &L, int h, int64_t tt,
+                                                int g, float *xh, const uint32_t *fm) {
+  constexpr int NG = D / G;
+  constexpr int WORDS = G * BITS / 32;
+  for (int s = 0; s < L.S; ++s) {
+    const uint8_t *cp = st + L.codes_off + uint64_t(s) * L.codes_stage + uint64_t(h) * L.codes_head +
+                        uint64_t(tt) * L.codes_token + uint64_t(g) * (G * BITS / 8);
+    uint32_t w[WORDS];
+    if constexpr (WORDS == 2) {
+      const uint2 v = *(const uint2 *)cp;
+      w[0] = v.x; w[1] = v.y;
+    } else {
+#pragma unroll
+      for (int i = 0; i < WORDS; i += 4) {
+        const uint4 v = *(const uint4 *)(cp + 4 * i);
+        w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
+      }
+    }
+    const uint32_t *mrow = (const uint32_t *)(st + L.meta_off + uint64_t(s) * L.meta_stage +
+                                              uint64_t(h) * L.meta_head + uint64_t(tt) * L.meta_token);
+    const uint32_t m = mrow[g], mo = mrow[NG];
+    const float sf = f16_bits_to_f32(uint16_t(m & 0xffffu)), zf = f16_bits_to_f32(uint16_t(m >> 16));
+    const float sfo = f16_bits_to_f32(uint16_t(mo & 0xffffu)), zfo = f16_bits_to_f32(uint16_t(mo >> 16));
+    float q[G];
+#pragma unroll
+    for (int i = 0; i < WORDS; ++i) {
+      if constexpr (BITS == 2) widen_codes2(w[i], q + 16 * i);
+      else widen_codes4(w[i], q + 8 * i);
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const bool f = (fm[j >> 5] >> (j & 31)) & 1u;
+      xh[j] = xh[j] + fmaf(q[j], f ? sfo : sf, f ? zfo : zf);
+    }
+  }
+}
+
 // Centroid base of token tt (snapshot of its chunk).
 template <int D, int G, bool CB_BF16>
 __device__ __forceinline__ void centroid_base(const uint8_t *st, const DevLayout &L, int h, int tt, int g,
@@ -1145,7 +1378,7 @@ __device__ __forceinline__ void store_wave_contiguous(uint4 *dst, uint4 *buf, co
 // The output of a wave (64 consecutive (token, group) items) is one
 // contiguous run of memory; it is stored through LDS in lane-contiguous
 // pieces.
-template <int D, int G, int BITS, bool CB_BF16>
+template <int D, int G, int BITS, bool CB_BF16, bool OUTL = false>
 __global__ __launch_bounds__(256) void k_reconstruct(ReconArgs a, int64_t out_tokens, int32_t out_t_off) {
   constexpr int NG = D / G;
   constexpr int PB = G * 2 / 16;             // 16-byte pieces of a group in bf16
@@ -1175,7 +1408,18 @@ __global__ __launch_bounds__(256) void k_reconstruct(ReconArgs a, int64_t out_to
   } else {
     centroid_base<D, G, CB_BF16>(st, L, h, tt, g, xh);
   }
-  add_stages<D, G, BITS>(st, L, h, tt, g, xh);
+  if constexpr (OUTL) {
+    constexpr int FW = (G + 31) / 32;
+    const int slot = chunk_of((const StreamHeader *)(st + L.header_off), tt);
+    const uint32_t *mw = (const uint32_t *)(st + L.mask_off + uint64_t(slot) * L.mask_chunk +
+                                            uint64_t(h) * L.mask_head);
+    uint32_t fm[FW];
+#pragma unroll
+    for (int i = 0; i < FW; ++i) fm[i] = mw[g * FW + i];
+    add_stages_outl<D, G, BITS>(st, L, h, tt, g, xh, fm);
+  } else {
+    add_stages<D, G, BITS>(st, L, h, tt, g, xh);
+  }
   // first item of the wave: token t_w = wave_item0 / NG, group 0 (runs of a
   // wave start at a token boundary because 64 % NG == 0)
   const int t_w = wave_item0 / NG;
@@ -1277,12 +1521,14 @@ __device__ __forceinline__ int chunk_of_lds(const int32_t *starts, int n_chunks,
 
 constexpr float AT3_TAU = 8.0f;
 
-template <int D, int G, int BITS, bool CB_BF16, int SMAX, bool FRESH = false>
+template <int D, int G, int BITS, bool CB_BF16, int SMAX, bool FRESH = false, bool OUTL = false>
 __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   // SMAX = the number of PRQ stages (a template parameter so that the staging
   // registers are sized exactly).  FRESH: the keys and values are the
   // uncoded bf16 rows a.k_new / a.v_new ([H][n_keys][D]) of the chunk being
-  // generated; an item is then copied to LDS as read.
+  // generated; an item is then copied to LDS as read.  OUTL: channels flagged
+  // in the mask of the key's chunk take the outlier group's (sigma, z)
+  // (meta entry D/G).
   constexpr int IC = 32;                   // channels of one rebuild item
   constexpr int NI = D / IC;               // items per key and tensor
   constexpr int KP = D + 8;                // bf16 elements per K row in LDS
@@ -1481,7 +1727,7 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     // from the stage-by-stage reconstruction (c + rhat_1) + rhat_2 ... by a few
     // fp32 ulps, which changes the bf16 operand only for values within those
     // ulps of a bf16 rounding boundary.
-    auto dequant_store = [&](int buf) {
+    auto dequant_store = [&](int buf, int tile) {
       if (!has_item) return;
       if constexpr (FRESH) {
         uint16_t *dst = it_kv ? &Vs[buf][it_key * VP + it_ch] : &Ks[buf][it_key * KP + it_ch];
@@ -1506,6 +1752,42 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
       for (int j = 0; j < IC; j += 8)
         *(uint4 *)(dst + j) = make_uint4(pack_bf16x2(xh[j], xh[j + 1]), pack_bf16x2(xh[j + 2], xh[j + 3]),
                                          pack_bf16x2(xh[j + 4], xh[j + 5]), pack_bf16x2(xh[j + 6], xh[j + 7]));
+      if constexpr (OUTL) {
+        // channels of the item flagged in the mask of the key's chunk: rebuilt
+        // again with the outlier group's (sigma, z) and stored over the first
+        // result (a few channels per item; their data is re-read from cache)
+        const int t = ks + tile * AT_BK + it_key;
+        if (t < ke) {
+          const int cslot = nch_s > 1 ? chunk_of_lds(starts_s, nch_s, t) : 0;
+          uint32_t fm = *(const uint32_t *)(st + L.mask_off + uint64_t(cslot) * L.mask_chunk +
+                                            uint64_t(h) * L.mask_head + (it_ch >> 5) * 4);
+          if (fm) {
+            const uint8_t *mo = meta_p + uint64_t(tile) * tile_meta + 4 * (D / G - it_g);
+            float so[SMAX];
+            float zso = 0.0f;
+  #pragma unroll
+            for (int s2 = 0; s2 < SMAX; ++s2) {
+              const uint32_t m = *(const uint32_t *)(mo + uint64_t(s2) * L.meta_stage);
+              so[s2] = f16_bits_to_f32(uint16_t(m & 0xffffu));
+              zso += f16_bits_to_f32(uint16_t(m >> 16));
+            }
+            const int id = L.id_bytes == 1 ? int(idp[t]) : int(((const uint16_t *)idp)[t]);
+            const uint8_t *crow = cb_p + uint64_t(cslot) * L.cb_chunk + uint64_t(id) * (D * EB);
+            while (fm) {
+              const int e = __builtin_ctz(fm);
+              fm &= fm - 1u;
+              float v = load_elem<CB_BF16>(crow, e) + zso;
+  #pragma unroll
+              for (int s2 = 0; s2 < SMAX; ++s2) {
+                const uint32_t w = R.codes[s2][(e * BITS) >> 5];
+                const float qv = float((w >> ((e * BITS) & 31)) & ((1u << BITS) - 1u));
+                v = fmaf(qv, so[s2], v);
+              }
+              dst[e] = f32_to_bf16_bits(v);
+            }
+          }
+        }
+      }
     };
 
     auto compute_tile = [&](int tile) {
@@ -1586,7 +1868,7 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     __syncthreads();  // previous segment's tiles no longer read
     int id_next;   // id of the item's key in tile+2
     load_data(0, load_ids(0));
-    dequant_store(0);
+    dequant_store(0, 0);
     load_data(1, load_ids(1));
     id_next = load_ids(2);
     __syncthreads();
@@ -1594,7 +1876,7 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     for (int tile = 0; tile < n_tiles; ++tile) {
       const int buf = tile & 1;
       if (mfma_first) compute_tile(tile);
-      if (tile + 1 < n_tiles) dequant_store(buf ^ 1);   // data of tile+1 already in R
+      if (tile + 1 < n_tiles) dequant_store(buf ^ 1, tile + 1);   // data of tile+1 already in R
       load_data(tile + 2, id_next);
       id_next = load_ids(tile + 3);
       if (!mfma_first) compute_tile(tile);
@@ -2073,11 +2355,19 @@ static void launch_update_t(const EncodeArgs &a, int streams, hipStream_t st) {
   hipLaunchKernelGGL((k_update<D, BF>), dim3(cdiv(a.L.C, 16), a.L.H, streams), dim3(1024), 0, st, a);
 }
 
+template <int D, bool BF>
+static void launch_chan_flags_t(const EncodeArgs &a, int streams, hipStream_t st) {
+  hipLaunchKernelGGL((k_chan_stats<D, BF>), dim3(kChanParts, a.L.H, streams), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_chan_flags<D>), dim3(a.L.H, streams), dim3(128), 0, st, a);
+}
+
 template <int D, int G, int BITS, bool BF>
 static void launch_quantize_t(const EncodeArgs &a, int streams, hipStream_t st) {
   const int64_t items = int64_t(a.n) * (D / G);
   const dim3 grid(cdiv(items, 256), a.L.H, streams);
-  if (a.chain)
+  if (a.L.mask_off)
+    hipLaunchKernelGGL((k_quantize<D, G, BITS, BF, false, true>), grid, dim3(256), 0, st, a);
+  else if (a.chain)
     hipLaunchKernelGGL((k_quantize<D, G, BITS, BF, true>), grid, dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((k_quantize<D, G, BITS, BF, false>), grid, dim3(256), 0, st, a);
@@ -2089,14 +2379,27 @@ static void launch_recon_t(const ReconArgs &a, int n_layers, int64_t out_tokens,
   const int64_t items = int64_t(a.n) * (D / G);
   // LDS: 4 waves x 64 lanes x one group of the output type
   const size_t lds = size_t(4) * 64 * G * (a.out && !a.out_bf16 ? 4 : 2);
-  hipLaunchKernelGGL((k_reconstruct<D, G, BITS, BF>), dim3(cdiv(items, 256), a.L.H, n_layers), dim3(256),
-                     lds, st, a, out_tokens, out_t_off);
+  if (a.L.mask_off)
+    hipLaunchKernelGGL((k_reconstruct<D, G, BITS, BF, true>), dim3(cdiv(items, 256), a.L.H, n_layers), dim3(256),
+                       lds, st, a, out_tokens, out_t_off);
+  else
+    hipLaunchKernelGGL((k_reconstruct<D, G, BITS, BF>), dim3(cdiv(items, 256), a.L.H, n_layers), dim3(256),
+                       lds, st, a, out_tokens, out_t_off);
 }
 
 template <int D, int G, int BITS, bool BF>
 static void launch_attend_t(const AttnArgs &a, hipStream_t st) {
   const int64_t total = int64_t(a.n_ktiles) * a.n_qblocks * a.L.H;
   const dim3 grid(unsigned(cdiv(total, a.units_per_block)));
+  if (a.L.mask_off) {
+    switch (a.L.S) {
+      case 1: hipLaunchKernelGGL((k_attend3<D, G, BITS, BF, 1, false, true>), grid, dim3(512), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((k_attend3<D, G, BITS, BF, 2, false, true>), grid, dim3(512), 0, st, a); break;
+      case 3: hipLaunchKernelGGL((k_attend3<D, G, BITS, BF, 3, false, true>), grid, dim3(512), 0, st, a); break;
+      default: hipLaunchKernelGGL((k_attend3<D, G, BITS, BF, 4, false, true>), grid, dim3(512), 0, st, a); break;
+    }
+    return;
+  }
   switch (a.L.S) {
     case 1: hipLaunchKernelGGL((k_attend3<D, G, BITS, BF, 1>), grid, dim3(512), 0, st, a); break;
     case 2: hipLaunchKernelGGL((k_attend3<D, G, BITS, BF, 2>), grid, dim3(512), 0, st, a); break;
@@ -2131,6 +2434,9 @@ void launch_assign(const EncodeArgs &a, int streams, hipStream_t st) {
 }
 void launch_update(const EncodeArgs &a, int streams, hipStream_t st) {
   QKV_DISPATCH_D_BF16(a.L.D, a.L.kv_bf16, launch_update_t, a, streams, st);
+}
+void launch_chan_flags(const EncodeArgs &a, int streams, hipStream_t st) {
+  QKV_DISPATCH_D_BF16(a.L.D, a.L.kv_bf16, launch_chan_flags_t, a, streams, st);
 }
 void launch_quantize(const EncodeArgs &a, int streams, hipStream_t st) {
   QKV_DISPATCH_CODEC(a.L, launch_quantize_t, a, streams, st);

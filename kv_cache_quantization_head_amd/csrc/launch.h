@@ -11,6 +11,7 @@ void launch_header(const EncodeArgs &a, int streams, hipStream_t st);
 void launch_init(const EncodeArgs &a, int streams, hipStream_t st);
 void launch_assign(const EncodeArgs &a, int streams, hipStream_t st);
 void launch_update(const EncodeArgs &a, int streams, hipStream_t st);
+void launch_chan_flags(const EncodeArgs &a, int streams, hipStream_t st);
 void launch_quantize(const EncodeArgs &a, int streams, hipStream_t st);
 void launch_reconstruct(const ReconArgs &a, int n_layers, int64_t out_tokens, int out_t_off,
                         hipStream_t st);

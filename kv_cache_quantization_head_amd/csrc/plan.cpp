@@ -29,6 +29,7 @@ int make_plan(const qkv_config *cfg, Plan *plan) {
   if (c.xlayer != 0 && c.xlayer != 1) return QKV_E_INVAL;
   if (c.codebook_reuse != 0 && c.codebook_reuse != 1) return QKV_E_INVAL;
   if (c.xlayer_adapt != 0 && (c.xlayer_adapt != 1 || !c.xlayer)) return QKV_E_INVAL;
+  if (c.outlier_channels != 0 && (c.outlier_channels != 1 || c.xlayer)) return QKV_E_INVAL;
   if (c.xlayer) {
     if (c.xlayer_rank < 1 || c.xlayer_rank > 64) return QKV_E_INVAL;
     if (c.kv_dtype != QKV_BF16) return QKV_E_INVAL;
@@ -55,7 +56,8 @@ int make_plan(const qkv_config *cfg, Plan *plan) {
   s.codes_stage = H * s.codes_head;
   s.codes_off = off;
   off = align_up(off + S * s.codes_stage);
-  s.meta_token = (d / G) * 4;
+  const uint64_t outl = c.outlier_channels ? 1 : 0;
+  s.meta_token = (d / G + outl) * 4;
   s.meta_head = T * s.meta_token;
   s.meta_stage = H * s.meta_head;
   s.meta_off = off;
@@ -75,6 +77,11 @@ int make_plan(const qkv_config *cfg, Plan *plan) {
   s.cn_chunk = c.codebook_reuse ? 0 : H * s.cn_head;
   s.cn_off = off;
   off = align_up(off + snaps * H * s.cn_head);
+  // outlier channel flags: one d-bit mask per head and encode call
+  s.mask_head = outl ? d / 8 : 0;
+  s.mask_chunk = H * s.mask_head;
+  s.mask_off = outl ? off : 0;
+  if (outl) off = align_up(off + K * s.mask_chunk);
   s.bytes = off;
 
   p.streams_bytes = 2 * uint64_t(c.n_layers) * s.bytes;
@@ -109,6 +116,9 @@ int make_plan(const qkv_config *cfg, Plan *plan) {
   // re-fit sums: [parts][2 kv][2 matrices][H][d][d] fp64 (adapted mode)
   p.xl_gram_off = enc;
   if (c.xlayer_adapt) enc = align_up(enc + uint64_t(kRefitParts) * 4 * H * d * d * 8);
+  // outlier flags: per-range channel sums of squares of the residual
+  p.chan_part_off = enc;
+  if (outl) enc = align_up(enc + 2 * uint64_t(c.n_layers) * H * kChanParts * d * 8);
   p.scratch_bytes = std::max(attn, enc);
   p.total_bytes = p.scratch_off + p.scratch_bytes;
   *plan = p;
@@ -246,6 +256,9 @@ extern "C" int qkv_layout(const qkv_ctx *ctx, int32_t layer, int32_t kv, qkv_lay
   d.cnorm_off = base + p.s.cn_off;
   d.cnorm_chunk_stride = p.s.cn_chunk;
   d.cnorm_head_stride = p.s.cn_head;
+  d.chmask_off = p.s.mask_off ? base + p.s.mask_off : 0;
+  d.chmask_chunk_stride = p.s.mask_chunk;
+  d.chmask_head_stride = p.s.mask_head;
   d.n_tokens = ctx->layers[layer].n_tokens;
   d.n_chunks = int32_t(ctx->layers[layer].starts.size());
   *out = d;

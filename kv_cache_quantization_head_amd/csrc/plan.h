@@ -16,6 +16,7 @@ constexpr int kMaxChunks = 256;      // snapshot slots per stream (header size)
 constexpr int kMaxSplits = 8;        // split-KV partitions of one attention call
 constexpr int kRefitParts = 8;       // adapted-predictor re-fit: token ranges summed apart, then in order
 constexpr int kSortMaxClusters = 4096;  // k-means update through per-tile sorts up to this C
+constexpr int kChanParts = 64;       // outlier flags: token ranges whose channel sums are kept apart
 constexpr uint64_t kAlign = 256;
 
 inline uint64_t align_up(uint64_t v, uint64_t a = kAlign) { return (v + a - 1) / a * a; }
@@ -37,6 +38,7 @@ struct StreamLayout {
   uint64_t ids_off, ids_head, id_bytes;
   uint64_t cb_off, cb_chunk, cb_head, cb_row;
   uint64_t cn_off, cn_chunk, cn_head;
+  uint64_t mask_off, mask_chunk, mask_head;   // outlier channel flags (0 when off)
   uint64_t bytes;      // whole stream, aligned
 };
 
@@ -52,6 +54,7 @@ struct Plan {
   uint64_t xl_gram_off;                            // relative to scratch (adapted mode re-fit)
   uint64_t sort_perm_off, sort_off_off;            // relative to scratch (encode)
   uint64_t sort_tiles;                             // 256-token tiles per call, max
+  uint64_t chan_part_off;                          // relative to scratch: [2L][H][kChanParts][d] fp64
   uint64_t total_bytes;
   int kv_elem_bytes;
 };

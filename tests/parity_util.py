@@ -13,17 +13,17 @@ import kv_cache_quantization_head_amd as qkv
 
 def make_codec(H, d, C, S, bits, G, iters=5, max_tokens=4096, max_chunks=4, dtype="bf16",
                max_q=256, n_layers=1, max_chunk_tokens=0, xlayer=0, rank=0, predictor=None, reuse=0,
-               adapt=0):
+               adapt=0, outliers=0):
     cfg = qkv.config(n_layers, H, d, C, S, bits, G, kmeans_iters=iters, max_tokens=max_tokens,
                      max_chunk_tokens=max_chunk_tokens, max_chunks=max_chunks,
                      kv_dtype=qkv.QKV_BF16 if dtype == "bf16" else qkv.QKV_F32,
                      max_query_tokens=max_q, xlayer=xlayer, xlayer_rank=rank, codebook_reuse=reuse,
-                     xlayer_adapt=adapt)
+                     xlayer_adapt=adapt, outlier_channels=outliers)
     return qkv.Codec(cfg, device="cuda", predictor=predictor)
 
 
-def oracle_stream(H, d, C, iters, S, bits, G, dtype, reuse=False):
-    return o_stream.Stream(H, d, C, iters, S, bits, G, dtype, reuse=reuse)
+def oracle_stream(H, d, C, iters, S, bits, G, dtype, reuse=False, outliers=False):
+    return o_stream.Stream(H, d, C, iters, S, bits, G, dtype, reuse=reuse, outliers=outliers)
 
 
 def f32_bits(a):

@@ -1,0 +1,112 @@
+"""GPU parity of the outlier-channel option against the oracle, through the C ABI.
+
+Q-ARVD explainer, outlier-aware adaptive dual-scale quantization (carried
+over to the KV residual): every encode call flags, per head, the channels
+whose residual norm stands out and codes them as one more group per token
+and stage.  Bit-exact bar: flags (the d-bit mask of each call), ids,
+snapshots, codes, (sigma, z) with the extra entry, and the fp32
+reconstruction; attention within the usual bound.  The flag decision
+depends on fp64 sums taken in another order on each side, so every case
+first checks that no channel lies within 1e-9 (relative) of either cut.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import outlier as o_outlier
+from oracle import sas as o_sas
+from parity_util import (assert_stream_equal, attention_tolerance_check, f32_bits, make_codec, o_attend,
+                         oracle_stream)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _check_masks(codec, layer, kv, ost):
+    for c, chunk in enumerate(ost.chunks):
+        got = codec.channel_mask(layer, kv, c).cpu().numpy().view(np.uint32)
+        for h, ch in enumerate(chunk):
+            want = o_outlier.pack_flags(ch.flags)
+            np.testing.assert_array_equal(got[h], want, err_msg=f"mask chunk {c} head {h}")
+
+
+def _check_margins(ost, xs):
+    """No channel's decision within 1e-9 of a cut (xs: the calls' inputs [H, n, d])."""
+    for chunk, x in zip(ost.chunks, xs):
+        for h, ch in enumerate(chunk):
+            r0 = o_sas.centroid_residual(x[h], ch.codebook, ch.ids)
+            m = o_outlier.flag_margin(o_outlier.channel_norms(r0))
+            assert m > 1e-9, f"near-tie flag decision (margin {m:.2e}): choose another case"
+
+
+CASES = [
+    # name, base config, H, d, C, S, bits, G, dtype, chunk sizes, reuse
+    ("wan_int2_g32", "wan", 3, 128, 32, 2, 2, 32, "bf16", [1000, 777], 0),
+    ("wan_int4_g64_s3", "wan", 2, 128, 48, 3, 4, 64, "bf16", [1300], 0),
+    ("d64_int2_g32_s4", "wan", 2, 64, 16, 4, 2, 32, "bf16", [600, 300, 129], 0),
+    ("tiny_f32_g64", "tiny", 2, 64, 16, 2, 2, 64, "f32", [1500], 0),
+    ("wan_reuse", "wan", 2, 128, 32, 2, 2, 32, "bf16", [900, 900], 1),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_outlier_stream_matches_oracle(case):
+    name, base, H, d, C, S, b, G, dtype, n_list, reuse = case
+    if base == "wan":
+        cfgs = synth.scaled(synth.WAN_LAYER, n_heads=H, head_dim=d, n_clusters=C, group=G, tokens=sum(n_list))
+    else:
+        cfgs = synth.scaled(synth.TINY, n_heads=H, tokens=sum(n_list))
+    it = 3
+    _say(f"outlier case {name}: chunks {n_list}")
+    codec = make_codec(H, d, C, S, b, G, iters=it, max_tokens=sum(n_list), max_chunks=len(n_list), dtype=dtype,
+                       max_q=256, reuse=reuse, outliers=1)
+    ost = [oracle_stream(H, d, C, it, S, b, G, dtype, reuse=bool(reuse), outliers=True) for _ in range(2)]
+    xs = [[], []]
+    t0 = 0
+    for n in n_list:
+        k = synth.kv_tokens(cfgs, 0, 0, t0, n)
+        v = synth.kv_tokens(cfgs, 0, 1, t0, n)
+        codec.encode_chunk(k.to(DEV), v.to(DEV))
+        for kv, x in ((0, k), (1, v)):
+            xs[kv].append(x.float().numpy())
+            ost[kv].encode(xs[kv][-1])
+        t0 += n
+    torch.cuda.synchronize()
+    for kv in (0, 1):
+        _check_margins(ost[kv], xs[kv])
+        assert any(ch.flags.any() for chunk in ost[kv].chunks for ch in chunk), "no channel flagged"
+        _check_masks(codec, 0, kv, ost[kv])
+        assert_stream_equal(codec, 0, kv, ost[kv])
+        rec = codec.reconstruct(0, 1, kv, 0, t0)[0].cpu().numpy()
+        np.testing.assert_array_equal(f32_bits(rec), f32_bits(ost[kv].xhat()))
+        # a ragged window across a chunk boundary, bf16 output
+        a0, a1 = n_list[0] // 2, min(t0, n_list[0] + 77)
+        recb = codec.reconstruct(0, 1, kv, a0, a1, out_dtype=torch.bfloat16)[0].float().cpu().numpy()
+        np.testing.assert_array_equal(recb, torch.from_numpy(ost[kv].xhat()[:, a0:a1]).bfloat16().float().numpy())
+    q = synth.queries(synth.scaled(cfgs, q_dtype=dtype), 0, 256)
+    out, lse = codec.attend(0, q.to(DEV))
+    o_ref, lse_ref = o_attend.attend(q.float().numpy(), ost[0].xhat(), ost[1].xhat())
+    err = attention_tolerance_check(out.cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
+    _say(f"  attention max abs error {err:.3e}")
+
+
+def test_outlier_dual_scale_lowers_error_on_device():
+    """The option's point, measured on the device's own output: on the
+    generator's shape (4 channels x10) the reconstruction error of the
+    dual-scale codes is below that of the plain codes."""
+    cfgs = synth.scaled(synth.WAN_LAYER, n_heads=4, tokens=3120)
+    k = synth.kv_tokens(cfgs, 0, 0, 0, 3120)
+    v = synth.kv_tokens(cfgs, 0, 1, 0, 3120)
+    errs = []
+    for outl in (0, 1):
+        codec = make_codec(4, 128, 64, 2, 2, 32, iters=5, max_tokens=3120, max_chunks=1, outliers=outl, max_q=0)
+        codec.encode_chunk(k.to(DEV), v.to(DEV))
+        rec = codec.reconstruct(0, 1, 0, 0, 3120)[0]
+        errs.append(float((rec - k.to(DEV).float()).norm()))
+    _say(f"  reconstruction error plain {errs[0]:.4f}, dual-scale {errs[1]:.4f}")
+    assert errs[1] < 0.8 * errs[0]

@@ -64,7 +64,7 @@ def test_workspace_bytes_matches_layout_closed_form():
     ("n_stages", 0), ("n_stages", 5), ("bits", 3), ("group_size", 16), ("group_size", 128),
     ("kmeans_iters", -1), ("max_tokens", 0), ("max_tokens", 1 << 31), ("max_chunks", 0),
     ("max_chunks", 257), ("kv_dtype", 7), ("max_chunk_tokens", 40000), ("xlayer", 2),
-    ("codebook_reuse", 2), ("xlayer_adapt", 1),
+    ("codebook_reuse", 2), ("xlayer_adapt", 1), ("outlier_channels", 2),
 ])
 def test_invalid_config_rejected(field, value):
     cfg = _cfg(**{field: value})
@@ -73,6 +73,45 @@ def test_invalid_config_rejected(field, value):
     rc = qkv.lib().qkv_init(ctypes.byref(cfg), ctypes.c_void_p(FAKE), ctypes.c_size_t(1 << 40), None,
                             ctypes.byref(ctx))
     assert rc == B.QKV_E_INVAL and not ctx.value
+
+
+def test_outlier_layout_closed_form():
+    # meta gains one (sigma, z) entry per token and stage; one d-bit mask per
+    # head and chunk; encode scratch holds [2L][H][64][d] fp64 channel sums
+    cfg = _cfg(outlier_channels=1, max_query_tokens=0)
+    H, d, T, S, C, G, K, L = 12, 128, 37440, 2, 256, 32, 4, 2
+    header = _align(8 + 4 * 257)
+    codes = _align(S * H * T * d * 2 // 8)
+    meta = _align(S * H * T * (d // G + 1) * 4)
+    ids = _align(H * T)
+    cb = _align(K * H * C * d * 2)
+    cn = _align(K * H * C * 4)
+    mask = _align(K * H * d // 8)
+    stream = header + codes + meta + ids + cb + cn + mask
+    tiles = (32760 + 255) // 256
+    units = 2 * L * H * tiles
+    sort = _align(_align(units * 256) + units * (C + 1) * 2)
+    chan = _align(2 * L * H * 64 * d * 8)
+    assert qkv.workspace_bytes(cfg) == 2 * L * stream + sort + chan
+    # not with the cross-layer mode
+    assert qkv.workspace_bytes(_cfg(outlier_channels=1, xlayer=1, xlayer_rank=8)) == 0
+    rc, ctx = _init(cfg)
+    assert rc == B.QKV_OK
+    try:
+        d0 = B.qkv_layout_desc()
+        assert qkv.lib().qkv_layout(ctx, 1, 1, ctypes.byref(d0)) == B.QKV_OK
+        assert d0.meta_token_stride == (d // G + 1) * 4
+        assert d0.chmask_off == 3 * stream + header + codes + meta + ids + cb + cn
+        assert d0.chmask_chunk_stride == H * d // 8 and d0.chmask_head_stride == d // 8
+    finally:
+        qkv.lib().qkv_destroy(ctx)
+    rc, ctx = _init(_cfg())
+    try:
+        d0 = B.qkv_layout_desc()
+        assert qkv.lib().qkv_layout(ctx, 0, 0, ctypes.byref(d0)) == B.QKV_OK
+        assert d0.chmask_off == 0 and d0.meta_token_stride == (d // G) * 4
+    finally:
+        qkv.lib().qkv_destroy(ctx)
 
 
 def test_group_must_divide_and_xlayer_needs_bf16_and_rank():
