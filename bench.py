@@ -46,6 +46,10 @@ def parse():
                     help="instead of the default step: encode a long-rollout layer (187200 tokens in 40 "
                          "calls) with codebook reuse and with per-call snapshots; time, reconstruction "
                          "error and storage cost of each")
+    ap.add_argument("--outliers", action="store_true",
+                    help="instead of the default step: the same wan_layer step with and without the "
+                         "outlier-channel option; time of each call, reconstruction error and storage "
+                         "cost of each mode")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (a known-size "
                          "reference for HBM byte counters)")
@@ -320,6 +324,80 @@ def reuse_main(args):
         "modes": res}), flush=True)
 
 
+def outliers_main(args):
+    """The default wan_layer step (encode + reconstruct K and V in bf16 +
+    4680-query attention) with the outlier-channel option on and off: HIP
+    event time of each call averaged over the timed steps, then the
+    reconstruction error of each mode over the layer and its storage cost."""
+    import torch
+    import kv_cache_quantization_head_amd as qkv
+    import synth
+    from fractions import Fraction
+
+    dev = torch.device("cuda:0")
+    cfgs = synth.WAN_LAYER
+    H, T, d, C, S, b, G = (cfgs.n_heads, cfgs.tokens, cfgs.head_dim, cfgs.n_clusters, cfgs.n_stages,
+                           cfgs.bits, cfgs.group)
+    k = synth.kv_tokens(cfgs, 0, 0, 0, T, device=dev)
+    v = synth.kv_tokens(cfgs, 0, 1, 0, T, device=dev)
+    q = synth.queries(cfgs, 0, cfgs.q_tokens, device=dev)
+    codecs = {}
+    for outl in (0, 1):
+        cfg = qkv.config(1, H, d, C, S, b, G, kmeans_iters=cfgs.iters, max_tokens=T, max_chunks=1,
+                         kv_dtype=qkv.QKV_BF16, max_query_tokens=cfgs.q_tokens, outlier_channels=outl)
+        codecs[outl] = qkv.Codec(cfg, device=dev)
+    names = ("qkv_encode_chunk", "qkv_reconstruct", "qkv_attend")
+    times = {o: {n: [] for n in names} for o in codecs}
+    rk = torch.empty((1, H, T, d), dtype=torch.bfloat16, device=dev)
+    rv = torch.empty_like(rk)
+
+    def step(record):
+        for outl, codec in codecs.items():
+            codec.rewind(0, 1, 0)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record()
+            codec.encode_chunk(k, v)
+            ev[1].record()
+            codec.reconstruct(0, 1, 0, 0, T, out_dtype=torch.bfloat16, out=rk)
+            codec.reconstruct(0, 1, 1, 0, T, out_dtype=torch.bfloat16, out=rv)
+            ev[2].record()
+            codec.attend(0, q)
+            ev[3].record()
+            if record:
+                for i, n in enumerate(names):
+                    times[outl][n].append((ev[i], ev[i + 1]))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    res = {}
+    for outl, codec in codecs.items():
+        calls = {n: round(sum(a.elapsed_time(e) for a, e in times[outl][n]) / args.steps, 4) for n in names}
+        err = []
+        for kv, x in ((0, k), (1, v)):
+            xf = x.float()
+            rec = codec.reconstruct(0, 1, kv, 0, T)[0]
+            err.append(float(((rec - xf) ** 2).sum() / (xf ** 2).sum()))
+            del rec
+        bits = Fraction(S * b) + Fraction(S * 32 * (d // G + outl), G * (d // G)) + Fraction(8, d) \
+            + Fraction(8 * 2 * C, T) + (Fraction(1, T) if outl else 0)
+        res["outliers" if outl else "plain"] = {
+            "calls_ms": calls, "step_ms": round(sum(calls.values()), 4),
+            "rel_sq_error_k": round(err[0], 7), "rel_sq_error_v": round(err[1], 7),
+            "bits_per_element": round(float(bits), 4)}
+    print(json.dumps({
+        "metric": "outlier-channel option: wan_layer step time and reconstruction error, on and off",
+        "value": res["outliers"]["step_ms"], "unit": "ms per step (encode + reconstruct + attend)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False, "dtype": "bf16",
+        "data": "synthetic (seeded prototype/drift/outlier generator)",
+        "config": {"workload": "wan_layer: K,V bf16 [12, 32760, 128], C=256, 5 iterations, 2-stage INT2, "
+                               "G=32; 4680 bf16 queries", "heads": H, "tokens": T},
+        "modes": res}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -334,6 +412,9 @@ def main():
         return
     if args.reuse:
         reuse_main(args)
+        return
+    if args.outliers:
+        outliers_main(args)
         return
     import torch
     import kv_cache_quantization_head_amd as qkv

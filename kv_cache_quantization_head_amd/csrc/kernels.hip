@@ -1125,6 +1125,11 @@ __global__ __launch_bounds__(256) void k_quantize(EncodeArgs a) {
   }
   for (int s = 0; s < L.S; ++s) {
     if constexpr (OUTL) {
+      // an empty asm statement makes the flag words opaque at every stage, so
+      // the per-channel flags are extracted where used (a bit test each)
+      // rather than held in registers across the stage loop
+#pragma unroll
+      for (int i = 0; i < FW; ++i) asm volatile("" : "+v"(fm[i]));
       float mn = INFINITY, mx = -INFINITY, omn = INFINITY, omx = -INFINITY;
 #pragma unroll
       for (int j = 0; j < G; ++j) {
@@ -1521,6 +1526,13 @@ __device__ __forceinline__ int chunk_of_lds(const int32_t *starts, int n_chunks,
 
 constexpr float AT3_TAU = 8.0f;
 
+// w[i] for a run-time i < N (selects, no indexed register access)
+template <int N>
+__device__ __forceinline__ uint32_t pick_word(const uint32_t *w, int i) {
+  if constexpr (N == 2) return i ? w[1] : w[0];
+  else return (i & 2) ? ((i & 1) ? w[3] : w[2]) : ((i & 1) ? w[1] : w[0]);
+}
+
 template <int D, int G, int BITS, bool CB_BF16, int SMAX, bool FRESH = false, bool OUTL = false>
 __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   // SMAX = the number of PRQ stages (a template parameter so that the staging
@@ -1722,6 +1734,22 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
         return __uint_as_float(w);
       }
     };
+    // centroid channel e of the item for a run-time e (a select tree over the
+    // item's registers)
+    auto cent_pick = [&](int e) -> float {
+      if constexpr (CB_BF16) {
+        const int wi = e >> 1;
+        const uint4 a = (wi & 8) ? ((wi & 4) ? R.cent[3] : R.cent[2]) : ((wi & 4) ? R.cent[1] : R.cent[0]);
+        const uint32_t w = (wi & 2) ? ((wi & 1) ? a.w : a.z) : ((wi & 1) ? a.y : a.x);
+        return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+      } else {
+        const int vi = e >> 2;
+        const uint4 a0 = (vi & 2) ? ((vi & 1) ? R.cent[3] : R.cent[2]) : ((vi & 1) ? R.cent[1] : R.cent[0]);
+        const uint4 a1 = (vi & 2) ? ((vi & 1) ? R.cent[7] : R.cent[6]) : ((vi & 1) ? R.cent[5] : R.cent[4]);
+        const uint4 a = (vi & 4) ? a1 : a0;
+        return __uint_as_float((e & 2) ? ((e & 1) ? a.w : a.z) : ((e & 1) ? a.y : a.x));
+      }
+    };
     // Rebuild the item for the products: xh = fmaf(q_S, sigma_S, ... fmaf(q_1,
     // sigma_1, c + (z_1 + ... + z_S))), then nearest-even bf16.  This differs
     // from the stage-by-stage reconstruction (c + rhat_1) + rhat_2 ... by a few
@@ -1734,6 +1762,21 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   #pragma unroll
         for (int i = 0; i < KC; ++i) *(uint4 *)(dst + 8 * i) = R.cent[i];
         return;
+      }
+      // OUTL: the key's chunk mask word for the item and the outlier group's
+      // (sigma, z) are loaded first, so that the loads overlap the rebuild
+      uint32_t fm = 0u;
+      uint32_t mo[OUTL ? SMAX : 1];
+      if constexpr (OUTL) {
+        const int t = ks + tile * AT_BK + it_key;
+        if (t < ke) {
+          const int cslot = nch_s > 1 ? chunk_of_lds(starts_s, nch_s, t) : 0;
+          fm = *(const uint32_t *)(st + L.mask_off + uint64_t(cslot) * L.mask_chunk + uint64_t(h) * L.mask_head +
+                                   (it_ch >> 5) * 4);
+          const uint8_t *mop = meta_p + uint64_t(tile) * tile_meta + 4 * (D / G - it_g);
+  #pragma unroll
+          for (int s2 = 0; s2 < SMAX; ++s2) mo[s2] = *(const uint32_t *)(mop + uint64_t(s2) * L.meta_stage);
+        }
       }
       float xh[IC];
       float zs = 0.0f;
@@ -1754,37 +1797,27 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
                                          pack_bf16x2(xh[j + 4], xh[j + 5]), pack_bf16x2(xh[j + 6], xh[j + 7]));
       if constexpr (OUTL) {
         // channels of the item flagged in the mask of the key's chunk: rebuilt
-        // again with the outlier group's (sigma, z) and stored over the first
-        // result (a few channels per item; their data is re-read from cache)
-        const int t = ks + tile * AT_BK + it_key;
-        if (t < ke) {
-          const int cslot = nch_s > 1 ? chunk_of_lds(starts_s, nch_s, t) : 0;
-          uint32_t fm = *(const uint32_t *)(st + L.mask_off + uint64_t(cslot) * L.mask_chunk +
-                                            uint64_t(h) * L.mask_head + (it_ch >> 5) * 4);
-          if (fm) {
-            const uint8_t *mo = meta_p + uint64_t(tile) * tile_meta + 4 * (D / G - it_g);
-            float so[SMAX];
-            float zso = 0.0f;
+        // again with the outlier group's (sigma, z) from the item's registers
+        // and stored over the first result
+        if (fm) {
+          float so[SMAX];
+          float zso = 0.0f;
+  #pragma unroll
+          for (int s2 = 0; s2 < SMAX; ++s2) {
+            so[s2] = f16_bits_to_f32(uint16_t(mo[s2] & 0xffffu));
+            zso += f16_bits_to_f32(uint16_t(mo[s2] >> 16));
+          }
+          while (fm) {
+            const int e = __builtin_ctz(fm);
+            fm &= fm - 1u;
+            float v = cent_pick(e) + zso;
   #pragma unroll
             for (int s2 = 0; s2 < SMAX; ++s2) {
-              const uint32_t m = *(const uint32_t *)(mo + uint64_t(s2) * L.meta_stage);
-              so[s2] = f16_bits_to_f32(uint16_t(m & 0xffffu));
-              zso += f16_bits_to_f32(uint16_t(m >> 16));
+              const uint32_t w = pick_word<KW>(R.codes[s2], (e * BITS) >> 5);
+              const float qv = float((w >> ((e * BITS) & 31)) & ((1u << BITS) - 1u));
+              v = fmaf(qv, so[s2], v);
             }
-            const int id = L.id_bytes == 1 ? int(idp[t]) : int(((const uint16_t *)idp)[t]);
-            const uint8_t *crow = cb_p + uint64_t(cslot) * L.cb_chunk + uint64_t(id) * (D * EB);
-            while (fm) {
-              const int e = __builtin_ctz(fm);
-              fm &= fm - 1u;
-              float v = load_elem<CB_BF16>(crow, e) + zso;
-  #pragma unroll
-              for (int s2 = 0; s2 < SMAX; ++s2) {
-                const uint32_t w = R.codes[s2][(e * BITS) >> 5];
-                const float qv = float((w >> ((e * BITS) & 31)) & ((1u << BITS) - 1u));
-                v = fmaf(qv, so[s2], v);
-              }
-              dst[e] = f32_to_bf16_bits(v);
-            }
+            dst[e] = f32_to_bf16_bits(v);
           }
         }
       }

@@ -110,3 +110,42 @@ def test_outlier_dual_scale_lowers_error_on_device():
         errs.append(float((rec - k.to(DEV).float()).norm()))
     _say(f"  reconstruction error plain {errs[0]:.4f}, dual-scale {errs[1]:.4f}")
     assert errs[1] < 0.8 * errs[0]
+
+
+def test_outlier_wan_layer_full_size():
+    """The Wan-layer workload at full size with the option on (12 heads,
+    32760 tokens, C = 256, 5 iterations, 2-stage INT2, G = 32) in the launch
+    configuration the benchmark times.  Oracle: heads 0 and 11 of K and V;
+    attention on every 97th query of those heads."""
+    cfgs = synth.WAN_LAYER
+    H, d, T = cfgs.n_heads, cfgs.head_dim, cfgs.tokens
+    heads = [0, H - 1]
+    codec = make_codec(H, d, cfgs.n_clusters, cfgs.n_stages, cfgs.bits, cfgs.group, iters=cfgs.iters,
+                       max_tokens=T, max_chunks=1, max_q=cfgs.q_tokens, outliers=1)
+    k = synth.kv_tokens(cfgs, 0, 0, 0, T)
+    v = synth.kv_tokens(cfgs, 0, 1, 0, T)
+    _say(f"outlier wan layer full size: {H} heads x {T} tokens")
+    codec.encode_chunk(k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    ost = []
+    for kv, x in ((0, k), (1, v)):
+        o = oracle_stream(len(heads), d, cfgs.n_clusters, cfgs.iters, cfgs.n_stages, cfgs.bits, cfgs.group,
+                          "bf16", outliers=True)
+        xh = x.float().numpy()[heads]
+        o.encode(xh)
+        _check_margins(o, [xh])
+        got = codec.channel_mask(0, kv, 0).cpu().numpy().view(np.uint32)
+        for i, h in enumerate(heads):
+            np.testing.assert_array_equal(got[h], o_outlier.pack_flags(o.chunks[0][i].flags))
+        assert_stream_equal(codec, 0, kv, o, heads=heads)
+        rec = codec.reconstruct(0, 1, kv, 0, T)[0].cpu().numpy()[heads]
+        np.testing.assert_array_equal(f32_bits(rec), f32_bits(o.xhat()))
+        ost.append(o)
+    q = synth.queries(cfgs, 0, cfgs.q_tokens)
+    out, lse = codec.attend(0, q.to(DEV))
+    sample = np.arange(0, cfgs.q_tokens, 97)
+    qs = q.float().numpy()[heads][:, sample]
+    o_ref, lse_ref = o_attend.attend(qs, ost[0].xhat(), ost[1].xhat())
+    err = attention_tolerance_check(out.cpu().numpy()[heads][:, sample], lse.cpu().numpy()[heads][:, sample],
+                                    o_ref, lse_ref)
+    _say(f"  attention max abs error {err:.3e}")
