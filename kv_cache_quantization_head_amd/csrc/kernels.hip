@@ -1556,6 +1556,8 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][AT_BK * VP];
   __shared__ int32_t starts_s[kMaxChunks + 1];
   __shared__ int32_t nch_s;
+  // OUTL: the segment head's mask words of every chunk, per tensor
+  __shared__ uint32_t masks_s[2][OUTL ? kMaxChunks * (D / 32) : 1];
 
   const DevLayout &L = a.L;
   const int tid = threadIdx.x;
@@ -1612,6 +1614,17 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     const int ke = min(a.n_keys, t1 * AT_BK);
     const int n_tiles = ke > ks ? (ke - ks + AT_BK - 1) / AT_BK : 0;
 
+    if constexpr (OUTL) {
+      // written after the previous segment's last tile barrier, read after
+      // the barrier before this segment's first rebuild
+      constexpr int MW = D / 32;
+      const int per = nch_s * MW;
+      for (int i = tid; i < 2 * per; i += blockDim.x) {
+        const int kv = i / per, c = (i % per) / MW, w = i % MW;
+        masks_s[kv][c * MW + w] = *(const uint32_t *)((kv ? a.stream_v : a.stream_k) + L.mask_off +
+                                                       uint64_t(c) * L.mask_chunk + uint64_t(h) * L.mask_head + 4 * w);
+      }
+    }
     const int q = qblk * AT_BQ + wave * 32 + c32;
     // B operand of S^T = K Q^T, k-step s: Q[q][16 s + 8 hh .. +8] in bf16
     bf16x8 qf[NS];
@@ -1763,19 +1776,21 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
         for (int i = 0; i < KC; ++i) *(uint4 *)(dst + 8 * i) = R.cent[i];
         return;
       }
-      // OUTL: the key's chunk mask word for the item and the outlier group's
-      // (sigma, z) are loaded first, so that the loads overlap the rebuild
+      // OUTL: the item's mask word (from LDS) and, for an item with flagged
+      // channels, the outlier group's (sigma, z), loaded first so that the
+      // loads overlap the rebuild
       uint32_t fm = 0u;
       uint32_t mo[OUTL ? SMAX : 1];
       if constexpr (OUTL) {
         const int t = ks + tile * AT_BK + it_key;
         if (t < ke) {
           const int cslot = nch_s > 1 ? chunk_of_lds(starts_s, nch_s, t) : 0;
-          fm = *(const uint32_t *)(st + L.mask_off + uint64_t(cslot) * L.mask_chunk + uint64_t(h) * L.mask_head +
-                                   (it_ch >> 5) * 4);
-          const uint8_t *mop = meta_p + uint64_t(tile) * tile_meta + 4 * (D / G - it_g);
+          fm = masks_s[it_kv][cslot * (D / 32) + (it_ch >> 5)];
+          if (fm) {
+            const uint8_t *mop = meta_p + uint64_t(tile) * tile_meta + 4 * (D / G - it_g);
   #pragma unroll
-          for (int s2 = 0; s2 < SMAX; ++s2) mo[s2] = *(const uint32_t *)(mop + uint64_t(s2) * L.meta_stage);
+            for (int s2 = 0; s2 < SMAX; ++s2) mo[s2] = *(const uint32_t *)(mop + uint64_t(s2) * L.meta_stage);
+          }
         }
       }
       float xh[IC];
