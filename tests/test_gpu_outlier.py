@@ -149,3 +149,36 @@ def test_outlier_wan_layer_full_size():
     err = attention_tolerance_check(out.cpu().numpy()[heads][:, sample], lse.cpu().numpy()[heads][:, sample],
                                     o_ref, lse_ref)
     _say(f"  attention max abs error {err:.3e}")
+
+
+def test_outlier_multi_layer_call():
+    """One encode call for 3 layers at once (the whole-cache call pattern),
+    then a second call: every (layer, K|V) stream gets its own flags from
+    its own residual; oracle on every head of every layer."""
+    cfgs = synth.scaled(synth.WHOLE_CACHE, n_heads=2, n_clusters=32, tokens=1300)
+    L, H, d = 3, 2, 128
+    n_list = [700, 600]
+    codec = make_codec(H, d, 32, 2, 2, 32, iters=3, max_tokens=1300, max_chunks=2, n_layers=L, max_q=0,
+                       outliers=1)
+    ost = {(l, kv): oracle_stream(H, d, 32, 3, 2, 2, 32, "bf16", outliers=True) for l in range(L) for kv in (0, 1)}
+    xs = {key: [] for key in ost}
+    t0 = 0
+    for n in n_list:
+        ks = torch.stack([synth.kv_tokens(cfgs, l, 0, t0, n) for l in range(L)])
+        vs = torch.stack([synth.kv_tokens(cfgs, l, 1, t0, n) for l in range(L)])
+        _say(f"outlier multi-layer call: {L} layers x {n} tokens")
+        codec.encode_chunk(ks.to(DEV), vs.to(DEV))
+        for l in range(L):
+            for kv, x in ((0, ks[l]), (1, vs[l])):
+                xs[(l, kv)].append(x.float().numpy())
+                ost[(l, kv)].encode(xs[(l, kv)][-1])
+        t0 += n
+    torch.cuda.synchronize()
+    for (l, kv), o in ost.items():
+        _check_margins(o, xs[(l, kv)])
+        _check_masks(codec, l, kv, o)
+        assert_stream_equal(codec, l, kv, o)
+    for kv in (0, 1):
+        rec = codec.reconstruct(0, L, kv, 0, t0).cpu().numpy()
+        for l in range(L):
+            np.testing.assert_array_equal(f32_bits(rec[l]), f32_bits(ost[(l, kv)].xhat()))
