@@ -1776,23 +1776,6 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
         for (int i = 0; i < KC; ++i) *(uint4 *)(dst + 8 * i) = R.cent[i];
         return;
       }
-      // OUTL: the item's mask word (from LDS) and, for an item with flagged
-      // channels, the outlier group's (sigma, z), loaded first so that the
-      // loads overlap the rebuild
-      uint32_t fm = 0u;
-      uint32_t mo[OUTL ? SMAX : 1];
-      if constexpr (OUTL) {
-        const int t = ks + tile * AT_BK + it_key;
-        if (t < ke) {
-          const int cslot = nch_s > 1 ? chunk_of_lds(starts_s, nch_s, t) : 0;
-          fm = masks_s[it_kv][cslot * (D / 32) + (it_ch >> 5)];
-          if (fm) {
-            const uint8_t *mop = meta_p + uint64_t(tile) * tile_meta + 4 * (D / G - it_g);
-  #pragma unroll
-            for (int s2 = 0; s2 < SMAX; ++s2) mo[s2] = *(const uint32_t *)(mop + uint64_t(s2) * L.meta_stage);
-          }
-        }
-      }
       float xh[IC];
       float zs = 0.0f;
   #pragma unroll
@@ -1811,9 +1794,22 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
         *(uint4 *)(dst + j) = make_uint4(pack_bf16x2(xh[j], xh[j + 1]), pack_bf16x2(xh[j + 2], xh[j + 3]),
                                          pack_bf16x2(xh[j + 4], xh[j + 5]), pack_bf16x2(xh[j + 6], xh[j + 7]));
       if constexpr (OUTL) {
-        // channels of the item flagged in the mask of the key's chunk: rebuilt
-        // again with the outlier group's (sigma, z) from the item's registers
-        // and stored over the first result
+        // channels of the item flagged in the mask of the key's chunk (mask
+        // words in LDS): rebuilt again with the outlier group's (sigma, z) and
+        // the item's registers, stored over the first result; read only
+        // here, so that nothing of it is held during the rebuild
+        uint32_t fm = 0u;
+        uint32_t mo[SMAX];
+        const int t = ks + tile * AT_BK + it_key;
+        if (t < ke) {
+          const int cslot = nch_s > 1 ? chunk_of_lds(starts_s, nch_s, t) : 0;
+          fm = masks_s[it_kv][cslot * (D / 32) + (it_ch >> 5)];
+          if (fm) {
+            const uint8_t *mop = meta_p + uint64_t(tile) * tile_meta + 4 * (D / G - it_g);
+  #pragma unroll
+            for (int s2 = 0; s2 < SMAX; ++s2) mo[s2] = *(const uint32_t *)(mop + uint64_t(s2) * L.meta_stage);
+          }
+        }
         if (fm) {
           float so[SMAX];
           float zso = 0.0f;
