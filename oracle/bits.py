@@ -13,16 +13,20 @@ element are
 
 with id_bytes = 1 for C <= 256, else 2, and cb_bytes the cache dtype's size.
 With codebook reuse the stream keeps one codebook, so n_call is replaced by
-every token the stream holds.
+every token the stream holds.  With outlier channels each token and stage
+holds one more fp16 (sigma, z) pair (S*32/d) and each call one d-bit flag
+mask per head (1/n_call).
 """
 from fractions import Fraction
 
 
 def bits_per_element(n_stages, bits, group, head_dim, n_clusters, cb_bytes, n_call,
-                     with_ids=True):
+                     with_ids=True, outliers=False):
     """Exact bits per element as a Fraction."""
     id_bytes = 1 if n_clusters <= 256 else 2
     total = Fraction(n_stages * bits) + Fraction(n_stages * 32, group)
+    if outliers:
+        total += Fraction(n_stages * 32, head_dim) + Fraction(1, n_call)
     if with_ids:
         total += Fraction(8 * id_bytes, head_dim)
         total += Fraction(8 * cb_bytes * n_clusters, n_call)

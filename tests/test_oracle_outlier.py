@@ -211,3 +211,20 @@ def test_stream_flags_find_planted_channels_and_cut_error():
         assert np.linalg.norm(dual.chunks[0][h].r_final) < 0.75 * np.linalg.norm(plain.chunks[0][h].r_final)
         assert outlier.flag_margin(outlier.channel_norms(
             sas.centroid_residual(x[h], dual.chunks[0][h].codebook, dual.chunks[0][h].ids))) > 1e-6
+
+
+def test_stored_sizes_with_outliers_match_closed_form():
+    # the bytes one encoded head holds with the option (codes, (sigma, z) with
+    # the extra entry, ids, codebook, the d-bit flag mask) = the closed form;
+    # at the Wan-layer shape that is 6.19 -> 6.69 bits per element
+    from fractions import Fraction
+    from oracle import bits
+    cfg = synth.scaled(synth.WAN_LAYER, n_heads=1, tokens=1024)
+    x = synth.kv_tokens(cfg, 0, 0, 0, 1024)[0].float().numpy()
+    ch = stream.encode_head(x, 16, 2, 2, 2, 32, "bf16", outliers=True)
+    nbytes = sum(p.nbytes for p in ch.packed) + sum(s.nbytes + z.nbytes for s, z in zip(ch.sigmas, ch.zs)) \
+        + 1024 * 1 + ch.codebook.shape[0] * 128 * 2 + outlier.pack_flags(ch.flags).nbytes
+    assert Fraction(8 * nbytes, 1024 * 128) == bits.bits_per_element(2, 2, 32, 128, 16, 2, 1024, outliers=True)
+    plain = bits.bits_per_element(2, 2, 32, 128, 256, 2, 32760)
+    dual = bits.bits_per_element(2, 2, 32, 128, 256, 2, 32760, outliers=True)
+    assert round(float(plain), 2) == 6.19 and round(float(dual), 2) == 6.69
