@@ -1,16 +1,25 @@
-"""Benchmark of the hot path on one MI355X: encode + reconstruct + fused attention.
+"""Benchmark of the hot path on one MI355X.
 
-One step = one pass of the whole path over one Wan2.1-1.3B-shaped layer
-(K and V bf16 [12 heads, 32760 tokens, d=128], C=256 clusters, 5 k-means
-iterations, 2-stage INT2 with group 32):
-  qkv_rewind to 0 (state reset, a one-thread kernel), qkv_encode_chunk of all
-  32760 tokens (k-means + PRQ + packing, K and V), qkv_reconstruct of K and V
-  (bf16 out), qkv_attend of a 4680-token bf16 query chunk over the packed
-  cache.
-Inputs are seeded synthetic tensors already resident in HBM.  Each library
-call is also bracketed by HIP events on the stream it is launched on.
+Default workload: the long-rollout cache, 30 layers x K,V bf16 [12 heads,
+187200 tokens (120 latent frames x 1560), d=128] = 34.5 GB of bf16 K/V,
+C=256 clusters, 5 k-means iterations, 3-stage INT2 with group 32.  Each
+layer's cache is built untimed by 40 encode calls of 4680 tokens (three
+latent frames), on device-generated seeded tokens.  One timed step is what a
+generating model does per new 4680-token chunk, plus the whole-cache read
+back:
+  qkv_attend of a 4680-query bf16 chunk over each of the 30 packed layers
+  (fused unpack -> dequant -> attention), qkv_encode_chunk of the chunk's
+  new K/V into all 30 layers at once (k-means warm-started from each
+  stream's last snapshot + PRQ + packing), qkv_reconstruct of every layer
+  (K and V, all 191880 tokens, bf16 out), qkv_rewind back to 187200 tokens.
+Inputs are resident in HBM before the timed region; each library call is
+bracketed by HIP events on the stream it runs on.  After the timed steps, a
+traced leg (the library's per-kernel HIP events) gives each kernel's time
+for the per-kernel rooflines; then the oracle is timed on a bounded sample of
+the same workload, and the one-layer Wan step (encode + reconstruct + attend
+of one 32760-token layer) is timed for its own figures.
 
-Prints ONE JSON line (see the repository's design notes for every field).
+Prints ONE JSON line.
 """
 import argparse
 import json
@@ -40,8 +49,10 @@ def parse():
                          "layers (attention over the packed cache plus the chunk's fresh bf16 K/V for "
                          "every denoising step and layer, then the chunk's encode)")
     ap.add_argument("--denoise", type=int, default=4, help="denoising steps per chunk (--fresh)")
-    ap.add_argument("--layers", type=int, default=4,
-                    help="layers of the model (--fresh; Wan2.1-1.3B has 30)")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="layers of the model (default step: 30; --fresh: 4; Wan2.1-1.3B has 30)")
+    ap.add_argument("--no-wan-layer", action="store_true",
+                    help="skip the one-layer Wan step that follows the default step")
     ap.add_argument("--reuse", action="store_true",
                     help="instead of the default step: encode a long-rollout layer (187200 tokens in 40 "
                          "calls) with codebook reuse and with per-call snapshots; time, reconstruction "
@@ -56,55 +67,12 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(cfgs, k_dev, v_dev, q_dev, budget_s=12.0):
-    """The oracle, as it stands, on a bounded sample of the same workload:
-    whole heads of the layer, one after another, until about ``budget_s``
-    seconds of CPU work are done.  Per head: full encode of K and V (k-means
-    + PRQ), reconstruction, attention of all of that head's queries.  Scaled
-    to the same GB/s unit as the GPU line (bf16 K+V bytes of the heads done
-    per second)."""
-    import numpy as np
-    import torch
-    from oracle import attend as o_attend
-    from oracle import stream as o_stream
-
-    threads = torch.get_num_threads()
-    H = k_dev.shape[0]
-    t = time.perf_counter()
-    heads = 0
-    while heads < H:
-        k = k_dev[heads:heads + 1].float().cpu().numpy()
-        v = v_dev[heads:heads + 1].float().cpu().numpy()
-        q = q_dev[heads:heads + 1].float().cpu().numpy()
-        xs = []
-        for x in (k, v):
-            s = o_stream.Stream(1, cfgs.head_dim, cfgs.n_clusters, cfgs.iters, cfgs.n_stages,
-                                cfgs.bits, cfgs.group, "bf16")
-            s.encode(x)
-            xs.append(s.xhat())
-        o_attend.attend(q, xs[0], xs[1])
-        heads += 1
-        if time.perf_counter() - t >= budget_s:
-            break
-    dt = time.perf_counter() - t
-    sample_bytes = heads * 2 * k_dev.shape[1] * k_dev.shape[2] * 2     # bf16 K+V of the heads done
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count()
-    return {"value": round(sample_bytes / dt / 1e9, 6), "unit": "GB/s", "cores": cores,
-            "blas_threads": threads, "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"heads 0..{heads - 1} of {H} of the layer, K and V: full encode "
-                      f"({cfgs.iters} k-means iterations + {cfgs.n_stages} PRQ stages), "
-                      f"reconstruction, attention of all {q_dev.shape[1]} queries of each head"}
-
-
 def recorded_traffic(kernel_source):
-    """HBM bytes of one qkv_attend call (attention kernel + merge), from the
-    committed counter summary, or None when the kernel source changed since
-    it was taken."""
+    """HBM bytes of one qkv_attend call (attention kernel + merge) on a
+    long-rollout layer, from the committed counter summary, or None when the
+    attention source changed since it was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "k_attend3_wan_layer_pmc.txt")
+    path = os.path.join(ROOT, "profiles", "k_attend3_long_rollout_pmc.txt")
     try:
         fields = dict(line.split(":", 1) for line in open(path) if ":" in line)
     except OSError:
@@ -201,7 +169,7 @@ def fresh_main(args):
     import synth
 
     dev = torch.device("cuda:0")
-    L = args.layers
+    L = args.layers or 4
     cfgs = synth.scaled(synth.WAN_LAYER, n_layers=L)
     H, T, d, Tq, n_new = cfgs.n_heads, cfgs.tokens, cfgs.head_dim, cfgs.q_tokens, cfgs.q_tokens
     cfg = qkv.config(L, H, d, cfgs.n_clusters, cfgs.n_stages, cfgs.bits, cfgs.group, kmeans_iters=cfgs.iters,
@@ -398,11 +366,126 @@ def outliers_main(args):
         "modes": res}), flush=True)
 
 
+def _avg_ms(pairs):
+    xs = [a.elapsed_time(b) for a, b in pairs]
+    return sum(xs) / len(xs)
+
+
+def wan_layer_step(args):
+    """One Wan2.1-1.3B-shaped layer (K,V bf16 [12, 32760, 128], C=256, 2-stage
+    INT2, G=32): encode of the whole layer from empty, reconstruct of K and V
+    (bf16 out), attention of 4680 bf16 queries.  Returns its figures."""
+    import torch
+    import kv_cache_quantization_head_amd as qkv
+    import synth
+
+    dev = torch.device("cuda:0")
+    cfgs = synth.WAN_LAYER
+    H, T, d, Tq = cfgs.n_heads, cfgs.tokens, cfgs.head_dim, cfgs.q_tokens
+    S, b, G, C = cfgs.n_stages, cfgs.bits, cfgs.group, cfgs.n_clusters
+    cfg = qkv.config(1, H, d, C, S, b, G, kmeans_iters=cfgs.iters, max_tokens=T, max_chunks=1,
+                     kv_dtype=qkv.QKV_BF16, max_query_tokens=Tq)
+    codec = qkv.Codec(cfg, device=dev)
+    k = synth.kv_tokens(cfgs, 0, 0, 0, T, device=dev)
+    v = synth.kv_tokens(cfgs, 0, 1, 0, T, device=dev)
+    q = synth.queries(cfgs, 0, Tq, device=dev)
+    rec = torch.empty((2, 1, H, T, d), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((H, Tq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((H, Tq), dtype=torch.float32, device=dev)
+    ev = {name: [] for name in ("encode", "reconstruct", "attend")}
+
+    def step(record):
+        codec.rewind(0, 1, 0)
+        m = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        m[0].record()
+        codec.encode_chunk(k, v)
+        m[1].record()
+        codec.reconstruct(0, 1, 0, 0, T, out=rec[0])
+        codec.reconstruct(0, 1, 1, 0, T, out=rec[1])
+        m[2].record()
+        codec.attend(0, q, out=out, lse=lse)
+        m[3].record()
+        if record:
+            for i, n in enumerate(ev):
+                ev[n].append((m[i], m[i + 1]))
+
+    for _ in range(2):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {n: _avg_ms(p) for n, p in ev.items()}
+    n_el = 2 * H * T * d
+    packed = n_el * (S * b / 8 + S * 4 / G) + 2 * H * T
+    att_tflops = 4.0 * H * Tq * T * d / (ms["attend"] * 1e-3) / 1e12
+    return {
+        "workload": "wan_layer: K,V bf16 [12, 32760, 128], C=256, 5 iters, 2-stage INT2 G=32; 4680 bf16 queries",
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "calls_ms": {n: round(x, 4) for n, x in ms.items()},
+        "encode_GBps": round((n_el * 2 + packed) / (ms["encode"] * 1e-3) / 1e9, 2),
+        "reconstruct_GBps": round((packed + 2 * H * C * d * 2 + n_el * 2) / (ms["reconstruct"] * 1e-3) / 1e9, 2),
+        "attend_q_tokens_per_s": round(Tq / (ms["attend"] * 1e-3), 1),
+        "attend_TFLOPs": round(att_tflops, 2),
+        "attend_frac_of_bf16_peak": round(att_tflops / BF16_PEAK_TFLOPS, 4),
+    }
+
+
+def rollout_cpu_baseline(cfgs, k_l0, v_l0, q_l0, n_layers, step_tokens, budget_s=14.0):
+    """The oracle, as it stands, on a bounded sample of the long-rollout
+    workload: head 0 of layer 0, its K and V streams encoded call after call
+    (4680 tokens each, warm-started) for about two thirds of the budget, then
+    the attention of 256 of that head's queries over the keys encoded so
+    far.  The per-token encode time and the per-(query, key) attention time
+    are scaled to the step's work (every layer and head: the chunk's encode,
+    the 4680-query attention over the 187200-token cache) and reported as
+    query tokens per second like the GPU line."""
+    import numpy as np
+    import torch
+    from oracle import attend as o_attend
+    from oracle import stream as o_stream
+
+    n_call = cfgs.chunk_tokens
+    H, T, d, Tq = cfgs.n_heads, cfgs.tokens, cfgs.head_dim, cfgs.q_tokens
+    streams = [o_stream.Stream(1, d, cfgs.n_clusters, cfgs.iters, cfgs.n_stages, cfgs.bits, cfgs.group, "bf16")
+               for _ in range(2)]
+    t = time.perf_counter()
+    calls = 0
+    while calls < T // n_call and time.perf_counter() - t < budget_s * 2 / 3:
+        for s, x in zip(streams, (k_l0, v_l0)):
+            s.encode(x[0:1, calls * n_call:(calls + 1) * n_call].float().cpu().numpy())
+        calls += 1
+    t_enc = time.perf_counter() - t
+    nq = 256
+    q = q_l0[0:1, :nq].float().cpu().numpy()
+    t = time.perf_counter()
+    o_attend.attend(q, streams[0].xhat(), streams[1].xhat())
+    t_att = time.perf_counter() - t
+    keys = calls * n_call
+    enc_per_token = t_enc / (2 * keys)                 # per token of one stream
+    att_per_pair = t_att / (nq * keys)
+    step_s = enc_per_token * 2 * n_layers * H * step_tokens + att_per_pair * n_layers * H * Tq * T
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"value": round(n_layers * Tq / step_s, 6), "unit": "query tokens/s", "cores": cores,
+            "blas_threads": torch.get_num_threads(), "kind": "oracle",
+            "seconds": round(t_enc + t_att, 2),
+            "sample": f"long_rollout layer 0, head 0: oracle encode of the first {calls} calls of 4680 tokens "
+                      f"(K and V, warm-started; {t_enc:.1f} s), attention of {nq} queries over those {keys} keys "
+                      f"({t_att:.2f} s); per-token encode and per-(query, key) attention times scaled to one "
+                      f"step over {n_layers} layers x {H} heads (chunk encode + 4680-query attention over "
+                      f"{T} keys)"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; the path shards by heads/layers "
-                          "with no exchange (see the design notes), but no multi-GPU run exists"}))
+        print(json.dumps({"error": "bench.py measures one GPU; the path would shard by heads and layers "
+                          "with no exchange, and no multi-GPU run is made"}))
         sys.exit(2)
     if args.xlayer:
         xlayer_main(args)
@@ -421,36 +504,60 @@ def main():
     import synth
 
     dev = torch.device("cuda:0")
-    cfgs = synth.WAN_LAYER
+    L = args.layers or 30
+    cfgs = synth.scaled(synth.LONG_ROLLOUT, n_layers=L)
     H, T, d, Tq = cfgs.n_heads, cfgs.tokens, cfgs.head_dim, cfgs.q_tokens
-    cfg = qkv.config(1, H, d, cfgs.n_clusters, cfgs.n_stages, cfgs.bits, cfgs.group,
-                     kmeans_iters=cfgs.iters, max_tokens=T, max_chunks=1, kv_dtype=qkv.QKV_BF16,
-                     max_query_tokens=Tq)
+    S, b, G, C = cfgs.n_stages, cfgs.bits, cfgs.group, cfgs.n_clusters
+    n_call = cfgs.chunk_tokens
+    n_calls = T // n_call
+    Tf = T + n_call
+    cfg = qkv.config(L, H, d, C, S, b, G, kmeans_iters=cfgs.iters, max_tokens=Tf, max_chunk_tokens=n_call,
+                     max_chunks=n_calls + 1, kv_dtype=qkv.QKV_BF16, max_query_tokens=Tq)
     codec = qkv.Codec(cfg, device=dev)
-    k = synth.kv_tokens(cfgs, 0, 0, 0, T, device=dev)
-    v = synth.kv_tokens(cfgs, 0, 1, 0, T, device=dev)
-    q = synth.queries(cfgs, 0, Tq, device=dev)
-    rec = torch.empty((2, 1, H, T, d), dtype=torch.bfloat16, device=dev)
-    out = torch.empty((H, Tq, d), dtype=torch.float32, device=dev)
+    # build the cache: 40 calls of 4680 tokens per layer (untimed)
+    t_build = time.perf_counter()
+    new_k = torch.empty((L, H, n_call, d), dtype=torch.bfloat16, device=dev)
+    new_v = torch.empty_like(new_k)
+    k0 = v0 = None
+    for l in range(L):
+        k = synth.kv_tokens(cfgs, l, 0, 0, Tf, device=dev)
+        v = synth.kv_tokens(cfgs, l, 1, 0, Tf, device=dev)
+        for i in range(n_calls):
+            codec.encode_chunk(k[:, i * n_call:(i + 1) * n_call], v[:, i * n_call:(i + 1) * n_call], layer0=l)
+        new_k[l].copy_(k[:, T:])
+        new_v[l].copy_(v[:, T:])
+        if l == 0:
+            k0, v0 = k, v
+        del k, v
+    qs = torch.stack([synth.queries(cfgs, l, Tq, device=dev) for l in range(L)])
+    torch.cuda.synchronize()
+    print(f"# built {L} layers x {T} tokens in {time.perf_counter() - t_build:.1f} s", file=sys.stderr, flush=True)
+    out = torch.empty((H, Tq, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((H, Tq), dtype=torch.float32, device=dev)
-
-    ev = {name: [] for name in ("encode", "reconstruct", "attend")}
+    rec = torch.empty((L, H, Tf, d), dtype=torch.bfloat16, device=dev)
+    ev = {name: [] for name in ("attend", "encode", "reconstruct", "rewind")}
+    att_calls = []
 
     def step(record):
-        codec.rewind(0, 1, 0)
-        marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
-        if record: marks[0].record()
-        codec.encode_chunk(k, v)
-        if record: marks[1].record()
-        codec.reconstruct(0, 1, 0, 0, T, out=rec[0])
-        codec.reconstruct(0, 1, 1, 0, T, out=rec[1])
-        if record: marks[2].record()
-        codec.attend(0, q, out=out, lse=lse)
+        m = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        a = [torch.cuda.Event(enable_timing=True) for _ in range(L + 1)]
+        m[0].record()
+        a[0].record()
+        for l in range(L):
+            codec.attend(l, qs[l], out=out, lse=lse)
+            a[l + 1].record()
+        m[1].record()
+        codec.encode_chunk(new_k, new_v, layer0=0)
+        m[2].record()
+        codec.reconstruct(0, L, 0, 0, Tf, out=rec)
+        codec.reconstruct(0, L, 1, 0, Tf, out=rec)
+        m[3].record()
+        codec.rewind(0, L, T)
+        m[4].record()
         if record:
-            marks[3].record()
-            ev["encode"].append((marks[0], marks[1]))
-            ev["reconstruct"].append((marks[1], marks[2]))
-            ev["attend"].append((marks[2], marks[3]))
+            for i, n in enumerate(ev):
+                ev[n].append((m[i], m[i + 1]))
+            att_calls.extend(zip(a[:-1], a[1:]))
 
     for _ in range(args.warmup):
         step(False)
@@ -461,43 +568,96 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     print(f"# timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
-
-    def avg_ms(name):
-        xs = [a.elapsed_time(b) for a, b in ev[name]]
-        return sum(xs) / len(xs)
-
-    ms = {n: avg_ms(n) for n in ev}
+    ms = {n: _avg_ms(p) for n, p in ev.items()}
+    ms_attend_call = _avg_ms(att_calls)
     ms_step = wall * 1e3 / args.steps
-    n_el = 2 * H * T * d                                   # K + V elements
-    kv_bytes = n_el * 2
-    S, b, G = cfgs.n_stages, cfgs.bits, cfgs.group
-    packed_bytes = n_el * (S * b / 8 + S * 4 / G) + 2 * H * T  # codes + meta + ids
+
+    # traced leg (not timed): per-kernel HIP events of two more steps
+    codec.trace(True)
+    for _ in range(2):
+        step(False)
+    torch.cuda.synchronize()
+    kt = codec.trace_read()
+    codec.trace(False)
+
+    def kernel_ms(name):
+        n, tot = kt.get(name, (0, 0.0))
+        return (tot / n, n) if n else (None, 0)
+
+    # algorithmic work per launch
+    id_b = 1
+    tok_packed = S * d * b // 8 + S * (d // G) * 4 + id_b        # bytes per token of one stream
+    enc_tokens = 2 * L * H * n_call                              # tokens of one encode call
+    cb_bytes = C * d * 2
+    quant_bytes = enc_tokens * (2 * d + tok_packed) + 2 * L * H * cb_bytes
+    recon_tokens = L * H * Tf                                    # per reconstruct call (one tensor)
+    recon_bytes = recon_tokens * (tok_packed + 2 * d) + L * H * (n_calls + 1) * cb_bytes
+    assign_flops = enc_tokens * 2.0 * C * d
+    assign_bytes = enc_tokens * (2 * d + id_b) + 2 * L * H * cb_bytes
+    update_bytes = enc_tokens * 2 * d + 2 * L * H * cb_bytes
     att_flops = 4.0 * H * Tq * T * d
-    att_tflops = att_flops / (ms["attend"] * 1e-3) / 1e12
-    codebook_bytes = 2 * H * cfgs.n_clusters * d * 2
-    recon_gbs = (packed_bytes + codebook_bytes + n_el * 2) / (ms["reconstruct"] * 1e-3) / 1e9
-    encode_gbs = (kv_bytes + packed_bytes) / (ms["encode"] * 1e-3) / 1e9
+    hbm_ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+
+    def hbm(name, nbytes, kernel):
+        t, n = kernel_ms(kernel)
+        if t is None:
+            return None
+        gbs = nbytes / (t * 1e-3) / 1e9
+        return {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "launch_ms": round(t, 4),
+                "launches": n, "bytes_per_launch": int(nbytes)}
+
+    rooflines = {}
+    t_att, n_att = kernel_ms("k_attend3")
+    if t_att:
+        tf = att_flops / (t_att * 1e-3) / 1e12
+        rooflines["attend"] = {"kernel": "k_attend3", "bound": "mfma", "achieved": round(tf, 2),
+                               "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                               "launch_ms": round(t_att, 4), "launches": n_att, "flops_per_launch": att_flops}
+    rooflines["quantize"] = hbm("quantize", quant_bytes, "k_quantize")
+    rooflines["reconstruct"] = hbm("reconstruct", recon_bytes, "k_reconstruct")
+    rooflines["update"] = hbm("update", update_bytes, "k_update_sorted")
+    t_as, n_as = kernel_ms("k_assign_mfma")
+    if t_as:
+        tf = assign_flops / (t_as * 1e-3) / 1e12
+        cap = min(1.0, (assign_flops / assign_bytes) / hbm_ridge)
+        rooflines["assign"] = {"kernel": "k_assign_mfma", "bound": "mfma", "achieved": round(tf, 2),
+                               "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                               "hbm_cap_frac": round(cap, 4), "launch_ms": round(t_as, 4), "launches": n_as,
+                               "flops_per_launch": assign_flops, "bytes_per_launch": int(assign_bytes)}
+    kernels = {k: {"launches": n, "avg_ms": round(tot / n, 4)} for k, (n, tot) in kt.items()}
+
+    att_tflops = att_flops / (ms_attend_call * 1e-3) / 1e12
     result = {
         "metric": "KV quantize+pack GB/s and fused dequant-attention tokens/s; % of HBM/MFMA peak",
-        "value": round(kv_bytes / (ms_step * 1e-3) / 1e9, 3),
-        "unit": "GB/s (bf16 K+V cache bytes through encode + reconstruct + attend per step)",
+        "value": round(L * Tq / (ms_step * 1e-3), 1),
+        "unit": "query tokens/s (a 4680-token chunk through all 30 layers' packed caches, per whole step: "
+                "attention + the chunk's encode + full reconstruct)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic (seeded prototype/drift/outlier generator)",
-        "config": {"workload": "wan_layer: K,V bf16 [12, 32760, 128], C=256, 5 iters, 2-stage INT2 "
-                               "G=32; 4680 bf16 queries", "heads": H, "tokens": T, "head_dim": d,
-                   "clusters": cfgs.n_clusters, "stages": S, "bits": b, "group": G, "q_tokens": Tq},
-        "calls_ms": {n: round(x, 4) for n, x in ms.items()},
-        "encode_GBps": round(encode_gbs, 2),
-        "reconstruct_GBps": round(recon_gbs, 2),
-        "attend_q_tokens_per_s": round(Tq / (ms["attend"] * 1e-3), 1),
+        "dtype": "bf16", "data": "synthetic (seeded prototype/drift/outlier generator, device-generated)",
+        "config": {"workload": f"long_rollout: {L} layers x K,V bf16 [12, 187200, 128] (34.5 GB at 30 layers) "
+                               "built by 40 calls of 4680 tokens per layer; C=256, 5 iters, 3-stage INT2 G=32; "
+                               "step = 4680 bf16 queries attend each layer, the next 4680-token chunk is encoded "
+                               "into all layers, every layer reconstructed (bf16)",
+                   "layers": L, "heads": H, "tokens": T, "head_dim": d, "clusters": C, "stages": S, "bits": b,
+                   "group": G, "q_tokens": Tq, "chunk_tokens": n_call},
+        "calls_ms": {"attend_per_layer": round(ms_attend_call, 4), "attend_all_layers": round(ms["attend"], 4),
+                     "encode_chunk_all_layers": round(ms["encode"], 4),
+                     "reconstruct_all_layers_k_and_v": round(ms["reconstruct"], 4),
+                     "rewind": round(ms["rewind"], 4)},
+        "attend_q_tokens_per_s": round(L * Tq / (ms["attend"] * 1e-3), 1),
         "attend_TFLOPs": round(att_tflops, 2),
-        "roofline": {"kernel": "qkv_attend (k_attend3 + k_attend_merge)", "bound": "mfma",
+        "encode_GBps": round((enc_tokens * (2 * d + tok_packed)) / (ms["encode"] * 1e-3) / 1e9, 2),
+        "reconstruct_GBps": round(2 * recon_bytes / (ms["reconstruct"] * 1e-3) / 1e9, 2),
+        "roofline": {"kernel": "qkv_attend (k_attend3 + k_attend_merge), per layer", "bound": "mfma",
                      "achieved": round(att_tflops, 3), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(att_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": recorded_traffic(os.path.join(ROOT, "kv_cache_quantization_head_amd",
-                                                              "csrc", "kernels.hip"))},
+                                                              "csrc", "attend.hip"))},
+        "rooflines": rooflines,
+        "kernels_traced": kernels,
     }
     if args.copy_calibration:
         src = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
@@ -507,7 +667,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfgs, k, v, q)
+        result["cpu_baseline"] = rollout_cpu_baseline(cfgs, k0, v0, qs[0], L, n_call)
+    del codec, rec, k0, v0, qs, new_k, new_v
+    torch.cuda.empty_cache()
+    if not args.no_wan_layer:
+        result["wan_layer"] = wan_layer_step(args)
     print(json.dumps(result), flush=True)
 
 

@@ -224,6 +224,25 @@ int qkv_chunk_starts(const qkv_ctx *ctx, int32_t layer, int64_t *starts, int32_t
  * stream was last empty.  Errors: QKV_E_INVAL (not adapted mode, bad layer). */
 int qkv_adapted_blocks(const qkv_ctx *ctx, int32_t layer, uint64_t *offset);
 
+/* Per-kernel timing, for measurement.  With enable = 1 every later call on
+ * ctx records a HIP event on its stream before and after each kernel it
+ * launches (the events are created by the library and reused); enable = 0
+ * stops recording.  Tracing adds a small gap between kernels, so timed
+ * regions should run with it off.  Errors: QKV_E_INVAL. */
+int qkv_trace(qkv_ctx *ctx, int32_t enable);
+
+typedef struct {
+  char name[64];           /* kernel base name, e.g. "k_attend3" */
+  int64_t launches;        /* launches recorded since the last read */
+  double total_ms;         /* sum of their event-to-event times */
+} qkv_trace_entry;
+
+/* Wait for every recorded event, add the intervals up per kernel name (in
+ * order of first launch), write up to max entries to out (out may be NULL)
+ * and forget the records.  Returns the number of distinct kernels, or a
+ * negative status (QKV_E_INVAL, QKV_E_HIP). */
+int qkv_trace_read(qkv_ctx *ctx, qkv_trace_entry *out, int32_t max);
+
 /* Release the context (not the caller's device memory). */
 void qkv_destroy(qkv_ctx *ctx);
 

@@ -42,6 +42,10 @@ class qkv_layout_desc(ctypes.Structure):
         (n, ctypes.c_uint64) for n in ("chmask_off", "chmask_chunk_stride", "chmask_head_stride")]
 
 
+class qkv_trace_entry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 64), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
+
+
 _lib = None
 
 
@@ -80,6 +84,10 @@ def lib():
     L.qkv_chunk_starts.restype = ctypes.c_int
     L.qkv_adapted_blocks.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_uint64)]
     L.qkv_adapted_blocks.restype = ctypes.c_int
+    L.qkv_trace.argtypes = [vp, i32]
+    L.qkv_trace.restype = ctypes.c_int
+    L.qkv_trace_read.argtypes = [vp, ctypes.POINTER(qkv_trace_entry), i32]
+    L.qkv_trace_read.restype = ctypes.c_int
     L.qkv_destroy.argtypes = [vp]
     L.qkv_destroy.restype = None
     L.qkv_status_string.argtypes = [vp, ctypes.c_int]
@@ -223,6 +231,18 @@ class Codec:
 
     def rewind(self, layer0, n_layers, n_tokens):
         _check(lib().qkv_rewind(self.ctx, layer0, n_layers, n_tokens, _stream()), self.ctx)
+
+    def trace(self, enable=True):
+        """Record HIP events around every kernel of later calls (qkv_trace)."""
+        _check(lib().qkv_trace(self.ctx, 1 if enable else 0), self.ctx)
+
+    def trace_read(self):
+        """{kernel: (launches, total ms)} since the last read (synchronizes)."""
+        buf = (qkv_trace_entry * 64)()
+        n = lib().qkv_trace_read(self.ctx, buf, 64)
+        if n < 0:
+            _check(n, self.ctx)
+        return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(n, 64))}
 
     def layout(self, layer, kv):
         d = qkv_layout_desc()

@@ -1,6 +1,6 @@
 // C-ABI entry points of the qkv library (see include/qkv.h).  Each call
 // validates its arguments on the host (plan.cpp), then enqueues the kernels
-// of kernels.hip on the caller's stream and updates the host bookkeeping.
+// of the kernel sources on the caller's stream and updates the host bookkeeping.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -22,6 +22,104 @@ static int hip_status(qkv_ctx *ctx) {
 }
 
 static uint8_t *scratch(qkv_ctx *ctx, uint64_t off) { return ctx->arena + ctx->plan.scratch_off + off; }
+
+namespace qkv {
+thread_local TraceSink *t_trace = nullptr;
+}
+
+// Records the launches of one call on ctx while tracing is on: installed as
+// the thread's trace sink for the lifetime of the scope.
+class TraceScope final : public TraceSink {
+ public:
+  explicit TraceScope(qkv_ctx *ctx) : ctx_(ctx) {
+    if (ctx_->trace) t_trace = this;
+  }
+  ~TraceScope() {
+    if (t_trace == this) t_trace = nullptr;
+  }
+  void begin(const char *label, hipStream_t st) override {
+    // "(k_name<...>)" -> "k_name"
+    const char *p = label;
+    while (*p == '(' || *p == ' ') ++p;
+    const char *e = p;
+    while (*e && *e != '<' && *e != ')' && *e != ' ') ++e;
+    name_.assign(p, size_t(e - p));
+    open_ = event();
+    if (open_) (void)hipEventRecord(static_cast<hipEvent_t>(open_), st);
+  }
+  void end(hipStream_t st) override {
+    void *close = event();
+    if (!open_ || !close) return;
+    (void)hipEventRecord(static_cast<hipEvent_t>(close), st);
+    ctx_->trace_marks.push_back({name_, open_, close});
+    open_ = nullptr;
+  }
+
+ private:
+  void *event() {
+    if (ctx_->trace_used == ctx_->trace_pool.size()) {
+      hipEvent_t ev = nullptr;
+      if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+      ctx_->trace_pool.push_back(ev);
+    }
+    return ctx_->trace_pool[ctx_->trace_used++];
+  }
+  qkv_ctx *ctx_;
+  void *open_ = nullptr;
+  std::string name_;
+};
+
+extern "C" void qkv_destroy(qkv_ctx *ctx) {
+  if (!ctx) return;
+  for (void *ev : ctx->trace_pool) (void)hipEventDestroy(static_cast<hipEvent_t>(ev));
+  delete ctx;
+}
+
+extern "C" int qkv_trace(qkv_ctx *ctx, int32_t enable) {
+  if (!ctx || (enable != 0 && enable != 1)) return QKV_E_INVAL;
+  ctx->trace = enable;
+  return QKV_OK;
+}
+
+extern "C" int qkv_trace_read(qkv_ctx *ctx, qkv_trace_entry *out, int32_t max) {
+  if (!ctx || max < 0) return QKV_E_INVAL;
+  std::vector<std::string> names;
+  std::vector<int64_t> counts;
+  std::vector<double> sums;
+  int rc = QKV_OK;
+  for (const auto &m : ctx->trace_marks) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(static_cast<hipEvent_t>(m.end)) != hipSuccess ||
+        hipEventElapsedTime(&ms, static_cast<hipEvent_t>(m.begin), static_cast<hipEvent_t>(m.end)) != hipSuccess) {
+      rc = QKV_E_HIP;
+      break;
+    }
+    size_t i = 0;
+    while (i < names.size() && names[i] != m.name) ++i;
+    if (i == names.size()) {
+      names.push_back(m.name);
+      counts.push_back(0);
+      sums.push_back(0.0);
+    }
+    counts[i] += 1;
+    sums[i] += ms;
+  }
+  ctx->trace_marks.clear();
+  ctx->trace_used = 0;
+  if (rc != QKV_OK) {
+    (void)hip_status(ctx);
+    return rc;
+  }
+  for (size_t i = 0; out && i < names.size() && int32_t(i) < max; ++i) {
+    qkv_trace_entry &e = out[i];
+    const size_t n = std::min(names[i].size(), sizeof(e.name) - 1);
+    std::copy(names[i].begin(), names[i].begin() + n, e.name);
+    e.name[n] = 0;
+    e.launches = counts[i];
+    e.total_ms = sums[i];
+  }
+  return int(names.size());
+}
 
 extern "C" int qkv_init(const qkv_config *cfg, void *d_arena, size_t arena_bytes,
                         const void *d_predictor, qkv_ctx **out) {
@@ -94,6 +192,7 @@ extern "C" int qkv_encode_chunk(qkv_ctx *ctx, int32_t layer0, int32_t n_layers, 
                                 const void *d_v, int64_t n, void *stream) {
   const int rc = check_encode(ctx, layer0, n_layers, d_k, d_v, n);
   if (rc != QKV_OK) return rc;
+  TraceScope trace(ctx);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Plan &p = ctx->plan;
   const qkv_config &c = p.cfg;
@@ -192,6 +291,7 @@ extern "C" int qkv_attend(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t 
   const int rc = check_attend(ctx, layer, d_q, n_q, q_dtype, d_out, out_dtype);
   if (rc != QKV_OK) return rc;
   if (n_q == 0) return QKV_OK;
+  TraceScope trace(ctx);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Plan &p = ctx->plan;
   const int64_t n_keys = ctx->layers[layer].n_tokens;
@@ -230,6 +330,7 @@ extern "C" int qkv_attend_with_chunk(qkv_ctx *ctx, int32_t layer, const void *d_
   if (n_q == 0) return QKV_OK;
   const int64_t n_cache = ctx->layers[layer].n_tokens;
   if (n_new == 0) return qkv_attend(ctx, layer, d_q, n_q, q_dtype, d_out, out_dtype, d_lse, stream);
+  TraceScope trace(ctx);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Plan &p = ctx->plan;
   const qkv_config &c = p.cfg;
@@ -303,6 +404,7 @@ extern "C" int qkv_reconstruct(qkv_ctx *ctx, int32_t layer0, int32_t n_layers, i
   const int rc = check_reconstruct(ctx, layer0, n_layers, kv, t0, t1, d_out, out_dtype);
   if (rc != QKV_OK) return rc;
   if (t1 == t0) return QKV_OK;
+  TraceScope trace(ctx);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Plan &p = ctx->plan;
   const qkv_config &c = p.cfg;
@@ -360,6 +462,7 @@ extern "C" int qkv_reconstruct(qkv_ctx *ctx, int32_t layer0, int32_t n_layers, i
 extern "C" int qkv_rewind(qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int64_t n_tokens, void *stream) {
   const int rc = check_rewind(ctx, layer0, n_layers, n_tokens);
   if (rc != QKV_OK) return rc;
+  TraceScope trace(ctx);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const DevLayout L = dev_layout(ctx->plan);
   bool launched = false;

@@ -1,0 +1,623 @@
+// Fused read of the qkv library: split-KV attention over the packed cache
+// (tiles rebuilt in bf16 in LDS, bf16 MFMA products, online softmax), the
+// uncoded read of a fresh chunk, and the LSE merges.
+#include "common.h"
+
+namespace qkv {
+
+// -------------------------------------------------------------- attention
+//
+// Fused read of the packed cache.  Block = 8 waves (two per SIMD) = 256
+// queries of one head, 32 per wave; the (head, query block, key tile) units
+// are split stream-K style over the blocks.  Per 64-key tile the block
+// rebuilds K and V in bf16 into a double-buffered LDS tile (both as
+// [key][d]); each wave then computes S^T = K Q^T for its 32 queries with
+// v_mfma_f32_32x32x16_bf16 (a lane's accumulators hold 32 keys of one query;
+// lanes l and l^32 share the query, so the softmax statistics need one
+// cross-lane exchange), runs the online softmax in fp32 and accumulates
+// O^T += V^T P^T with the probabilities rounded to bf16.  V^T comes from
+// the row-major V tile through transposing LDS loads.  The key order inside
+// each 16-key MFMA step is permuted identically in both operands so that
+// P^T comes straight from the S^T accumulators.
+//
+//  * Rebuild items: one (tensor, key, 32 channels) per thread, K on even and
+//    V on odd threads (every wave runs the same code, stores included; the
+//    threads of a key read one centroid row).  The rebuild is
+//    bf16(fl32 chain: c + sum_s z_s, then fmaf(q_s, sigma_s, .) per stage);
+//    2-bit codes are widened four at a time from one masked code word
+//    (byte-to-float conversions).  Keys past the end rebuild to zero from
+//    zeroed registers.
+//  * Loads are software-pipelined: ids of tile i+2 and the packed data
+//    (codes, scale/zero, centroid rows) of tile i+1 are in flight while tile
+//    i is rebuilt and multiplied; half of the waves multiply before they
+//    rebuild and half after, so that the MFMA work of one wave of a SIMD
+//    overlaps the VALU work of the other.  The chunk table is cached in LDS.
+//  * The softmax scale is folded into the exponent's fma; the running max is
+//    only raised (and O, l rescaled) when a tile's max exceeds it by more
+//    than 8 (log2 units), so exponentials stay <= 256; row sums of P are
+//    accumulated from the bf16 probabilities with v_dot2_f32_bf16.
+constexpr int AT_WAVES = 8;
+constexpr int AT_BQ = 32 * AT_WAVES;
+constexpr int AT_BK = 64;
+
+// Transposing LDS load (ds_read_b64_tr_b16): within each 16-lane group,
+// lane l receives element l%4 of the 8-byte rows addressed by lanes
+// l/4 + 4j (j = 0..3), as element j.
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x4 lds_read_tr16(const uint16_t *p) {
+  const shortx4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4 *)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+// max / sum of the values of lanes l and l^32, identical on both lanes
+// (v_permlane32_swap_b32 hands each half the other half's values)
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ int chunk_of_lds(const int32_t *starts, int n_chunks, int t) {
+  int lo = 0, hi = n_chunks - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (starts[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+constexpr float AT3_TAU = 8.0f;
+
+// w[i] for a run-time i < N (selects, no indexed register access)
+template <int N>
+__device__ __forceinline__ uint32_t pick_word(const uint32_t *w, int i) {
+  if constexpr (N == 2) return i ? w[1] : w[0];
+  else return (i & 2) ? ((i & 1) ? w[3] : w[2]) : ((i & 1) ? w[1] : w[0]);
+}
+
+template <int D, int G, int BITS, bool CB_BF16, int SMAX, bool FRESH = false, bool OUTL = false>
+__global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
+  // SMAX = the number of PRQ stages (a template parameter so that the staging
+  // registers are sized exactly).  FRESH: the keys and values are the
+  // uncoded bf16 rows a.k_new / a.v_new ([H][n_keys][D]) of the chunk being
+  // generated; an item is then copied to LDS as read.  OUTL: channels flagged
+  // in the mask of the key's chunk take the outlier group's (sigma, z)
+  // (meta entry D/G).
+  constexpr int IC = 32;                   // channels of one rebuild item
+  constexpr int NI = D / IC;               // items per key and tensor
+  constexpr int KP = D + 8;                // bf16 elements per K row in LDS
+  constexpr int VP = D + 32;               // bf16 elements per V row in LDS (the 4 rows x
+                                           // 64 bytes of a transposing read by 32 lanes
+                                           // fall in distinct banks)
+  constexpr int EB = CB_BF16 ? 2 : 4;
+  constexpr int KW = IC * BITS / 32;       // code words of an item
+  constexpr int KC = IC * EB / 16;         // uint4 of an item's centroid slice
+  static_assert(2 * 64 * NI <= 512, "one item per thread");
+  static_assert(G % IC == 0, "an item lies inside one quantization group");
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][AT_BK * KP];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][AT_BK * VP];
+  __shared__ int32_t starts_s[kMaxChunks + 1];
+  __shared__ int32_t nch_s;
+  // OUTL: the segment head's mask words of every chunk, per tensor
+  __shared__ uint32_t masks_s[2][OUTL ? kMaxChunks * (D / 32) : 1];
+
+  const DevLayout &L = a.L;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int hh = lane >> 5, c32 = lane & 31;
+  const float sc = 1.4426950408889634f / sqrtf(float(D));
+  constexpr int NS = D / 16, NDB = D / 32;
+  // lane's transposing-read address in a V tile: key 4*hh + (lane%16)/4 of a
+  // 16-key step, channels 16*((lane/16)%2) + 4*(lane%4) .. +3 of a 32-channel block
+  const int v_lane = (4 * hh + ((lane & 15) >> 2)) * VP + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  // Rebuild items: one (tensor, key, 32 channels) per thread, K on even and
+  // V on odd threads, so every wave runs the same rebuild code and the
+  // threads of one key read one centroid row.  K and V tiles are
+  // both stored [key][d]; the PV step reads V with transposing LDS loads.
+  const int it_kv = tid & 1, it_rem = tid >> 1;
+  const bool has_item = it_rem < 64 * NI;
+  const int it_key = it_rem / NI;
+  const int it_ch = (it_rem % NI) * IC, it_g = it_ch / G;
+  const uint8_t *st = it_kv ? a.stream_v : a.stream_k;
+
+  if constexpr (FRESH) {
+    if (tid == 0) nch_s = 1;
+  } else {
+    if (tid == 0) nch_s = ((const StreamHeader *)(a.stream_k + L.header_off))->n_chunks;
+    __syncthreads();
+    for (int i = tid; i < nch_s; i += blockDim.x)
+      starts_s[i] = ((const StreamHeader *)(a.stream_k + L.header_off))->start[i];
+  }
+
+  // Stream-K work split: the (head, query block, key tile) units are dealt
+  // out in equal consecutive runs, one run per block; a block walks its run
+  // segment by segment (one segment per query block it touches).  A segment
+  // that covers all key tiles of its query block writes the result; the
+  // others write a partial (O, LSE) into slot (block - first block of the
+  // query block) for the merge kernel.  Blocks are numbered so that each XCD
+  // (blocks are dealt to the 8 XCDs round robin) gets a consecutive range of
+  // runs: the query blocks of one head then share that XCD's L2.
+  const int lb = a.xcd_remap ? (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int64_t T = a.n_ktiles, U = a.units_per_block;
+  const int64_t total = T * a.n_qblocks * L.H;
+  int64_t u = int64_t(lb) * U;
+  const int64_t u_end = min(total, u + U);
+  __syncthreads();  // chunk table in LDS
+  while (u < u_end) {
+    const int64_t seg = u / T;
+    const int h = int(seg / a.n_qblocks), qblk = int(seg % a.n_qblocks);
+    const int t0 = int(u % T);
+    const int t1 = int(min(T, t0 + (u_end - u)));
+    const int slot = (t0 == 0 && t1 == T) ? -1 : int(lb - (seg * T) / U);
+    u += t1 - t0;
+    const uint8_t *idp = FRESH ? nullptr : st + L.ids_off + uint64_t(h) * L.ids_head;
+    const int ks = t0 * AT_BK;
+    const int ke = min(a.n_keys, t1 * AT_BK);
+    const int n_tiles = ke > ks ? (ke - ks + AT_BK - 1) / AT_BK : 0;
+
+    if constexpr (OUTL) {
+      // written after the previous segment's last tile barrier, read after
+      // the barrier before this segment's first rebuild
+      constexpr int MW = D / 32;
+      const int per = nch_s * MW;
+      for (int i = tid; i < 2 * per; i += blockDim.x) {
+        const int kv = i / per, c = (i % per) / MW, w = i % MW;
+        masks_s[kv][c * MW + w] = *(const uint32_t *)((kv ? a.stream_v : a.stream_k) + L.mask_off +
+                                                       uint64_t(c) * L.mask_chunk + uint64_t(h) * L.mask_head + 4 * w);
+      }
+    }
+    const int q = qblk * AT_BQ + wave * 32 + c32;
+    // B operand of S^T = K Q^T, k-step s: Q[q][16 s + 8 hh .. +8] in bf16
+    bf16x8 qf[NS];
+  #pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      bf16x8 v;
+      if (q < a.n_q) {
+        const uint64_t off = (uint64_t(h) * a.n_q + q) * D + s * 16 + hh * 8;
+        if (a.q_bf16) {
+          v = *(const bf16x8 *)((const uint16_t *)a.q + off);
+        } else {
+          const float *qp = (const float *)a.q + off;
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = (__bf16)qp[e];
+        }
+      } else {
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+      }
+      qf[s] = v;
+    }
+    bf16x2 ones2;
+    ones2[0] = (__bf16)1.0f;
+    ones2[1] = (__bf16)1.0f;
+    floatx16 o[NDB];
+  #pragma unroll
+    for (int db = 0; db < NDB; ++db)
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+    float l_part = 0.0f;       // this lane's share of the row sum
+    float m_run = -INFINITY;
+
+    // id of the item's key in a tile (-1: no key)
+    auto load_ids = [&](int tile) -> int {
+      if (!has_item || tile >= n_tiles) return -1;
+      const int t = ks + tile * AT_BK + it_key;
+      if (t >= ke) return -1;
+      if constexpr (FRESH) return 0;
+      return L.id_bytes == 1 ? int(idp[t]) : int(((const uint16_t *)idp)[t]);
+    };
+    struct Regs {
+      uint32_t codes[SMAX][KW];
+      uint32_t meta[SMAX];
+      uint4 cent[KC];
+    } R;
+    // per-item pointers of the segment (key t = ks + AT_BK * tile + it_key)
+    const int t_first = ks + it_key;
+    const uint8_t *code_p = FRESH ? nullptr : st + L.codes_off + uint64_t(h) * L.codes_head +
+                                              uint64_t(t_first) * L.codes_token + it_ch * BITS / 8;
+    const uint8_t *meta_p = FRESH ? nullptr : st + L.meta_off + uint64_t(h) * L.meta_head +
+                                              uint64_t(t_first) * L.meta_token + 4 * it_g;
+    const uint8_t *cb_p = FRESH ? nullptr : st + L.cb_off + uint64_t(h) * L.cb_head + uint64_t(it_ch) * EB;
+    // fresh rows: channels it_ch .. it_ch+31 of key t_first of head h
+    const uint16_t *fresh_p = FRESH ? (it_kv ? a.v_new : a.k_new) + (uint64_t(h) * a.n_keys + t_first) * D + it_ch
+                                    : nullptr;
+    const uint64_t tile_codes = uint64_t(AT_BK) * L.codes_token, tile_meta = uint64_t(AT_BK) * L.meta_token;
+    // packed data of the item's key: centroid slice, codes, (sigma, z); all
+    // zero when there is no key, which rebuilds to zero
+    auto load_data = [&](int tile, int id) {
+      if (id < 0) {
+  #pragma unroll
+        for (int i = 0; i < KC; ++i) R.cent[i] = make_uint4(0u, 0u, 0u, 0u);
+  #pragma unroll
+        for (int s2 = 0; s2 < SMAX; ++s2) {
+          R.meta[s2] = 0u;
+  #pragma unroll
+          for (int w = 0; w < KW; ++w) R.codes[s2][w] = 0u;
+        }
+        return;
+      }
+      if constexpr (FRESH) {
+        const uint16_t *row = fresh_p + uint64_t(tile) * AT_BK * D;
+  #pragma unroll
+        for (int i = 0; i < KC; ++i) R.cent[i] = *(const uint4 *)(row + 8 * i);
+        return;
+      }
+      const int cslot = nch_s > 1 ? chunk_of_lds(starts_s, nch_s, ks + tile * AT_BK + it_key) : 0;
+      const uint8_t *crow = cb_p + uint64_t(cslot) * L.cb_chunk + uint64_t(id) * (D * EB);
+  #pragma unroll
+      for (int i = 0; i < KC; ++i) R.cent[i] = *(const uint4 *)(crow + 16 * i);
+      const uint8_t *cp = code_p + uint64_t(tile) * tile_codes;
+      const uint8_t *mp = meta_p + uint64_t(tile) * tile_meta;
+  #pragma unroll
+      for (int s2 = 0; s2 < SMAX; ++s2) {
+        if constexpr (KW == 2) {
+          const uint2 v = *(const uint2 *)(cp + uint64_t(s2) * L.codes_stage);
+          R.codes[s2][0] = v.x; R.codes[s2][1] = v.y;
+        } else {
+  #pragma unroll
+          for (int w = 0; w < KW; w += 4) {
+            const uint4 v = *(const uint4 *)(cp + uint64_t(s2) * L.codes_stage + 4 * w);
+            R.codes[s2][w] = v.x; R.codes[s2][w + 1] = v.y; R.codes[s2][w + 2] = v.z; R.codes[s2][w + 3] = v.w;
+          }
+        }
+        R.meta[s2] = *(const uint32_t *)(mp + uint64_t(s2) * L.meta_stage);
+      }
+    };
+    // one PRQ stage folded into 16 channels: xh[c] = fmaf(q_c, sigma, xh[c]) (the
+    // zero points of all stages are added to the centroid beforehand)
+    auto stage16 = [&](const uint32_t *cw, float sf, float *xh) {
+      float q[16];
+      if constexpr (BITS == 2) {
+        widen_codes2(cw[0], q);
+      } else {
+        widen_codes4(cw[0], q);
+        widen_codes4(cw[1], q + 8);
+      }
+  #pragma unroll
+      for (int c = 0; c < 16; ++c) xh[c] = fmaf(q[c], sf, xh[c]);
+    };
+    // centroid channel e of the item as fp32
+    auto cent_f32 = [&](int e) -> float {
+      if constexpr (CB_BF16) {
+        const uint4 v = R.cent[e >> 3];
+        const uint32_t w = ((e & 7) >> 1) == 0 ? v.x : ((e & 7) >> 1) == 1 ? v.y : ((e & 7) >> 1) == 2 ? v.z : v.w;
+        return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+      } else {
+        const uint4 v = R.cent[e >> 2];
+        const uint32_t w = (e & 3) == 0 ? v.x : (e & 3) == 1 ? v.y : (e & 3) == 2 ? v.z : v.w;
+        return __uint_as_float(w);
+      }
+    };
+    // centroid channel e of the item for a run-time e (a select tree over the
+    // item's registers)
+    auto cent_pick = [&](int e) -> float {
+      if constexpr (CB_BF16) {
+        const int wi = e >> 1;
+        const uint4 a = (wi & 8) ? ((wi & 4) ? R.cent[3] : R.cent[2]) : ((wi & 4) ? R.cent[1] : R.cent[0]);
+        const uint32_t w = (wi & 2) ? ((wi & 1) ? a.w : a.z) : ((wi & 1) ? a.y : a.x);
+        return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+      } else {
+        const int vi = e >> 2;
+        const uint4 a0 = (vi & 2) ? ((vi & 1) ? R.cent[3] : R.cent[2]) : ((vi & 1) ? R.cent[1] : R.cent[0]);
+        const uint4 a1 = (vi & 2) ? ((vi & 1) ? R.cent[7] : R.cent[6]) : ((vi & 1) ? R.cent[5] : R.cent[4]);
+        const uint4 a = (vi & 4) ? a1 : a0;
+        return __uint_as_float((e & 2) ? ((e & 1) ? a.w : a.z) : ((e & 1) ? a.y : a.x));
+      }
+    };
+    // Rebuild the item for the products: xh = fmaf(q_S, sigma_S, ... fmaf(q_1,
+    // sigma_1, c + (z_1 + ... + z_S))), then nearest-even bf16.  This differs
+    // from the stage-by-stage reconstruction (c + rhat_1) + rhat_2 ... by a few
+    // fp32 ulps, which changes the bf16 operand only for values within those
+    // ulps of a bf16 rounding boundary.
+    auto dequant_store = [&](int buf, int tile) {
+      if (!has_item) return;
+      if constexpr (FRESH) {
+        uint16_t *dst = it_kv ? &Vs[buf][it_key * VP + it_ch] : &Ks[buf][it_key * KP + it_ch];
+  #pragma unroll
+        for (int i = 0; i < KC; ++i) *(uint4 *)(dst + 8 * i) = R.cent[i];
+        return;
+      }
+      float xh[IC];
+      float zs = 0.0f;
+  #pragma unroll
+      for (int s2 = 0; s2 < SMAX; ++s2) zs += f16_bits_to_f32(uint16_t(R.meta[s2] >> 16));
+  #pragma unroll
+      for (int e = 0; e < IC; ++e) xh[e] = cent_f32(e) + zs;
+  #pragma unroll
+      for (int s2 = 0; s2 < SMAX; ++s2) {
+        const float sf = f16_bits_to_f32(uint16_t(R.meta[s2] & 0xffffu));
+  #pragma unroll
+        for (int b16 = 0; b16 < IC / 16; ++b16) stage16(&R.codes[s2][b16 * (BITS / 2)], sf, &xh[16 * b16]);
+      }
+      uint16_t *dst = it_kv ? &Vs[buf][it_key * VP + it_ch] : &Ks[buf][it_key * KP + it_ch];
+  #pragma unroll
+      for (int j = 0; j < IC; j += 8)
+        *(uint4 *)(dst + j) = make_uint4(pack_bf16x2(xh[j], xh[j + 1]), pack_bf16x2(xh[j + 2], xh[j + 3]),
+                                         pack_bf16x2(xh[j + 4], xh[j + 5]), pack_bf16x2(xh[j + 6], xh[j + 7]));
+      if constexpr (OUTL) {
+        // channels of the item flagged in the mask of the key's chunk (mask
+        // words in LDS): rebuilt again with the outlier group's (sigma, z) and
+        // the item's registers, stored over the first result; read only
+        // here, so that nothing of it is held during the rebuild
+        uint32_t fm = 0u;
+        uint32_t mo[SMAX];
+        const int t = ks + tile * AT_BK + it_key;
+        if (t < ke) {
+          const int cslot = nch_s > 1 ? chunk_of_lds(starts_s, nch_s, t) : 0;
+          fm = masks_s[it_kv][cslot * (D / 32) + (it_ch >> 5)];
+          if (fm) {
+            const uint8_t *mop = meta_p + uint64_t(tile) * tile_meta + 4 * (D / G - it_g);
+  #pragma unroll
+            for (int s2 = 0; s2 < SMAX; ++s2) mo[s2] = *(const uint32_t *)(mop + uint64_t(s2) * L.meta_stage);
+          }
+        }
+        if (fm) {
+          float so[SMAX];
+          float zso = 0.0f;
+  #pragma unroll
+          for (int s2 = 0; s2 < SMAX; ++s2) {
+            so[s2] = f16_bits_to_f32(uint16_t(mo[s2] & 0xffffu));
+            zso += f16_bits_to_f32(uint16_t(mo[s2] >> 16));
+          }
+          while (fm) {
+            const int e = __builtin_ctz(fm);
+            fm &= fm - 1u;
+            float v = cent_pick(e) + zso;
+  #pragma unroll
+            for (int s2 = 0; s2 < SMAX; ++s2) {
+              const uint32_t w = pick_word<KW>(R.codes[s2], (e * BITS) >> 5);
+              const float qv = float((w >> ((e * BITS) & 31)) & ((1u << BITS) - 1u));
+              v = fmaf(qv, so[s2], v);
+            }
+            dst[e] = f32_to_bf16_bits(v);
+          }
+        }
+      }
+    };
+
+    auto compute_tile = [&](int tile) {
+      const int buf = tile & 1;
+      const int kt0 = ks + tile * AT_BK;
+      // S^T for keys 32*kb + (8*(r/4) + 4*hh + r%4) of the tile, query c32
+      floatx16 s0, s1;
+  #pragma unroll
+      for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
+      const uint16_t *kp = &Ks[buf][c32 * KP + 8 * hh];
+  #pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 k0 = *(const bf16x8 *)(kp + 16 * s);
+        const bf16x8 k1 = *(const bf16x8 *)(kp + 32 * KP + 16 * s);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], s1, 0, 0, 0);
+      }
+      if (kt0 + AT_BK > ke) {
+  #pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key >= ke) s0[r] = -INFINITY;
+          if (key + 32 >= ke) s1[r] = -INFINITY;
+        }
+      }
+      float tmax = -INFINITY;
+  #pragma unroll
+      for (int r = 0; r < 16; ++r)
+        tmax = __builtin_elementwise_maximum(tmax, __builtin_elementwise_maximum(s0[r], s1[r]));
+      tmax = pair_max(tmax);
+      const float mt = tmax * sc;
+      const bool need = mt > m_run + AT3_TAU;
+      if (__any(need)) {
+        const float mnew = need ? mt : m_run;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - mnew) : 1.0f;
+        m_run = mnew;
+  #pragma unroll
+        for (int db = 0; db < NDB; ++db) o[db] *= alpha;
+        l_part *= alpha;
+      }
+      const float nm = -m_run;
+      // O^T += V^T P^T over 16-key steps (kb, jj).  B operand: lane registers
+      // 8*jj .. 8*jj+7 of S^T block kb, i.e. k index 8*hh + e <-> key
+      // 32*kb + 16*jj + 8*(e/4) + 4*hh + e%4.  A operand (V^T, rows = channels
+      // 32*db + lane%32): two transposing loads, keys 32*kb + 16*jj + 4*hh +
+      // 0..3 and the same + 8.
+      const uint16_t *vp = &Vs[buf][v_lane];
+  #pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+  #pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          bf16x8 pb;
+  #pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pb[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(kb ? s1[8 * jj + e] : s0[8 * jj + e], sc, nm));
+          const uint4 w = __builtin_bit_cast(uint4, pb);
+          l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.x), ones2, l_part, false);
+          l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.y), ones2, l_part, false);
+          l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.z), ones2, l_part, false);
+          l_part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w.w), ones2, l_part, false);
+  #pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            const bf16x4 lo = lds_read_tr16(vp + (32 * kb + 16 * jj) * VP + 32 * db);
+            const bf16x4 hi = lds_read_tr16(vp + (32 * kb + 16 * jj + 8) * VP + 32 * db);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                            pb, o[db], 0, 0, 0);
+          }
+        }
+    };
+
+    // Pipeline: at iteration i every wave rebuilds tile i+1 from data loaded
+    // during iteration i-1 and issues the loads of tile i+2 (ids of tile i+3);
+    // one barrier per tile.  Two waves share each SIMD; half of the waves
+    // multiply tile i before rebuilding and half after, so one wave's MFMA work
+    // overlaps its partner's VALU work.  The split flips between waves w and
+    // w+4 and between waves 2k and 2k+1, whichever way waves sit on SIMDs.
+    const bool mfma_first = ((wave >> 2) ^ wave) & 1;
+    __syncthreads();  // previous segment's tiles no longer read
+    int id_next;   // id of the item's key in tile+2
+    load_data(0, load_ids(0));
+    dequant_store(0, 0);
+    load_data(1, load_ids(1));
+    id_next = load_ids(2);
+    __syncthreads();
+
+    for (int tile = 0; tile < n_tiles; ++tile) {
+      const int buf = tile & 1;
+      if (mfma_first) compute_tile(tile);
+      if (tile + 1 < n_tiles) dequant_store(buf ^ 1, tile + 1);   // data of tile+1 already in R
+      load_data(tile + 2, id_next);
+      id_next = load_ids(tile + 3);
+      if (!mfma_first) compute_tile(tile);
+      __syncthreads();
+    }
+
+    const float l = pair_sum(l_part);
+    if (q < a.n_q) {
+      const bool empty = !(l > 0.0f);
+      const float inv_l = empty ? 0.0f : 1.0f / l;
+      const float lse = empty ? -INFINITY : (m_run + log2f(l)) * 0.6931471805599453f;
+      // lane holds channels 32*db + 8*j + 4*hh + 0..3 in o[db][4j .. 4j+3]
+      if (slot < 0) {
+  #pragma unroll
+        for (int db = 0; db < NDB; ++db)
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint64_t off = (uint64_t(h) * a.n_q + q) * D + 32 * db + 8 * j + 4 * hh;
+            const float v0 = o[db][4 * j] * inv_l, v1 = o[db][4 * j + 1] * inv_l;
+            const float v2 = o[db][4 * j + 2] * inv_l, v3 = o[db][4 * j + 3] * inv_l;
+            if (a.out_bf16)
+              *(uint2 *)((uint16_t *)a.out + off) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
+            else
+              *(float4 *)((float *)a.out + off) = make_float4(v0, v1, v2, v3);
+          }
+        if (a.lse && hh == 0) a.lse[uint64_t(h) * a.n_q + q] = lse;
+      } else {
+  #pragma unroll
+        for (int db = 0; db < NDB; ++db)
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint64_t off = ((uint64_t(slot) * L.H + h) * a.n_q + q) * D + 32 * db + 8 * j + 4 * hh;
+            *(float4 *)(a.part_o + off) = make_float4(o[db][4 * j] * inv_l, o[db][4 * j + 1] * inv_l,
+                                                      o[db][4 * j + 2] * inv_l, o[db][4 * j + 3] * inv_l);
+          }
+        if (hh == 0) a.part_lse[(uint64_t(slot) * L.H + h) * a.n_q + q] = lse;
+      }
+    }
+  }
+}
+
+// Merge the partials of query blocks shared by several blocks:
+// O = sum_s w_s O_s / sum_s w_s with w_s = exp(lse_s - max).  One thread per
+// (query, 4 channels); blockIdx.y = head.  Query blocks covered by one block
+// were written directly and are skipped.
+__global__ __launch_bounds__(256) void k_attend_merge(AttnArgs a) {
+  const int D = a.L.D, D4 = D / 4;
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= int64_t(a.n_q) * D4) return;
+  const int q = int(idx / D4), d4 = int(idx % D4), h = blockIdx.y;
+  const int64_t T = a.n_ktiles, U = a.units_per_block;
+  const int64_t first = (int64_t(h) * a.n_qblocks + q / AT_BQ) * T;
+  const int nseg = int((first + T - 1) / U - first / U) + 1;
+  if (nseg == 1) return;
+  float ls[kMaxSplits];
+  float mx = -INFINITY;
+  for (int s = 0; s < nseg; ++s) {
+    ls[s] = a.part_lse[(uint64_t(s) * a.L.H + h) * a.n_q + q];
+    mx = fmaxf(mx, ls[s]);
+  }
+  float wsum = 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < nseg; ++s) {
+    if (ls[s] == -INFINITY) continue;
+    const float w = expf(ls[s] - mx);
+    wsum += w;
+    const float4 v = *(const float4 *)(a.part_o + ((uint64_t(s) * a.L.H + h) * a.n_q + q) * D + 4 * d4);
+    acc.x = fmaf(w, v.x, acc.x); acc.y = fmaf(w, v.y, acc.y);
+    acc.z = fmaf(w, v.z, acc.z); acc.w = fmaf(w, v.w, acc.w);
+  }
+  const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+  const uint64_t off = (uint64_t(h) * a.n_q + q) * D + 4 * d4;
+  if (a.out_bf16) {
+    *(uint2 *)((uint16_t *)a.out + off) = make_uint2(
+        uint32_t(f32_to_bf16_bits(acc.x * inv)) | (uint32_t(f32_to_bf16_bits(acc.y * inv)) << 16),
+        uint32_t(f32_to_bf16_bits(acc.z * inv)) | (uint32_t(f32_to_bf16_bits(acc.w * inv)) << 16));
+  } else {
+    *(float4 *)((float *)a.out + off) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  }
+  if (a.lse && d4 == 0) a.lse[uint64_t(h) * a.n_q + q] = wsum > 0.0f ? mx + logf(wsum) : -INFINITY;
+}
+
+// Two complete results over disjoint key sets (the packed cache and the fresh
+// chunk) combined by their log-sum-exps: O = (w1 O1 + w2 O2) / (w1 + w2),
+// w_i = exp(lse_i - max), LSE = max + log(w1 + w2); an empty side has
+// lse = -inf and weight 0.  One thread per (query, 4 channels); blockIdx.y =
+// head.
+__global__ __launch_bounds__(256) void k_attend_merge2(MergeArgs m) {
+  const int D4 = m.D / 4;
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= int64_t(m.n_q) * D4) return;
+  const int q = int(idx / D4), d4 = int(idx % D4), h = blockIdx.y;
+  const uint64_t r = uint64_t(h) * m.n_q + q;
+  const float l1 = m.lse1[r], l2 = m.lse2[r];
+  const float mx = fmaxf(l1, l2);
+  const float w1 = l1 == -INFINITY ? 0.0f : expf(l1 - mx);
+  const float w2 = l2 == -INFINITY ? 0.0f : expf(l2 - mx);
+  const float ws = w1 + w2;
+  const float inv = ws > 0.0f ? 1.0f / ws : 0.0f;
+  const float4 a = *(const float4 *)(m.o1 + r * m.D + 4 * d4);
+  const float4 b = *(const float4 *)(m.o2 + r * m.D + 4 * d4);
+  const float4 o = make_float4(fmaf(w1, a.x, w2 * b.x) * inv, fmaf(w1, a.y, w2 * b.y) * inv,
+                               fmaf(w1, a.z, w2 * b.z) * inv, fmaf(w1, a.w, w2 * b.w) * inv);
+  const uint64_t off = r * m.D + 4 * d4;
+  if (m.out_bf16)
+    *(uint2 *)((uint16_t *)m.out + off) = make_uint2(pack_bf16x2(o.x, o.y), pack_bf16x2(o.z, o.w));
+  else
+    *(float4 *)((float *)m.out + off) = o;
+  if (m.lse && d4 == 0) m.lse[r] = ws > 0.0f ? mx + logf(ws) : -INFINITY;
+}
+
+// ---------------------------------------------------------------- launchers
+
+template <int D, int G, int BITS, bool BF>
+static void launch_attend_t(const AttnArgs &a, hipStream_t st) {
+  const int64_t total = int64_t(a.n_ktiles) * a.n_qblocks * a.L.H;
+  const dim3 grid(unsigned(cdiv(total, a.units_per_block)));
+  if (a.L.mask_off) {
+    switch (a.L.S) {
+      case 1: QKV_LAUNCH((k_attend3<D, G, BITS, BF, 1, false, true>), grid, dim3(512), 0, st, a); break;
+      case 2: QKV_LAUNCH((k_attend3<D, G, BITS, BF, 2, false, true>), grid, dim3(512), 0, st, a); break;
+      case 3: QKV_LAUNCH((k_attend3<D, G, BITS, BF, 3, false, true>), grid, dim3(512), 0, st, a); break;
+      default: QKV_LAUNCH((k_attend3<D, G, BITS, BF, 4, false, true>), grid, dim3(512), 0, st, a); break;
+    }
+    return;
+  }
+  switch (a.L.S) {
+    case 1: QKV_LAUNCH((k_attend3<D, G, BITS, BF, 1>), grid, dim3(512), 0, st, a); break;
+    case 2: QKV_LAUNCH((k_attend3<D, G, BITS, BF, 2>), grid, dim3(512), 0, st, a); break;
+    case 3: QKV_LAUNCH((k_attend3<D, G, BITS, BF, 3>), grid, dim3(512), 0, st, a); break;
+    default: QKV_LAUNCH((k_attend3<D, G, BITS, BF, 4>), grid, dim3(512), 0, st, a); break;
+  }
+}
+
+void launch_attend_fresh(const AttnArgs &a, hipStream_t st) {
+  const int64_t total = int64_t(a.n_ktiles) * a.n_qblocks * a.L.H;
+  const dim3 grid(unsigned(cdiv(total, a.units_per_block)));
+  if (a.L.D == 64)
+    QKV_LAUNCH((k_attend3<64, 32, 2, true, 1, true>), grid, dim3(512), 0, st, a);
+  else
+    QKV_LAUNCH((k_attend3<128, 32, 2, true, 1, true>), grid, dim3(512), 0, st, a);
+  if (a.max_segments > 1)
+    QKV_LAUNCH(k_attend_merge, dim3(cdiv(int64_t(a.n_q) * (a.L.D / 4), 256), a.L.H), dim3(256), 0, st, a);
+}
+void launch_attend_merge2(const MergeArgs &m, hipStream_t st) {
+  QKV_LAUNCH(k_attend_merge2, dim3(cdiv(int64_t(m.n_q) * (m.D / 4), 256), m.H), dim3(256), 0, st, m);
+}
+void launch_attend(const AttnArgs &a, hipStream_t st) {
+  QKV_DISPATCH_CODEC(a.L, launch_attend_t, a, st);
+  if (a.max_segments > 1)
+    QKV_LAUNCH(k_attend_merge, dim3(cdiv(int64_t(a.n_q) * (a.L.D / 4), 256), a.L.H), dim3(256), 0, st, a);
+}
+}  // namespace qkv

@@ -126,4 +126,21 @@ struct RefitArgs {
   uint16_t *b_out;             // [2][H][D][D] bf16 re-fitted blocks
 };
 
+// Optional per-kernel timing (qkv_trace): while a sink is installed for the
+// duration of a call, every kernel launch is bracketed by two HIP events
+// recorded on the launch's stream.  `label` is the stringified kernel
+// expression; the sink keeps the kernel's base name.
+struct TraceSink {
+  virtual void begin(const char *label, hipStream_t st) = 0;
+  virtual void end(hipStream_t st) = 0;
+};
+extern thread_local TraceSink *t_trace;
+
+#define QKV_LAUNCH(KERNEL, GRID, BLOCK, LDS, ST, ...)                         \
+  do {                                                                        \
+    if (::qkv::t_trace) ::qkv::t_trace->begin(#KERNEL, ST);                   \
+    hipLaunchKernelGGL(KERNEL, GRID, BLOCK, LDS, ST, __VA_ARGS__);            \
+    if (::qkv::t_trace) ::qkv::t_trace->end(ST);                              \
+  } while (0)
+
 }  // namespace qkv

@@ -1,4 +1,5 @@
-// Host launchers of the qkv kernels (defined in kernels.hip).
+// Host launchers of the qkv kernels (defined in encode.hip, decode.hip,
+// attend.hip and xlayer.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>

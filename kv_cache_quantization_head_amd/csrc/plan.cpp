@@ -274,8 +274,6 @@ extern "C" int qkv_chunk_starts(const qkv_ctx *ctx, int32_t layer, int64_t *star
   return n;
 }
 
-extern "C" void qkv_destroy(qkv_ctx *ctx) { delete ctx; }
-
 extern "C" const char *qkv_status_string(const qkv_ctx *ctx, int status) {
   switch (status) {
     case QKV_OK: return "ok";

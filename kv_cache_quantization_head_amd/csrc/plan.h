@@ -80,6 +80,13 @@ struct qkv_ctx {
   int32_t chain_layer = -1;
   int64_t chain_t0 = 0, chain_n = 0;
   int n_cu = 0;                  // compute units of the device, read at the first attention call
+  // per-kernel timing (qkv_trace): HIP events (as void*) recorded around each
+  // launch while tracing is on; the pool is reused after every read
+  struct TraceMark { std::string name; void *begin, *end; };
+  int trace = 0;
+  std::vector<TraceMark> trace_marks;
+  std::vector<void *> trace_pool;
+  size_t trace_used = 0;
   int last_hip_error = 0;
   std::string last_error;
 };

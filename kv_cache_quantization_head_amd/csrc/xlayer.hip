@@ -1,0 +1,341 @@
+// Cross-layer kernels of the qkv library: block-diagonal + low-rank
+// prediction in fp64 with a fixed summation order, and the adapted-mode
+// re-fit (Gram sums + Cholesky solve).
+#include "common.h"
+
+namespace qkv {
+
+// ------------------------------------------------------------ cross layer
+
+// Cross-layer prediction (r <= 64), in fp64 with a fixed summation order per
+// output: the projection sums over m = 0 .. H*D-1, the prediction over j, then
+// over k.  Every product is of two bf16 values, hence exact in fp64, so
+// fma(p, q, acc) equals acc + p*q rounded once: each output is exactly that
+// sequence of fp64 additions, however the work is tiled.
+
+// proj[t][k] = bf16(sum over m = 0 .. H*D-1 of y[t][m] V[m][k]).  Block = 256
+// threads = (token groups of 4) x (output groups of 8: 4 groups for r <= 32,
+// else 8), i.e. 256 or 128 tokens; the m axis is staged through LDS 32 at a
+// time (transposed, fp32; outputs past r read zero columns).
+constexpr int XL_MC = 32;
+__host__ __device__ constexpr int xl_project_groups(int r) { return r <= 32 ? 4 : 8; }
+__global__ __launch_bounds__(256) void k_xl_project(XlArgs a, int kv0) {
+  __shared__ float ys[XL_MC][256 + 4];    // [m][token]
+  __shared__ float vs[XL_MC][64 + 4];     // [m][k]
+  const int KG = xl_project_groups(a.r), KP = 8 * KG, TG = 256 / KG, TT = 4 * TG;
+  const int tid = threadIdx.x, kv = kv0 + blockIdx.y;
+  const int kg = tid % KG, tg = tid / KG;
+  const int t0 = blockIdx.x * TT;
+  const uint64_t HD = uint64_t(a.H) * a.D;
+  const uint16_t *Vw = a.weights + uint64_t(kv) * a.kv_weight_stride + HD * a.D + HD * a.r;
+  const uint16_t *y = a.chain + uint64_t(kv) * HD * a.n;
+  double acc[4][8];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[u][c] = 0.0;
+  for (uint64_t m0 = 0; m0 < HD; m0 += XL_MC) {
+    const int hh = int(m0 / a.D), j0 = int(m0 % a.D);   // a chunk lies inside one head (D % 32 == 0)
+    __syncthreads();                                    // previous chunk consumed
+    for (int e = tid; e < TT * XL_MC; e += 256) {
+      const int tt = e / XL_MC, jj = e % XL_MC, t = min(t0 + tt, a.n - 1);
+      ys[jj][tt] = bf16_to_f32(y[(uint64_t(hh) * a.n + t) * a.D + j0 + jj]);
+    }
+    for (int e = tid; e < XL_MC * KP; e += 256) {
+      const int jj = e / KP, kk = e % KP;
+      vs[jj][kk] = kk < a.r ? bf16_to_f32(Vw[(m0 + jj) * a.r + kk]) : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int jj = 0; jj < XL_MC; ++jj) {
+      const float4 yv = *(const float4 *)&ys[jj][4 * tg];
+      const float4 v0 = *(const float4 *)&vs[jj][8 * kg], v1 = *(const float4 *)&vs[jj][8 * kg + 4];
+      const double yd[4] = {double(yv.x), double(yv.y), double(yv.z), double(yv.w)};
+      const double vd[8] = {double(v0.x), double(v0.y), double(v0.z), double(v0.w),
+                            double(v1.x), double(v1.y), double(v1.z), double(v1.w)};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[u][c] = fma(yd[u], vd[c], acc[u][c]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int t = t0 + 4 * tg + u;
+    if (t >= a.n) continue;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int kk = 8 * kg + c;
+      if (kk < a.r) a.proj[(uint64_t(kv) * a.n + t) * a.r + kk] = bf16_to_f32(f64_to_bf16_bits(acc[u][c]));
+    }
+  }
+}
+
+// pred[h][t][i] = sum_j B_h[i][j] y[t][j] (order j), then + sum_k U[h*D+i][k]
+// w[t][k] (order k), fp64, rounded once to fp32.  Block = 256 threads =
+// (token groups of 4) x (output groups of 8) over token tiles of 4*256/(D/8)
+// tokens; B_h and U_h are staged once per block (transposed, as bf16: two
+// blocks fit a CU) and the block walks every gridDim.x-th token tile.
+__global__ __launch_bounds__(256) void k_xl_predict(XlArgs a, int kv0) {
+  extern __shared__ uint16_t xs16[];
+  const int D = a.D, RP = (a.r + 7) & ~7;
+  const int IG = D / 8, TG = 256 / IG, TT = 4 * TG;
+  uint16_t *bsT = xs16;                       // [D j][D i] bf16
+  uint16_t *usT = bsT + D * D;                // [RP k][D i]
+  uint16_t *ysT = usT + RP * D;               // [D j][TT]
+  uint16_t *wsT = ysT + D * TT;               // [RP k][TT]
+  const int tid = threadIdx.x, h = blockIdx.y, kv = kv0 + blockIdx.z;
+  const int ig = tid % IG, tg = tid / IG;
+  const uint64_t HD = uint64_t(a.H) * D;
+  const uint16_t *W = a.weights + uint64_t(kv) * a.kv_weight_stride;
+  const uint16_t *B = a.b_weights ? a.b_weights + (uint64_t(kv) * a.H + h) * D * D : W + uint64_t(h) * D * D;
+  const uint16_t *U = W + HD * D + uint64_t(h) * D * a.r;
+  const uint16_t *y = a.chain + uint64_t(kv) * HD * a.n + uint64_t(h) * a.n * D;
+  const float *w = a.proj + uint64_t(kv) * a.n * a.r;
+  for (int e = tid; e < D * D; e += 256) {
+    const int i = e / D, j = e % D;
+    bsT[j * D + i] = B[e];
+  }
+  for (int e = tid; e < D * RP; e += 256) {
+    const int i = e / RP, kk = e % RP;
+    usT[kk * D + i] = kk < a.r ? U[uint64_t(i) * a.r + kk] : uint16_t(0);
+  }
+  const int n_tiles = (a.n + TT - 1) / TT;
+  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const int t0 = tile * TT;
+    __syncthreads();                          // weights staged / previous tile consumed
+    for (int e = tid; e < TT * D; e += 256) {
+      const int tt = e / D, j = e % D, t = min(t0 + tt, a.n - 1);
+      ysT[j * TT + tt] = y[uint64_t(t) * D + j];
+    }
+    for (int e = tid; e < TT * RP; e += 256) {
+      const int tt = e / RP, kk = e % RP, t = min(t0 + tt, a.n - 1);
+      // w holds bf16 values (rounded in the projection): exact in bf16
+      wsT[kk * TT + tt] = kk < a.r ? f32_to_bf16_bits(w[uint64_t(t) * a.r + kk]) : uint16_t(0);
+    }
+    __syncthreads();
+    double acc[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[u][c] = 0.0;
+    auto step = [&](const uint16_t *ycol, const uint16_t *bcol) {
+      const uint2 yv = *(const uint2 *)(ycol + 4 * tg);
+      const uint4 bv = *(const uint4 *)(bcol + 8 * ig);
+      const double yd[4] = {double(__uint_as_float(yv.x << 16)), double(__uint_as_float(yv.x & 0xffff0000u)),
+                            double(__uint_as_float(yv.y << 16)), double(__uint_as_float(yv.y & 0xffff0000u))};
+      const double bd[8] = {double(__uint_as_float(bv.x << 16)), double(__uint_as_float(bv.x & 0xffff0000u)),
+                            double(__uint_as_float(bv.y << 16)), double(__uint_as_float(bv.y & 0xffff0000u)),
+                            double(__uint_as_float(bv.z << 16)), double(__uint_as_float(bv.z & 0xffff0000u)),
+                            double(__uint_as_float(bv.w << 16)), double(__uint_as_float(bv.w & 0xffff0000u))};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[u][c] = fma(bd[c], yd[u], acc[u][c]);
+    };
+    if (!a.lowrank_only) {
+#pragma unroll 4
+      for (int j = 0; j < D; ++j) step(ysT + j * TT, bsT + j * D);
+    }
+    for (int kk = 0; kk < a.r; ++kk) step(wsT + kk * TT, usT + kk * D);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + 4 * tg + u;
+      if (t >= a.n) continue;
+      float *pp = a.pred + (uint64_t(kv) * HD * a.n) + (uint64_t(h) * a.n + t) * D + 8 * ig;
+      *(float4 *)pp = make_float4(float(acc[u][0]), float(acc[u][1]), float(acc[u][2]), float(acc[u][3]));
+      *(float4 *)(pp + 4) = make_float4(float(acc[u][4]), float(acc[u][5]), float(acc[u][6]), float(acc[u][7]));
+    }
+  }
+}
+
+// Adapted predictor, step 1: per (token range p, head, kv, matrix) the fp64
+// sums over the range's tokens of y y^T (matrix 0) and y (x - U w)^T
+// (matrix 1), in token order.  Block = 16 x 16 threads, thread (ti, tj)
+// owns entries [8 ti .. 8 ti + 7][8 tj .. 8 tj + 7]; tokens are staged
+// through LDS 32 at a time (y as fp32, the second factor as fp64).
+constexpr int RF_TC = 32;
+__global__ __launch_bounds__(256) void k_xl_gram(RefitArgs a) {
+  __shared__ float ys[RF_TC][128];
+  __shared__ double zs[RF_TC][128];
+  const int D = a.D, part = blockIdx.x, h = blockIdx.y, kv = blockIdx.z >> 1, mat = blockIdx.z & 1;
+  const int tid = threadIdx.x, ti = tid / 16, tj = tid % 16;
+  const int64_t t_beg = int64_t(a.n) * part / kRefitParts, t_end = int64_t(a.n) * (part + 1) / kRefitParts;
+  const uint16_t *y = a.chain + (uint64_t(kv) * a.H + h) * uint64_t(a.n) * D;
+  const uint16_t *x = (const uint16_t *)(kv ? a.v_in : a.k_in) + uint64_t(h) * a.n * D;
+  const float *lr = a.low_rank + (uint64_t(kv) * a.H + h) * uint64_t(a.n) * D;
+  const bool active = 8 * ti < D && 8 * tj < D;
+  double acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
+  for (int64_t c0 = t_beg; c0 < t_end; c0 += RF_TC) {
+    const int nc = int(min<int64_t>(RF_TC, t_end - c0));
+    // eight channels per thread and step, every load of the chunk issued
+    // before any is used (past the range: zeros)
+    constexpr int NU = RF_TC * 128 / 8 / 256;
+    uint4 yv[NU], xv[NU];
+    float4 lv[NU][2];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int e8 = tid + 256 * u, tt = e8 / (D / 8), j = 8 * (e8 % (D / 8));
+      yv[u] = xv[u] = make_uint4(0, 0, 0, 0);
+      lv[u][0] = lv[u][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (tt < nc && e8 < RF_TC * D / 8) {
+        const uint64_t off = uint64_t(c0 + tt) * D + j;
+        yv[u] = *(const uint4 *)(y + off);
+        if (mat) {
+          xv[u] = *(const uint4 *)(x + off);
+          lv[u][0] = *(const float4 *)(lr + off);
+          lv[u][1] = *(const float4 *)(lr + off + 4);
+        }
+      }
+    }
+    __syncthreads();                          // previous chunk consumed
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int e8 = tid + 256 * u, tt = e8 / (D / 8), j = 8 * (e8 % (D / 8));
+      if (e8 >= RF_TC * D / 8) continue;
+      const uint32_t yw[4] = {yv[u].x, yv[u].y, yv[u].z, yv[u].w}, xw[4] = {xv[u].x, xv[u].y, xv[u].z, xv[u].w};
+      const float lf[8] = {lv[u][0].x, lv[u][0].y, lv[u][0].z, lv[u][0].w,
+                           lv[u][1].x, lv[u][1].y, lv[u][1].z, lv[u][1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float yf = __uint_as_float((e & 1) ? (yw[e >> 1] & 0xffff0000u) : (yw[e >> 1] << 16));
+        const float xf = __uint_as_float((e & 1) ? (xw[e >> 1] & 0xffff0000u) : (xw[e >> 1] << 16));
+        ys[tt][j + e] = yf;
+        zs[tt][j + e] = mat == 0 ? double(yf) : double(xf) - double(lf[e]);
+      }
+    }
+    __syncthreads();
+    if (active) {
+      for (int tt = 0; tt < nc; ++tt) {
+        double yi[8], zj[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) yi[i] = double(ys[tt][8 * ti + i]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) zj[j] = zs[tt][8 * tj + j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) acc[i][j] = fma(yi[i], zj[j], acc[i][j]);
+      }
+    }
+  }
+  if (active) {
+    double *g = a.gram + (((uint64_t(part) * 2 + kv) * 2 + mat) * a.H + h) * uint64_t(D) * D;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) g[uint64_t(8 * ti + i) * D + 8 * tj + j] = acc[i][j];
+  }
+}
+
+// Adapted predictor, step 2: one block per (head, kv).  A = sum of the parts
+// of y y^T (in part order) + lam I, lam = 2^-20 trace(A) / D; Cholesky
+// factor L (left-looking, in LDS); then, 16 right-hand sides at a time, the
+// columns c of R = sum of the parts of y (x - U w)^T are solved through
+// L z' = r and L^T z = z', and row c of the block is z, rounded to bf16.
+__global__ __launch_bounds__(256) void k_xl_solve(RefitArgs a) {
+  extern __shared__ double lds64[];
+  const int D = a.D, h = blockIdx.x, kv = blockIdx.y, tid = threadIdx.x;
+  double *Lm = lds64;                 // [D][D]
+  double *Z = lds64 + D * D;          // [16][D]
+  __shared__ double lam_s;
+  const uint64_t DD = uint64_t(D) * D;
+  auto part_ptr = [&](int p, int mat) {
+    return a.gram + (((uint64_t(p) * 2 + kv) * 2 + mat) * a.H + h) * DD;
+  };
+  for (int e = tid; e < D * D; e += 256) {
+    double v = 0.0;
+    for (int p = 0; p < kRefitParts; ++p) v += part_ptr(p, 0)[e];
+    Lm[e] = v;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double tr = 0.0;
+    for (int i = 0; i < D; ++i) tr += Lm[i * D + i];
+    lam_s = 0x1p-20 * tr / D;
+  }
+  __syncthreads();
+  if (tid < D) Lm[tid * D + tid] += lam_s;
+  __syncthreads();
+  // left-looking Cholesky: column j from the columns before it
+  for (int j = 0; j < D; ++j) {
+    if (tid == 0) {
+      double s = Lm[j * D + j];
+      for (int k = 0; k < j; ++k) s -= Lm[j * D + k] * Lm[j * D + k];
+      Lm[j * D + j] = sqrt(s > 0.0 ? s : 0x1p-1000);
+    }
+    __syncthreads();
+    const int i = j + 1 + tid;
+    if (i < D) {
+      double s = Lm[i * D + j];
+      for (int k = 0; k < j; ++k) s -= Lm[i * D + k] * Lm[j * D + k];
+      Lm[i * D + j] = s / Lm[j * D + j];
+    }
+    __syncthreads();
+  }
+  // 16 right-hand sides at a time: thread (cc, q) = column c0 + cc, terms k = q mod 16
+  const int cc = tid / 16, q = tid % 16;
+  for (int c0 = 0; c0 < D; c0 += 16) {
+    for (int e = tid; e < 16 * D; e += 256) {
+      const int col = e / D, row = e % D;
+      double v = 0.0;
+      for (int p = 0; p < kRefitParts; ++p) v += part_ptr(p, 1)[uint64_t(row) * D + c0 + col];
+      Z[col * D + row] = v;
+    }
+    __syncthreads();
+    for (int i = 0; i < D; ++i) {              // forward: L z' = r
+      double s = 0.0;
+      for (int k = q; k < i; k += 16) s += Lm[i * D + k] * Z[cc * D + k];
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 16);
+      if (q == 0) Z[cc * D + i] = (Z[cc * D + i] - s) / Lm[i * D + i];
+      __syncthreads();
+    }
+    for (int i = D - 1; i >= 0; --i) {         // backward: L^T z = z'
+      double s = 0.0;
+      for (int k = i + 1 + q; k < D; k += 16) s += Lm[k * D + i] * Z[cc * D + k];
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 16);
+      if (q == 0) Z[cc * D + i] = (Z[cc * D + i] - s) / Lm[i * D + i];
+      __syncthreads();
+    }
+    uint16_t *bo = a.b_out + (uint64_t(kv) * a.H + h) * DD;
+    for (int e = tid; e < 16 * D; e += 256) {
+      const int col = e / D, j = e % D;
+      bo[uint64_t(c0 + col) * D + j] = f64_to_bf16_bits(Z[col * D + j]);
+    }
+    __syncthreads();
+  }
+}
+
+// chunk table after a rewind: blockIdx.x = stream of the range
+// ---------------------------------------------------------------- launchers
+
+void launch_xl_refit(const RefitArgs &a, hipStream_t st) {
+  QKV_LAUNCH(k_xl_gram, dim3(kRefitParts, a.H, 4), dim3(256), 0, st, a);
+  const size_t lds = (size_t(a.D) * a.D + 16 * size_t(a.D)) * sizeof(double);
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_xl_solve),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  QKV_LAUNCH(k_xl_solve, dim3(a.H, 2), dim3(256), lds, st, a);
+}
+void launch_xl_predict(const XlArgs &a, int kv0, int n_kv, hipStream_t st) {
+  // tiled kernels (fp32 LDS staging of the bf16 operands)
+  const int TT = 4 * (256 / xl_project_groups(a.r));
+  if (!a.skip_project) QKV_LAUNCH(k_xl_project, dim3(cdiv(a.n, TT), n_kv), dim3(256), 0, st, a, kv0);
+  const int RP = (a.r + 7) & ~7;
+  const int IG = a.D / 8, TTp = 4 * (256 / IG);
+  const size_t lds = size_t(a.D * a.D + RP * a.D + a.D * TTp + RP * TTp) * 2;
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_xl_predict),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  // two blocks per CU fit (the staged weights); about 512 blocks in all,
+  // each walking every gx-th token tile of its (head, kv)
+  const int64_t n_tiles = cdiv(a.n, TTp);
+  const int64_t hk = int64_t(a.H) * n_kv;
+  const unsigned gx = unsigned(std::max<int64_t>(1, std::min<int64_t>(n_tiles, (512 + hk - 1) / hk)));
+  QKV_LAUNCH(k_xl_predict, dim3(gx, a.H, n_kv), dim3(256), lds, st, a, kv0);
+}
+}  // namespace qkv

@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     L = qkv.lib()
     names = _declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), n
     assert "qkv_encode_chunk" in names and "qkv_attend" in names
