@@ -181,6 +181,21 @@ int qkv_encode_chunk(qkv_ctx *ctx, int32_t layer0, int32_t n_layers,
 int qkv_attend(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t n_q, int32_t q_dtype,
                void *d_out, int32_t out_dtype, float *d_lse, void *stream);
 
+/* qkv_attend for callers that cannot allocate device memory or use the
+ * arena's scratch region (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, kernels, result and
+ * errors as qkv_attend, but the split partials go to a fixed 128 MiB device
+ * array the library holds on every GPU it runs on until the process ends
+ * (looked up at qkv_init).  The call allocates nothing.  Every call on one
+ * GPU shares that array and finds it as the last call left it (nothing in
+ * it needs to start at zero): calls that overlap on one GPU, from any
+ * context or stream, race.  Extra errors: QKV_E_CAPACITY when the call's
+ * partials (slots x H x n_q x (d + 1) floats, at most 8 slots) exceed 128
+ * MiB; QKV_E_UNSUPPORTED when the array's address could not be found at
+ * qkv_init (no usable device, or max_query_tokens = 0). */
+int qkv_attend_noalloc(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t n_q, int32_t q_dtype,
+                       void *d_out, int32_t out_dtype, float *d_lse, void *stream);
+
 /* The read as a generating model issues it: attention of n_q queries over
  * every token encoded in `layer` followed by n_new fresh tokens of the chunk
  * being generated, which are not in the cache yet (QVG explainer, "Sommario

@@ -72,6 +72,8 @@ def lib():
     L.qkv_encode_chunk.restype = ctypes.c_int
     L.qkv_attend.argtypes = [vp, i32, vp, i64, i32, vp, i32, vp, vp]
     L.qkv_attend.restype = ctypes.c_int
+    L.qkv_attend_noalloc.argtypes = [vp, i32, vp, i64, i32, vp, i32, vp, vp]
+    L.qkv_attend_noalloc.restype = ctypes.c_int
     L.qkv_attend_with_chunk.argtypes = [vp, i32, vp, i64, i32, vp, vp, i64, vp, i32, vp, vp]
     L.qkv_attend_with_chunk.restype = ctypes.c_int
     L.qkv_reconstruct.argtypes = [vp, i32, i32, i32, i64, i64, vp, i32, vp]
@@ -191,6 +193,20 @@ class Codec:
         _check(lib().qkv_attend(self.ctx, layer, ctypes.c_void_p(q.data_ptr()), n_q,
                                 _dtype_code(q.dtype), ctypes.c_void_p(out.data_ptr()),
                                 _dtype_code(out.dtype), lse_ptr, _stream()), self.ctx)
+        return out, lse
+
+    def attend_noalloc(self, layer, q, out, lse=None):
+        """qkv_attend_noalloc: out [H, n_q, d] and lse [H, n_q] are the caller's;
+        the split partials live in the library's fixed per-GPU array."""
+        H, n_q, d = q.shape
+        if H != self.cfg.n_heads or d != self.cfg.head_dim or tuple(out.shape) != (H, n_q, d):
+            raise ValueError("q / out shape does not match the configuration")
+        if not q.is_contiguous() or not out.is_contiguous():
+            raise ValueError("q and out must be contiguous")
+        lse_ptr = ctypes.c_void_p(lse.data_ptr()) if lse is not None else None
+        _check(lib().qkv_attend_noalloc(self.ctx, layer, ctypes.c_void_p(q.data_ptr()), n_q,
+                                        _dtype_code(q.dtype), ctypes.c_void_p(out.data_ptr()),
+                                        _dtype_code(out.dtype), lse_ptr, _stream()), self.ctx)
         return out, lse
 
     def attend_with_chunk(self, layer, q, k_new, v_new, out_dtype=torch.float32, with_lse=True, out=None,

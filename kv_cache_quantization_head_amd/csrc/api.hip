@@ -4,8 +4,10 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "device.h"
 #include "launch.h"
@@ -121,6 +123,28 @@ extern "C" int qkv_trace_read(qkv_ctx *ctx, qkv_trace_entry *out, int32_t max) {
   return int(names.size());
 }
 
+// Device address of the fixed partials array on the current device, looked
+// up once per device (with that device current) and kept; nullptr when the
+// lookup fails (no usable device).
+static void *noalloc_scratch_for_current_device() {
+  static std::mutex mu;
+  static std::vector<void *> ptrs;
+  static std::vector<char> done;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (size_t(dev) >= ptrs.size()) {
+    ptrs.resize(size_t(dev) + 1, nullptr);
+    done.resize(size_t(dev) + 1, 0);
+  }
+  if (!done[dev]) {
+    void *p = nullptr;
+    if (noalloc_scratch_address(&p) == 0) ptrs[dev] = p;
+    done[dev] = 1;
+  }
+  return ptrs[dev];
+}
+
 extern "C" int qkv_init(const qkv_config *cfg, void *d_arena, size_t arena_bytes,
                         const void *d_predictor, qkv_ctx **out) {
   if (!out) return QKV_E_INVAL;
@@ -139,6 +163,10 @@ extern "C" int qkv_init(const qkv_config *cfg, void *d_arena, size_t arena_bytes
   ctx->arena_bytes = arena_bytes;
   ctx->predictor = static_cast<const uint8_t *>(d_predictor);
   ctx->layers.resize(size_t(p.cfg.n_layers));
+  if (p.cfg.max_query_tokens > 0) {
+    ctx->noalloc_scratch = noalloc_scratch_for_current_device();
+    (void)hipGetLastError();  // a failed lookup only disables qkv_attend_noalloc
+  }
   *out = ctx;
   return QKV_OK;
 }
@@ -286,18 +314,12 @@ extern "C" int qkv_encode_chunk(qkv_ctx *ctx, int32_t layer0, int32_t n_layers, 
   return QKV_OK;
 }
 
-extern "C" int qkv_attend(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t n_q, int32_t q_dtype,
-                          void *d_out, int32_t out_dtype, float *d_lse, void *stream) {
-  const int rc = check_attend(ctx, layer, d_q, n_q, q_dtype, d_out, out_dtype);
-  if (rc != QKV_OK) return rc;
-  if (n_q == 0) return QKV_OK;
-  TraceScope trace(ctx);
-  hipStream_t st = static_cast<hipStream_t>(stream);
+// Enqueue the attention of n_q queries over `layer` with the split partials
+// at part_o / part_lse ([max_segments][H][n_q][d] and [max_segments][H][n_q]).
+static void enqueue_attend(qkv_ctx *ctx, const AttnSplit &w, int32_t layer, const void *d_q, int64_t n_q,
+                           int32_t q_dtype, void *d_out, int32_t out_dtype, float *d_lse, float *part_o,
+                           float *part_lse, hipStream_t st) {
   const Plan &p = ctx->plan;
-  const int64_t n_keys = ctx->layers[layer].n_tokens;
-  ensure_cu_count(ctx);
-  const AttnSplit w = attention_split(p, n_keys, n_q, ctx->n_cu);
-
   AttnArgs a{};
   a.L = dev_layout(p);
   a.stream_k = ctx->arena + stream_offset(p, layer, 0);
@@ -305,7 +327,7 @@ extern "C" int qkv_attend(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t 
   a.q = d_q;
   a.q_bf16 = q_dtype == QKV_BF16;
   a.n_q = int32_t(n_q);
-  a.n_keys = int32_t(n_keys);
+  a.n_keys = int32_t(ctx->layers[layer].n_tokens);
   a.n_qblocks = int32_t(w.n_qblocks);
   a.n_ktiles = int32_t(w.n_ktiles);
   a.units_per_block = int32_t(w.units_per_block);
@@ -314,11 +336,45 @@ extern "C" int qkv_attend(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t 
   a.out = d_out;
   a.out_bf16 = out_dtype == QKV_BF16;
   a.lse = d_lse;
-  a.part_o = reinterpret_cast<float *>(scratch(ctx, p.attn_part_o_off));
-  a.part_lse = reinterpret_cast<float *>(scratch(ctx, p.attn_part_lse_off));
-  (void)hipGetLastError();
+  a.part_o = part_o;
+  a.part_lse = part_lse;
   launch_attend(a, st);
+}
+
+extern "C" int qkv_attend(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t n_q, int32_t q_dtype,
+                          void *d_out, int32_t out_dtype, float *d_lse, void *stream) {
+  const int rc = check_attend(ctx, layer, d_q, n_q, q_dtype, d_out, out_dtype);
+  if (rc != QKV_OK) return rc;
+  if (n_q == 0) return QKV_OK;
+  TraceScope trace(ctx);
+  const Plan &p = ctx->plan;
+  ensure_cu_count(ctx);
+  const AttnSplit w = attention_split(p, ctx->layers[layer].n_tokens, n_q, ctx->n_cu);
+  (void)hipGetLastError();
+  enqueue_attend(ctx, w, layer, d_q, n_q, q_dtype, d_out, out_dtype, d_lse,
+                 reinterpret_cast<float *>(scratch(ctx, p.attn_part_o_off)),
+                 reinterpret_cast<float *>(scratch(ctx, p.attn_part_lse_off)), static_cast<hipStream_t>(stream));
   ctx->chain_layer = -1;  // scratch reused
+  return hip_status(ctx);
+}
+
+extern "C" int qkv_attend_noalloc(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t n_q, int32_t q_dtype,
+                                  void *d_out, int32_t out_dtype, float *d_lse, void *stream) {
+  const int rc = check_attend(ctx, layer, d_q, n_q, q_dtype, d_out, out_dtype);
+  if (rc != QKV_OK) return rc;
+  if (n_q == 0) return QKV_OK;
+  if (!ctx->noalloc_scratch) return QKV_E_UNSUPPORTED;
+  const Plan &p = ctx->plan;
+  ensure_cu_count(ctx);
+  const AttnSplit w = attention_split(p, ctx->layers[layer].n_tokens, n_q, ctx->n_cu);
+  // partials of the slots this call can use, in the fixed array
+  const uint64_t rows = uint64_t(w.max_segments) * p.cfg.n_heads * uint64_t(n_q);
+  const uint64_t lse_off = align_up(rows * p.cfg.head_dim * 4);
+  if (lse_off + rows * 4 > kNoAllocScratchBytes) return QKV_E_CAPACITY;
+  uint8_t *base = static_cast<uint8_t *>(ctx->noalloc_scratch);
+  (void)hipGetLastError();
+  enqueue_attend(ctx, w, layer, d_q, n_q, q_dtype, d_out, out_dtype, d_lse, reinterpret_cast<float *>(base),
+                 reinterpret_cast<float *>(base + lse_off), static_cast<hipStream_t>(stream));
   return hip_status(ctx);
 }
 

@@ -615,6 +615,16 @@ void launch_attend_fresh(const AttnArgs &a, hipStream_t st) {
 void launch_attend_merge2(const MergeArgs &m, hipStream_t st) {
   QKV_LAUNCH(k_attend_merge2, dim3(cdiv(int64_t(m.n_q) * (m.D / 4), 256), m.H), dim3(256), 0, st, m);
 }
+// Split partials of qkv_attend_noalloc: a fixed device array instead of the
+// arena's scratch region.  Every GPU the library runs on holds its own copy
+// until the process ends.  In host code `scratch` only names the symbol: its
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+int noalloc_scratch_address(void **ptr) {
+  return hipGetSymbolAddress(ptr, HIP_SYMBOL(scratch)) == hipSuccess ? 0 : -1;
+}
+
 void launch_attend(const AttnArgs &a, hipStream_t st) {
   QKV_DISPATCH_CODEC(a.L, launch_attend_t, a, st);
   if (a.max_segments > 1)

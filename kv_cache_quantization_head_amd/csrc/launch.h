@@ -17,6 +17,8 @@ void launch_quantize(const EncodeArgs &a, int streams, hipStream_t st);
 void launch_reconstruct(const ReconArgs &a, int n_layers, int64_t out_tokens, int out_t_off,
                         hipStream_t st);
 void launch_attend(const AttnArgs &a, hipStream_t st);
+// device address of the fixed partials array of the current device (0 on success)
+int noalloc_scratch_address(void **ptr);
 void launch_attend_fresh(const AttnArgs &a, hipStream_t st);
 void launch_attend_merge2(const MergeArgs &m, hipStream_t st);
 void launch_xl_predict(const XlArgs &a, int kv0, int n_kv, hipStream_t st);

@@ -18,6 +18,7 @@ constexpr int kRefitParts = 8;       // adapted-predictor re-fit: token ranges s
 constexpr int kSortMaxClusters = 4096;  // k-means update through per-tile sorts up to this C
 constexpr int kChanParts = 64;       // outlier flags: token ranges whose channel sums are kept apart
 constexpr uint64_t kAlign = 256;
+constexpr uint64_t kNoAllocScratchBytes = uint64_t(128) << 20;  // qkv_attend_noalloc partials, per GPU
 
 inline uint64_t align_up(uint64_t v, uint64_t a = kAlign) { return (v + a - 1) / a * a; }
 
@@ -80,6 +81,7 @@ struct qkv_ctx {
   int32_t chain_layer = -1;
   int64_t chain_t0 = 0, chain_n = 0;
   int n_cu = 0;                  // compute units of the device, read at the first attention call
+  void *noalloc_scratch = nullptr; // this device's fixed partials array (qkv_attend_noalloc), set at init
   // per-kernel timing (qkv_trace): HIP events (as void*) recorded around each
   // launch while tracing is on; the pool is reused after every read
   struct TraceMark { std::string name; void *begin, *end; };

@@ -27,7 +27,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     L = qkv.lib()
     names = _declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
     assert "qkv_encode_chunk" in names and "qkv_attend" in names
@@ -164,6 +164,12 @@ def test_call_validation_before_enqueue(ctx):
     assert L.qkv_attend(ctx, 2, p, 16, B.QKV_BF16, p, B.QKV_F32, None, None) == B.QKV_E_INVAL
     assert L.qkv_attend(ctx, 0, p, 16, 5, p, B.QKV_F32, None, None) == B.QKV_E_INVAL
     assert L.qkv_attend(ctx, 0, None, 16, B.QKV_BF16, p, B.QKV_F32, None, None) == B.QKV_E_INVAL
+    # the no-allocation variant validates the same way before anything else
+    N = L.qkv_attend_noalloc
+    assert N(ctx, 0, p, 16, B.QKV_BF16, p, B.QKV_F32, None, None) == B.QKV_E_STATE
+    assert N(ctx, 0, p, 4681, B.QKV_BF16, p, B.QKV_F32, None, None) == B.QKV_E_CAPACITY
+    assert N(ctx, 2, p, 16, B.QKV_BF16, p, B.QKV_F32, None, None) == B.QKV_E_INVAL
+    assert N(ctx, 0, None, 16, B.QKV_BF16, p, B.QKV_F32, None, None) == B.QKV_E_INVAL
     # attention with a fresh chunk: nothing to attend to, capacity, arguments
     A = L.qkv_attend_with_chunk
     assert A(ctx, 0, p, 16, B.QKV_BF16, None, None, 0, p, B.QKV_F32, None, None) == B.QKV_E_STATE
