@@ -61,6 +61,10 @@ def parse():
                     help="instead of the default step: the same wan_layer step with and without the "
                          "outlier-channel option; time of each call, reconstruction error and storage "
                          "cost of each mode")
+    ap.add_argument("--wide", action="store_true",
+                    help="instead of the default step: one wide-head layer (K,V bf16 [40, 62400, 128], C=512, "
+                         "G=64) coded as 2-stage INT2 and as 1-stage INT4; encode and reconstruct time, "
+                         "reconstruction error and storage cost of each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain 1 GiB device copy (a known-size "
                          "reference for HBM byte counters)")
@@ -102,8 +106,9 @@ def xlayer_main(args):
     for kv in (0, 1):
         B, U, V = synth.predictor(cfgs, 0, kv, rank=r)
         parts += [B.reshape(-1), U.reshape(-1), V.reshape(-1)]
+    Tq = 4680
     cfg = qkv.config(2, H, d, C, cfgs.n_stages, cfgs.bits, cfgs.group, kmeans_iters=cfgs.iters,
-                     max_tokens=T, max_chunks=1, kv_dtype=qkv.QKV_BF16, max_query_tokens=0, xlayer=1,
+                     max_tokens=T, max_chunks=1, kv_dtype=qkv.QKV_BF16, max_query_tokens=Tq, xlayer=1,
                      xlayer_rank=r)
     blob = torch.cat(parts).to(dev)
     codec = qkv.Codec(cfg, device=dev, predictor=blob)
@@ -114,6 +119,9 @@ def xlayer_main(args):
     ks = torch.stack([synth.kv_tokens(cfgs, l, 0, 0, T, device=dev) for l in range(2)])
     vs = torch.stack([synth.kv_tokens(cfgs, l, 1, 0, T, device=dev) for l in range(2)])
     ev, ev_a = [], []
+    q = synth.queries(cfgs, 1, Tq, device=dev)
+    out = torch.empty((H, Tq, d), dtype=torch.bfloat16, device=dev)
+    read_ev = []
 
     def step(record):
         for c, sink in ((codec, ev), (codec_a, ev_a)):
@@ -137,6 +145,34 @@ def xlayer_main(args):
     xl = sum(m[1].elapsed_time(m[2]) for m in ev) / len(ev)
     xl_a = sum(m[1].elapsed_time(m[2]) for m in ev_a) / len(ev_a)
 
+    # the read of the two layers in order (a model's forward pass): layer 0
+    # (packed SAS read, its reconstruction kept as the rolling copy), then
+    # layer 1 (prediction from that copy, reconstruction over it, bf16 read)
+    def read(record):
+        m = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        m[0].record()
+        codec.attend(0, q, out=out, with_lse=False)
+        m[1].record()
+        codec.attend(1, q, out=out, with_lse=False)
+        m[2].record()
+        if record:
+            read_ev.append(m)
+
+    for _ in range(args.warmup):
+        read(False)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        read(True)
+    torch.cuda.synchronize()
+    r0 = sum(m[0].elapsed_time(m[1]) for m in read_ev) / len(read_ev)
+    r1 = sum(m[1].elapsed_time(m[2]) for m in read_ev) / len(read_ev)
+    codec.trace(True)
+    read(False)
+    torch.cuda.synchronize()
+    kt = codec.trace_read()
+    codec.trace(False)
+    sweep_bytes = 2 * H * T * d * 2
+
     def layer1_error(c):
         err = []
         for kv, x in ((0, ks[1]), (1, vs[1])):
@@ -153,7 +189,13 @@ def xlayer_main(args):
                                "cross-layer rank 32", "heads": H, "tokens": T, "rank": r},
         "sas_layer_ms": round(sas, 4), "layer1_rel_sq_error_kv": layer1_error(codec),
         "adapted_layer_ms_with_refit": round(xl_a, 4),
-        "adapted_layer1_rel_sq_error_kv": layer1_error(codec_a)}), flush=True)
+        "adapted_layer1_rel_sq_error_kv": layer1_error(codec_a),
+        "read_q_tokens": Tq,
+        "read_layer0_ms": round(r0, 4), "read_layer1_ms": round(r1, 4),
+        "read_kernels": {k: {"launches": n, "avg_ms": round(tot / max(n, 1), 4)} for k, (n, tot) in kt.items()},
+        "read_rolling_copy_bytes": sweep_bytes,
+        "read_note": "layer 0: packed read + its reconstruction into the rolling bf16 copy; layer 1: "
+                     "prediction from the copy (fp64), reconstruction over it, bf16 read"}), flush=True)
 
 
 def fresh_main(args):
@@ -366,6 +408,79 @@ def outliers_main(args):
         "modes": res}), flush=True)
 
 
+def wide_main(args):
+    """The wide-head comparison: one layer of 40 heads x 62400 tokens (C = 512,
+    G = 64, 8 outlier channels x20) coded as INT2 x 2 stages and as INT4 x 1
+    stage (equal code bits).  A step encodes the layer from empty and
+    reconstructs K and V (bf16 out) in each variant; then the relative
+    squared reconstruction error of each variant and its storage cost."""
+    import torch
+    import kv_cache_quantization_head_amd as qkv
+    import synth
+    from fractions import Fraction
+
+    dev = torch.device("cuda:0")
+    base = synth.WIDE_HEAD
+    H, T, d, C, G = base.n_heads, base.tokens, base.head_dim, base.n_clusters, base.group
+    k = synth.kv_tokens(base, 0, 0, 0, T, device=dev)
+    v = synth.kv_tokens(base, 0, 1, 0, T, device=dev)
+    rec = torch.empty((2, 1, H, T, d), dtype=torch.bfloat16, device=dev)
+    codecs = {}
+    for name, S, b, _ in [(n, s_, b_, g_) for n, s_, b_, g_ in base.variants]:
+        cfg = qkv.config(1, H, d, C, S, b, G, kmeans_iters=base.iters, max_tokens=T, max_chunks=1,
+                         kv_dtype=qkv.QKV_BF16, max_query_tokens=0)
+        codecs[name] = (qkv.Codec(cfg, device=dev), S, b)
+    times = {n: {"encode": [], "reconstruct": []} for n in codecs}
+
+    def step(record):
+        for name, (codec, _, _) in codecs.items():
+            codec.rewind(0, 1, 0)
+            m = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            m[0].record()
+            codec.encode_chunk(k, v)
+            m[1].record()
+            codec.reconstruct(0, 1, 0, 0, T, out=rec[0])
+            codec.reconstruct(0, 1, 1, 0, T, out=rec[1])
+            m[2].record()
+            if record:
+                times[name]["encode"].append((m[0], m[1]))
+                times[name]["reconstruct"].append((m[1], m[2]))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    res = {}
+    n_el = 2 * H * T * d
+    for name, (codec, S, b) in codecs.items():
+        err = []
+        for kv, x in ((0, k), (1, v)):
+            rec_f = codec.reconstruct(0, 1, kv, 0, T)[0]
+            xf = x.float()
+            err.append(float(((rec_f - xf) ** 2).sum() / (xf ** 2).sum()))
+            del rec_f, xf
+        fixed = Fraction(S * b) + Fraction(S * 32, G) + Fraction(16, d)      # codes, meta, u16 ids
+        bits = float(fixed + Fraction(16 * C, T))
+        enc = _avg_ms(times[name]["encode"])
+        rc = _avg_ms(times[name]["reconstruct"])
+        packed = n_el * (S * b / 8 + S * 4 / G) + 2 * H * T * 2
+        res[name] = {"stages": S, "bits": b, "encode_ms": round(enc, 4), "reconstruct_k_and_v_ms": round(rc, 4),
+                     "quantize_GBps_in_plus_out": round((n_el * 2 + packed) / (enc * 1e-3) / 1e9, 1),
+                     "reconstruct_GBps": round((packed + n_el * 2) / (rc * 1e-3) / 1e9, 1),
+                     "rel_sq_error_k": round(err[0], 7), "rel_sq_error_v": round(err[1], 7),
+                     "bits_per_element": round(bits, 4)}
+    print(json.dumps({
+        "metric": "wide-head layer: 2-stage INT2 vs 1-stage INT4 (G=64), encode + reconstruct time, error, bits",
+        "value": res["int2x2"]["encode_ms"], "unit": "ms (INT2 x 2 encode of one layer)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False, "dtype": "bf16",
+        "data": "synthetic (seeded prototype/drift/outlier generator, device-generated)",
+        "config": {"workload": "wide_head layer: K,V bf16 [40, 62400, 128], C=512, 5 iterations, G=64, "
+                               "8 outlier channels x20", "heads": H, "tokens": T},
+        "variants": res}), flush=True)
+
+
 def _avg_ms(pairs):
     xs = [a.elapsed_time(b) for a, b in pairs]
     return sum(xs) / len(xs)
@@ -498,6 +613,9 @@ def main():
         return
     if args.outliers:
         outliers_main(args)
+        return
+    if args.wide:
+        wide_main(args)
         return
     import torch
     import kv_cache_quantization_head_amd as qkv

@@ -175,9 +175,20 @@ int qkv_encode_chunk(qkv_ctx *ctx, int32_t layer0, int32_t n_layers,
  * packed cache in registers/LDS (never stored).  q: device [H][n_q][d] in
  * q_dtype; out: device [H][n_q][d] in out_dtype; d_lse: device [H][n_q] f32
  * natural-log softmax denominators, or NULL.  Operands enter the products in
- * bf16; softmax and accumulation are fp32.  Errors: QKV_E_INVAL,
- * QKV_E_CAPACITY (n_q > max_query_tokens), QKV_E_STATE (nothing encoded),
- * QKV_E_UNSUPPORTED (cross-layer coded layer >= 1). */
+ * bf16; softmax and accumulation are fp32.
+ * Cross-layer mode (Coral-KV news article, section on cross-layer
+ * prediction): a layer l >= 1 is coded against the prediction from layer
+ * l-1's reconstruction, so its keys exist only through that chain.  The
+ * library keeps a rolling bf16 reconstruction of one layer (the last one
+ * read; arena region of one layer's K and V, 1/L of the cache in bf16):
+ * reading layer 0 stores its reconstruction there; reading layer l >= 1
+ * requires the region to hold layer l-1 over the same tokens (the layers
+ * are read in order 0, 1, 2, ... after the last encode call, as a model's
+ * forward pass does), predicts layer l from it, writes layer l's
+ * reconstruction over it and attends to those bf16 rows.  An encode call
+ * or a rewind empties the region.  Errors: QKV_E_INVAL, QKV_E_CAPACITY
+ * (n_q > max_query_tokens), QKV_E_STATE (nothing encoded; in cross-layer
+ * mode, layer l >= 1 read before layer l-1). */
 int qkv_attend(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t n_q, int32_t q_dtype,
                void *d_out, int32_t out_dtype, float *d_lse, void *stream);
 
@@ -192,7 +203,8 @@ int qkv_attend(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t n_q, int32_
  * context or stream, race.  Extra errors: QKV_E_CAPACITY when the call's
  * partials (slots x H x n_q x (d + 1) floats, at most 8 slots) exceed 128
  * MiB; QKV_E_UNSUPPORTED when the array's address could not be found at
- * qkv_init (no usable device, or max_query_tokens = 0). */
+ * qkv_init (no usable device, or max_query_tokens = 0) and in cross-layer
+ * mode (whose read also uses the arena's scratch for the prediction). */
 int qkv_attend_noalloc(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t n_q, int32_t q_dtype,
                        void *d_out, int32_t out_dtype, float *d_lse, void *stream);
 
@@ -207,7 +219,7 @@ int qkv_attend_noalloc(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t n_q
  * n_new = 0 is qkv_attend; an empty cache with n_new > 0 attends to the
  * fresh tokens alone.  Other arguments as qkv_attend.  Errors: QKV_E_INVAL,
  * QKV_E_CAPACITY (n_q > max_query_tokens), QKV_E_STATE (empty cache and
- * n_new = 0), QKV_E_UNSUPPORTED (cross-layer coded layer >= 1). */
+ * n_new = 0; in cross-layer mode, as qkv_attend). */
 int qkv_attend_with_chunk(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t n_q, int32_t q_dtype,
                           const void *d_k_new, const void *d_v_new, int64_t n_new, void *d_out,
                           int32_t out_dtype, float *d_lse, void *stream);

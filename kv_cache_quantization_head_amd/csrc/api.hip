@@ -310,8 +310,56 @@ extern "C" int qkv_encode_chunk(qkv_ctx *ctx, int32_t layer0, int32_t n_layers, 
     ctx->chain_layer = layer0 + n_layers - 1;
     ctx->chain_t0 = t0;
     ctx->chain_n = n;
+    ctx->sweep_layer = -1;   // the encoded layers hold more tokens now
   }
   return QKV_OK;
+}
+
+// Cross-layer read: bring the sweep region to `layer` over all its tokens,
+// slice by slice.  Layer 0 (SAS-coded) is reconstructed into it; a layer
+// l >= 1 is predicted from the region's layer l-1 and its reconstruction
+// is written over the same slice (the prediction of a slice is complete
+// before its slice is overwritten: both run in stream order).
+static void sweep_to(qkv_ctx *ctx, int layer, hipStream_t st) {
+  const Plan &p = ctx->plan;
+  const qkv_config &c = p.cfg;
+  const int64_t T = ctx->layers[layer].n_tokens, M = p.xl_sweep_slice;
+  const uint64_t HD = uint64_t(c.n_heads) * c.head_dim;
+  const uint64_t kv_stride = HD * c.head_dim + 2 * HD * uint64_t(c.xlayer_rank);
+  uint16_t *sweep = reinterpret_cast<uint16_t *>(ctx->arena + p.xl_sweep_off);
+  float *pred = reinterpret_cast<float *>(scratch(ctx, p.xl_pred_off));
+  float *proj = reinterpret_cast<float *>(scratch(ctx, p.xl_proj_off));
+  ReconArgs r{};
+  r.L = dev_layout(p);
+  r.arena = ctx->arena;
+  r.out = nullptr;
+  r.out_bf16 = 1;
+  for (int64_t ts = 0, sl = 0; ts < T; ts += M, ++sl) {
+    const int64_t ns = std::min(M, T - ts);
+    uint16_t *blk = sweep + uint64_t(sl) * 2 * HD * uint64_t(M);   // [2][H][ns][d]
+    if (layer >= 1) {
+      XlArgs x{};
+      x.H = c.n_heads; x.D = c.head_dim; x.r = c.xlayer_rank; x.n = int32_t(ns);
+      x.chain = blk;
+      x.weights = reinterpret_cast<const uint16_t *>(ctx->predictor) + uint64_t(layer - 1) * 2 * kv_stride;
+      x.kv_weight_stride = kv_stride;
+      x.proj = proj;
+      x.pred = pred;
+      x.b_weights = c.xlayer_adapt ? refit_blocks(ctx, layer) : nullptr;
+      launch_xl_predict(x, 0, 2, st);
+    }
+    for (int kv = 0; kv < 2; ++kv) {
+      r.layer0 = layer;
+      r.kv = kv;
+      r.t0 = int32_t(ts);
+      r.n = int32_t(ns);
+      r.pred = layer >= 1 ? pred + uint64_t(kv) * HD * ns : nullptr;
+      r.chain = blk + uint64_t(kv) * HD * ns;
+      launch_reconstruct(r, 1, ns, 0, st);
+    }
+  }
+  ctx->sweep_layer = layer;
+  ctx->sweep_tokens = T;
 }
 
 // Enqueue the attention of n_q queries over `layer` with the split partials
@@ -338,6 +386,13 @@ static void enqueue_attend(qkv_ctx *ctx, const AttnSplit &w, int32_t layer, cons
   a.lse = d_lse;
   a.part_o = part_o;
   a.part_lse = part_lse;
+  if (p.cfg.xlayer && layer >= 1) {
+    // cross-layer coded layer: the bf16 tiles of the sweep region
+    a.k_new = a.v_new = reinterpret_cast<const uint16_t *>(ctx->arena + p.xl_sweep_off);
+    a.fresh_slice = int32_t(p.xl_sweep_slice);
+    launch_attend_fresh(a, st);
+    return;
+  }
   launch_attend(a, st);
 }
 
@@ -350,10 +405,12 @@ extern "C" int qkv_attend(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t 
   const Plan &p = ctx->plan;
   ensure_cu_count(ctx);
   const AttnSplit w = attention_split(p, ctx->layers[layer].n_tokens, n_q, ctx->n_cu);
+  hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  if (p.cfg.xlayer && (layer >= 1 || p.cfg.n_layers > 1)) sweep_to(ctx, layer, st);
   enqueue_attend(ctx, w, layer, d_q, n_q, q_dtype, d_out, out_dtype, d_lse,
                  reinterpret_cast<float *>(scratch(ctx, p.attn_part_o_off)),
-                 reinterpret_cast<float *>(scratch(ctx, p.attn_part_lse_off)), static_cast<hipStream_t>(stream));
+                 reinterpret_cast<float *>(scratch(ctx, p.attn_part_lse_off)), st);
   ctx->chain_layer = -1;  // scratch reused
   return hip_status(ctx);
 }
@@ -363,7 +420,7 @@ extern "C" int qkv_attend_noalloc(qkv_ctx *ctx, int32_t layer, const void *d_q, 
   const int rc = check_attend(ctx, layer, d_q, n_q, q_dtype, d_out, out_dtype);
   if (rc != QKV_OK) return rc;
   if (n_q == 0) return QKV_OK;
-  if (!ctx->noalloc_scratch) return QKV_E_UNSUPPORTED;
+  if (!ctx->noalloc_scratch || ctx->plan.cfg.xlayer) return QKV_E_UNSUPPORTED;
   const Plan &p = ctx->plan;
   ensure_cu_count(ctx);
   const AttnSplit w = attention_split(p, ctx->layers[layer].n_tokens, n_q, ctx->n_cu);
@@ -428,13 +485,21 @@ extern "C" int qkv_attend_with_chunk(qkv_ctx *ctx, int32_t layer, const void *d_
     ctx->chain_layer = -1;  // scratch reused
     return hip_status(ctx);
   }
+  if (c.xlayer && (layer >= 1 || c.n_layers > 1)) sweep_to(ctx, layer, st);
   AttnArgs a = args_for(n_cache);
-  a.stream_k = ctx->arena + stream_offset(p, layer, 0);
-  a.stream_v = ctx->arena + stream_offset(p, layer, 1);
   a.out = o_part[0];
   a.out_bf16 = 0;
   a.lse = l_part[0];
-  launch_attend(a, st);
+  if (c.xlayer && layer >= 1) {
+    // cross-layer coded layer: the bf16 tiles of the sweep region
+    a.k_new = a.v_new = reinterpret_cast<const uint16_t *>(ctx->arena + p.xl_sweep_off);
+    a.fresh_slice = int32_t(p.xl_sweep_slice);
+    launch_attend_fresh(a, st);
+  } else {
+    a.stream_k = ctx->arena + stream_offset(p, layer, 0);
+    a.stream_v = ctx->arena + stream_offset(p, layer, 1);
+    launch_attend(a, st);
+  }
   f.out = o_part[1];
   f.out_bf16 = 0;
   f.lse = l_part[1];
@@ -541,5 +606,6 @@ extern "C" int qkv_rewind(qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int64_
     ls.n_tokens = n_tokens;
   }
   ctx->chain_layer = -1;
+  ctx->sweep_layer = -1;
   return QKV_OK;
 }

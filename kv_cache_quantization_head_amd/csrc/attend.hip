@@ -244,6 +244,14 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
       }
       if constexpr (FRESH) {
         const uint16_t *row = fresh_p + uint64_t(tile) * AT_BK * D;
+        if (a.fresh_slice > 0) {
+          // key t of tensor it_kv, head h in the block of fresh_slice tokens holding it
+          const int t = ks + tile * AT_BK + it_key;
+          const int M = a.fresh_slice, sl = t / M, ts = t - sl * M;
+          const int ns = min(M, a.n_keys - sl * M);
+          row = a.k_new + uint64_t(sl) * 2 * L.H * uint64_t(M) * D +
+                (uint64_t(it_kv * L.H + h) * ns + ts) * D + it_ch;
+        }
   #pragma unroll
         for (int i = 0; i < KC; ++i) R.cent[i] = *(const uint4 *)(row + 8 * i);
         return;

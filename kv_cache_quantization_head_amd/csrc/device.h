@@ -91,6 +91,10 @@ struct AttnArgs {
   float *part_o;                        // [max_segments][H][n_q][D] partials
   float *part_lse;                      // [max_segments][H][n_q]
   const uint16_t *k_new, *v_new;        // fresh keys/values [H][n_keys][D] bf16 (uncoded read)
+  // uncoded read of the cross-layer sweep region instead: consecutive blocks
+  // of fresh_slice tokens, block s = [2 (K, V)][H][n_s][D] bf16 at
+  // k_new + s * 2 * H * fresh_slice * D (0: the plain layout above)
+  int32_t fresh_slice;
 };
 
 // LSE merge of two complete attention results over disjoint key sets.

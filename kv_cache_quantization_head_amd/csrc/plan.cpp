@@ -88,7 +88,15 @@ int make_plan(const qkv_config *cfg, Plan *plan) {
   // re-fitted predictor blocks (adapted cross-layer mode), kept between calls
   p.xl_refit_off = p.streams_bytes;
   const uint64_t refit_bytes = c.xlayer_adapt ? align_up(uint64_t(c.n_layers) * 2 * H * d * d * 2) : 0;
-  p.scratch_off = p.streams_bytes + refit_bytes;
+  // cross-layer read: one layer's bf16 K and V in blocks of the chunk size
+  p.xl_sweep_slice = p.cfg.max_chunk_tokens;
+  p.xl_sweep_off = p.streams_bytes + refit_bytes;
+  p.xl_sweep_bytes = 0;
+  if (c.xlayer && c.max_query_tokens > 0) {
+    const uint64_t slices = (T + uint64_t(p.xl_sweep_slice) - 1) / uint64_t(p.xl_sweep_slice);
+    p.xl_sweep_bytes = align_up(slices * 2 * H * uint64_t(p.xl_sweep_slice) * d * 2);
+  }
+  p.scratch_off = p.xl_sweep_off + p.xl_sweep_bytes;
   uint64_t attn = 0;
   if (c.max_query_tokens > 0) {
     const uint64_t Q = c.max_query_tokens;
@@ -157,8 +165,13 @@ int check_attend(const qkv_ctx *ctx, int32_t layer, const void *q, int64_t n_q, 
   if (!valid_dtype(q_dtype) || !valid_dtype(out_dtype) || n_q < 0) return QKV_E_INVAL;
   if (n_q > 0 && (!q || !out)) return QKV_E_INVAL;
   if (n_q > ctx->plan.cfg.max_query_tokens) return QKV_E_CAPACITY;
-  if (ctx->plan.cfg.xlayer && layer >= 1) return QKV_E_UNSUPPORTED;
   if (ctx->layers[layer].n_tokens == 0) return QKV_E_STATE;
+  return check_sweep(ctx, layer);
+}
+
+int check_sweep(const qkv_ctx *ctx, int32_t layer) {
+  if (!ctx->plan.cfg.xlayer || layer == 0) return QKV_OK;
+  if (ctx->sweep_layer != layer - 1 || ctx->sweep_tokens != ctx->layers[layer].n_tokens) return QKV_E_STATE;
   return QKV_OK;
 }
 
@@ -172,8 +185,8 @@ int check_attend_with_chunk(const qkv_ctx *ctx, int32_t layer, const void *q, in
   if (n_q > 0 && (!q || !out)) return QKV_E_INVAL;
   if (n_new > 0 && (!k_new || !v_new)) return QKV_E_INVAL;
   if (n_q > ctx->plan.cfg.max_query_tokens) return QKV_E_CAPACITY;
-  if (ctx->plan.cfg.xlayer && layer >= 1) return QKV_E_UNSUPPORTED;
   if (ctx->layers[layer].n_tokens == 0 && n_new == 0) return QKV_E_STATE;
+  if (ctx->layers[layer].n_tokens > 0) return check_sweep(ctx, layer);
   return QKV_OK;
 }
 

@@ -56,6 +56,11 @@ struct Plan {
   uint64_t sort_perm_off, sort_off_off;            // relative to scratch (encode)
   uint64_t sort_tiles;                             // 256-token tiles per call, max
   uint64_t chan_part_off;                          // relative to scratch: [2L][H][kChanParts][d] fp64
+  // cross-layer read: bf16 reconstruction of one layer (the last one read),
+  // in blocks of xl_sweep_slice tokens, each [2][H][n_s][d] (absolute offset;
+  // 0 bytes when the mode or attention is off)
+  uint64_t xl_sweep_off, xl_sweep_bytes;
+  int64_t xl_sweep_slice;
   uint64_t total_bytes;
   int kv_elem_bytes;
 };
@@ -80,6 +85,10 @@ struct qkv_ctx {
   // [chain_t0, chain_t0 + chain_n) is held in scratch after an encode call
   int32_t chain_layer = -1;
   int64_t chain_t0 = 0, chain_n = 0;
+  // cross-layer read: the sweep region holds the bf16 reconstruction of
+  // layer sweep_layer over its first sweep_tokens tokens (-1: nothing valid)
+  int32_t sweep_layer = -1;
+  int64_t sweep_tokens = 0;
   int n_cu = 0;                  // compute units of the device, read at the first attention call
   void *noalloc_scratch = nullptr; // this device's fixed partials array (qkv_attend_noalloc), set at init
   // per-kernel timing (qkv_trace): HIP events (as void*) recorded around each
@@ -101,6 +110,9 @@ int check_encode(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, const voi
                  const void *v, int64_t n);
 int check_attend(const qkv_ctx *ctx, int32_t layer, const void *q, int64_t n_q, int32_t q_dtype,
                  const void *out, int32_t out_dtype);
+// cross-layer mode, layer >= 1: the read of `layer` needs the sweep region to
+// hold layer-1 over every token of `layer` (QKV_OK, else QKV_E_STATE)
+int check_sweep(const qkv_ctx *ctx, int32_t layer);
 int check_reconstruct(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int32_t kv, int64_t t0,
                       int64_t t1, const void *out, int32_t out_dtype);
 int check_rewind(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int64_t n_tokens);

@@ -119,6 +119,14 @@ def test_group_must_divide_and_xlayer_needs_bf16_and_rank():
     assert qkv.workspace_bytes(_cfg(xlayer=1, xlayer_rank=0)) == 0
     assert qkv.workspace_bytes(_cfg(xlayer=1, xlayer_rank=32, kv_dtype=B.QKV_F32)) == 0
     assert qkv.workspace_bytes(_cfg(xlayer=1, xlayer_rank=32)) > 0
+    # the cross-layer read keeps one layer's bf16 K and V in blocks of the
+    # chunk size (two blocks of 32760 tokens for 37440): only with attention
+    H, d, T, M = 12, 128, 37440, 32760
+    sweep = 2 * 2 * H * M * d * 2
+    with_q = qkv.workspace_bytes(_cfg(xlayer=1, xlayer_rank=32))
+    no_q = qkv.workspace_bytes(_cfg(xlayer=1, xlayer_rank=32, max_query_tokens=0))
+    attn = _align(_align(8 * H * 4680 * d * 4) + 8 * H * 4680 * 4)
+    assert with_q - no_q >= sweep and with_q - no_q <= sweep + attn
 
 
 def _init(cfg, arena=FAKE, nbytes=None, predictor=None):
@@ -197,15 +205,17 @@ def test_call_validation_before_enqueue(ctx):
     assert L.qkv_chunk_starts(ctx, 0, None, 0) == 0
 
 
-def test_cross_layer_attend_unsupported_and_order():
+def test_cross_layer_attend_order():
     cfg = _cfg(xlayer=1, xlayer_rank=8)
     rc, c = _init(cfg, predictor=FAKE)
     assert rc == B.QKV_OK
     L = qkv.lib()
     p = ctypes.c_void_p(FAKE)
-    assert L.qkv_attend(c, 1, p, 16, B.QKV_BF16, p, B.QKV_F32, None, None) == B.QKV_E_UNSUPPORTED
-    assert L.qkv_attend_with_chunk(c, 1, p, 16, B.QKV_BF16, p, p, 8, p, B.QKV_F32, None,
-                                   None) == B.QKV_E_UNSUPPORTED
+    # nothing encoded yet, and no layer swept: reading layer 1 is a state error
+    assert L.qkv_attend(c, 1, p, 16, B.QKV_BF16, p, B.QKV_F32, None, None) == B.QKV_E_STATE
+    assert L.qkv_attend_with_chunk(c, 1, p, 16, B.QKV_BF16, None, None, 0, p, B.QKV_F32, None,
+                                   None) == B.QKV_E_STATE
+    assert L.qkv_attend_noalloc(c, 0, p, 16, B.QKV_BF16, p, B.QKV_F32, None, None) == B.QKV_E_STATE
     # layer 1 before layer 0 (no chain) is a state error
     assert L.qkv_encode_chunk(c, 1, 1, p, p, 100, None) == B.QKV_E_STATE
     L.qkv_destroy(c)
