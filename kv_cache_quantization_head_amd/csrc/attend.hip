@@ -24,14 +24,17 @@ namespace qkv {
 //    V on odd threads (every wave runs the same code, stores included; the
 //    threads of a key read one centroid row).  The rebuild is
 //    bf16(fl32 chain: c + sum_s z_s, then fmaf(q_s, sigma_s, .) per stage);
-//    2-bit codes are widened four at a time from one masked code word
-//    (byte-to-float conversions).  Keys past the end rebuild to zero from
-//    zeroed registers.
+//    2-bit codes are widened two at a time by the fp4 conversion.  A key
+//    past the segment's end is rebuilt from the segment's last key (its
+//    logit is masked, so it weighs 0): the loads have no data-dependent
+//    path, and only a segment's last tile runs the masking code.
 //  * Loads are software-pipelined: ids of tile i+2 and the packed data
 //    (codes, scale/zero, centroid rows) of tile i+1 are in flight while tile
 //    i is rebuilt and multiplied; half of the waves multiply before they
 //    rebuild and half after, so that the MFMA work of one wave of a SIMD
-//    overlaps the VALU work of the other.  The chunk table is cached in LDS.
+//    overlaps the VALU work of the other.  The chunk table is cached in LDS;
+//    each item follows its key's chunk with a cursor that only moves
+//    forward.
 //  * The softmax scale is folded into the exponent's fma; the running max is
 //    only raised (and O, l rescaled) when a tile's max exceeds it by more
 //    than 8 (log2 units), so exponentials stay <= 256; row sums of P are
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     const int t1 = int(min(T, t0 + (u_end - u)));
     const int slot = (t0 == 0 && t1 == T) ? -1 : int(lb - (seg * T) / U);
     u += t1 - t0;
-    const uint8_t *idp = FRESH ? nullptr : st + L.ids_off + uint64_t(h) * L.ids_head;
+    const uint8_t *ids_base = FRESH ? nullptr : st + L.ids_off;
     const int ks = t0 * AT_BK;
     const int ke = min(a.n_keys, t1 * AT_BK);
     const int n_tiles = ke > ks ? (ke - ks + AT_BK - 1) / AT_BK : 0;
@@ -193,6 +196,9 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
       }
       qf[s] = v;
     }
+    // the query loads complete before the tile pipeline starts, so that no
+    // wait for them is left inside the tile loop (vmcnt(0))
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     bf16x2 ones2;
     ones2[0] = (__bf16)1.0f;
     ones2[1] = (__bf16)1.0f;
@@ -204,13 +210,27 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     float l_part = 0.0f;       // this lane's share of the row sum
     float m_run = -INFINITY;
 
-    // id of the item's key in a tile (-1: no key)
-    auto load_ids = [&](int tile) -> int {
-      if (!has_item || tile >= n_tiles) return -1;
-      const int t = ks + tile * AT_BK + it_key;
-      if (t >= ke) return -1;
-      if constexpr (FRESH) return 0;
-      return L.id_bytes == 1 ? int(idp[t]) : int(((const uint16_t *)idp)[t]);
+    // The item's key in a tile, clamped to the segment's last key: a key
+    // past the end is rebuilt from the last key's data (finite values whose
+    // logits the last tile masks to -inf, so they weigh 0 in P V), which
+    // leaves no data-dependent path in the loads.
+    auto item_key = [&](int tile) -> int { return min(ks + tile * AT_BK + it_key, ke - 1); };
+    // id of the item's key in a tile (tiles past the segment load nothing)
+    // The id of the item's key in a tile is read as the aligned dword of the
+    // ids region (256-byte aligned) that holds it, for 1- and 2-byte ids
+    // alike, with no condition on the load (a tile past the segment reads
+    // the segment's last tile); the id is cut out of the word only where it
+    // is used, a tile later.  A load per width, or a shift right after the
+    // load, made the compiler wait there for every load in flight.
+    auto id_off = [&](int tile) -> uint64_t {
+      return uint64_t(h) * L.ids_head + uint64_t(item_key(min(tile, n_tiles - 1))) * uint64_t(L.id_bytes);
+    };
+    auto load_id_word = [&](int tile) -> uint32_t {
+      if constexpr (FRESH) return 0u;
+      return *(const uint32_t *)(ids_base + (id_off(tile) & ~uint64_t(3)));
+    };
+    auto id_of = [&](int tile, uint32_t w) -> int {
+      return int((w >> (8 * uint32_t(id_off(tile) & 3))) & (L.id_bytes == 1 ? 0xffu : 0xffffu));
     };
     struct Regs {
       uint32_t codes[SMAX][KW];
@@ -227,26 +247,18 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     // fresh rows: channels it_ch .. it_ch+31 of key t_first of head h
     const uint16_t *fresh_p = FRESH ? (it_kv ? a.v_new : a.k_new) + (uint64_t(h) * a.n_keys + t_first) * D + it_ch
                                     : nullptr;
-    const uint64_t tile_codes = uint64_t(AT_BK) * L.codes_token, tile_meta = uint64_t(AT_BK) * L.meta_token;
-    // packed data of the item's key: centroid slice, codes, (sigma, z); all
-    // zero when there is no key, which rebuilds to zero
-    auto load_data = [&](int tile, int id) {
-      if (id < 0) {
-  #pragma unroll
-        for (int i = 0; i < KC; ++i) R.cent[i] = make_uint4(0u, 0u, 0u, 0u);
-  #pragma unroll
-        for (int s2 = 0; s2 < SMAX; ++s2) {
-          R.meta[s2] = 0u;
-  #pragma unroll
-          for (int w = 0; w < KW; ++w) R.codes[s2][w] = 0u;
-        }
-        return;
-      }
+    const uint64_t tile_meta = uint64_t(AT_BK) * L.meta_token;
+    // chunk (snapshot slot) of the item's key, advanced tile by tile: keys
+    // only grow, and a tile's keys rarely cross more than one chunk start
+    int c_cur = (FRESH || nch_s == 1) ? 0 : chunk_of_lds(starts_s, nch_s, t_first);
+    // packed data of the item's key: centroid slice, codes, (sigma, z)
+    auto load_data = [&](int tile, uint32_t id_word) {
+      if (!has_item || tile >= n_tiles) return;   // wave-uniform
+      const int t = item_key(tile);
       if constexpr (FRESH) {
-        const uint16_t *row = fresh_p + uint64_t(tile) * AT_BK * D;
+        const uint16_t *row = fresh_p + uint64_t(t - t_first) * D;
         if (a.fresh_slice > 0) {
           // key t of tensor it_kv, head h in the block of fresh_slice tokens holding it
-          const int t = ks + tile * AT_BK + it_key;
           const int M = a.fresh_slice, sl = t / M, ts = t - sl * M;
           const int ns = min(M, a.n_keys - sl * M);
           row = a.k_new + uint64_t(sl) * 2 * L.H * uint64_t(M) * D +
@@ -256,12 +268,12 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
         for (int i = 0; i < KC; ++i) R.cent[i] = *(const uint4 *)(row + 8 * i);
         return;
       }
-      const int cslot = nch_s > 1 ? chunk_of_lds(starts_s, nch_s, ks + tile * AT_BK + it_key) : 0;
-      const uint8_t *crow = cb_p + uint64_t(cslot) * L.cb_chunk + uint64_t(id) * (D * EB);
+      while (c_cur + 1 < nch_s && starts_s[c_cur + 1] <= t) ++c_cur;
+      const uint8_t *crow = cb_p + uint64_t(c_cur) * L.cb_chunk + uint64_t(id_of(tile, id_word)) * (D * EB);
   #pragma unroll
       for (int i = 0; i < KC; ++i) R.cent[i] = *(const uint4 *)(crow + 16 * i);
-      const uint8_t *cp = code_p + uint64_t(tile) * tile_codes;
-      const uint8_t *mp = meta_p + uint64_t(tile) * tile_meta;
+      const uint8_t *cp = code_p + uint64_t(t - t_first) * L.codes_token;
+      const uint8_t *mp = meta_p + uint64_t(t - t_first) * L.meta_token;
   #pragma unroll
       for (int s2 = 0; s2 < SMAX; ++s2) {
         if constexpr (KW == 2) {
@@ -389,6 +401,8 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
       }
     };
 
+    // a tile that reaches past the segment's last key (its last tile only)
+    auto partial_tile = [&](int tile) { return ks + (tile + 1) * AT_BK > ke; };
     auto compute_tile = [&](int tile) {
       const int buf = tile & 1;
       const int kt0 = ks + tile * AT_BK;
@@ -404,7 +418,10 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], s1, 0, 0, 0);
       }
-      if (kt0 + AT_BK > ke) {
+      if (partial_tile(tile)) {
+        // an empty volatile asm keeps this a branch taken on the last tile
+        // only (speculated, its selects would run on every tile)
+        asm volatile("");
   #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt0 + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -465,11 +482,11 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     // w+4 and between waves 2k and 2k+1, whichever way waves sit on SIMDs.
     const bool mfma_first = ((wave >> 2) ^ wave) & 1;
     __syncthreads();  // previous segment's tiles no longer read
-    int id_next;   // id of the item's key in tile+2
-    load_data(0, load_ids(0));
+    uint32_t id_next;   // id word of the item's key in tile+2
+    load_data(0, load_id_word(0));
     dequant_store(0, 0);
-    load_data(1, load_ids(1));
-    id_next = load_ids(2);
+    load_data(1, load_id_word(1));
+    id_next = load_id_word(2);
     __syncthreads();
 
     for (int tile = 0; tile < n_tiles; ++tile) {
@@ -477,7 +494,7 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
       if (mfma_first) compute_tile(tile);
       if (tile + 1 < n_tiles) dequant_store(buf ^ 1, tile + 1);   // data of tile+1 already in R
       load_data(tile + 2, id_next);
-      id_next = load_ids(tile + 3);
+      id_next = load_id_word(tile + 3);
       if (!mfma_first) compute_tile(tile);
       __syncthreads();
     }
@@ -589,24 +606,29 @@ __global__ __launch_bounds__(256) void k_attend_merge2(MergeArgs m) {
 
 // ---------------------------------------------------------------- launchers
 
+template <int D, int G, int BITS, bool BF, int S, bool OUTL>
+static void launch_attend_s(const AttnArgs &a, const dim3 &grid, hipStream_t st) {
+  QKV_LAUNCH((k_attend3<D, G, BITS, BF, S, false, OUTL>), grid, dim3(512), 0, st, a);
+}
+
 template <int D, int G, int BITS, bool BF>
 static void launch_attend_t(const AttnArgs &a, hipStream_t st) {
   const int64_t total = int64_t(a.n_ktiles) * a.n_qblocks * a.L.H;
   const dim3 grid(unsigned(cdiv(total, a.units_per_block)));
   if (a.L.mask_off) {
     switch (a.L.S) {
-      case 1: QKV_LAUNCH((k_attend3<D, G, BITS, BF, 1, false, true>), grid, dim3(512), 0, st, a); break;
-      case 2: QKV_LAUNCH((k_attend3<D, G, BITS, BF, 2, false, true>), grid, dim3(512), 0, st, a); break;
-      case 3: QKV_LAUNCH((k_attend3<D, G, BITS, BF, 3, false, true>), grid, dim3(512), 0, st, a); break;
-      default: QKV_LAUNCH((k_attend3<D, G, BITS, BF, 4, false, true>), grid, dim3(512), 0, st, a); break;
+      case 1: launch_attend_s<D, G, BITS, BF, 1, true>(a, grid, st); break;
+      case 2: launch_attend_s<D, G, BITS, BF, 2, true>(a, grid, st); break;
+      case 3: launch_attend_s<D, G, BITS, BF, 3, true>(a, grid, st); break;
+      default: launch_attend_s<D, G, BITS, BF, 4, true>(a, grid, st); break;
     }
     return;
   }
   switch (a.L.S) {
-    case 1: QKV_LAUNCH((k_attend3<D, G, BITS, BF, 1>), grid, dim3(512), 0, st, a); break;
-    case 2: QKV_LAUNCH((k_attend3<D, G, BITS, BF, 2>), grid, dim3(512), 0, st, a); break;
-    case 3: QKV_LAUNCH((k_attend3<D, G, BITS, BF, 3>), grid, dim3(512), 0, st, a); break;
-    default: QKV_LAUNCH((k_attend3<D, G, BITS, BF, 4>), grid, dim3(512), 0, st, a); break;
+    case 1: launch_attend_s<D, G, BITS, BF, 1, false>(a, grid, st); break;
+    case 2: launch_attend_s<D, G, BITS, BF, 2, false>(a, grid, st); break;
+    case 3: launch_attend_s<D, G, BITS, BF, 3, false>(a, grid, st); break;
+    default: launch_attend_s<D, G, BITS, BF, 4, false>(a, grid, st); break;
   }
 }
 
