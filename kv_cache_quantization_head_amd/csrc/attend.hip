@@ -429,11 +429,24 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
           if (key + 32 >= ke) s1[r] = -INFINITY;
         }
       }
-      float tmax = -INFINITY;
+      // tile max: a tree of three-way maxima (v_maximum3_f32) over the 32 values
+      // (finite or -inf)
+      float vv[32];
   #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        tmax = __builtin_elementwise_maximum(tmax, __builtin_elementwise_maximum(s0[r], s1[r]));
-      tmax = pair_max(tmax);
+      for (int r = 0; r < 16; ++r) { vv[r] = s0[r]; vv[16 + r] = s1[r]; }
+      int nv = 32;
+  #pragma unroll
+      for (int lvl = 0; lvl < 4; ++lvl) {
+        if (nv == 1) break;
+        int o = 0;
+  #pragma unroll
+        for (int i = 0; i + 3 <= nv; i += 3)
+          vv[o++] = __builtin_elementwise_maximum(vv[i], __builtin_elementwise_maximum(vv[i + 1], vv[i + 2]));
+        if (nv % 3 == 2) vv[o++] = __builtin_elementwise_maximum(vv[nv - 2], vv[nv - 1]);
+        else if (nv % 3 == 1) vv[o++] = vv[nv - 1];
+        nv = o;
+      }
+      float tmax = pair_max(vv[0]);
       const float mt = tmax * sc;
       const bool need = mt > m_run + AT3_TAU;
       if (__any(need)) {
