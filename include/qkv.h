@@ -42,7 +42,12 @@
  *
  * Streams: every call enqueues on the given HIP stream (a hipStream_t passed
  * as void*, NULL = the default stream) and returns without synchronizing.
- * Calls on one context must be serialized by the caller.
+ * All device work of one context must be ordered: one stream, or event
+ * dependencies between the streams used.  The attention's split partials,
+ * the encoder's sort buffers and channel sums and the cross-layer chain
+ * and prediction share one scratch region of the arena, so an encode and an
+ * attention of one context running concurrently on two unordered streams
+ * corrupt each other without any error being reported.
  *
  * Errors: every entry point returns a qkv_status.  Arguments are validated
  * before anything is enqueued; a call that fails validation enqueues nothing
