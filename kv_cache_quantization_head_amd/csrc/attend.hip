@@ -65,15 +65,6 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ int chunk_of_lds(const int32_t *starts, int n_chunks, int t) {
-  int lo = 0, hi = n_chunks - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (starts[mid] <= t) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 constexpr float AT3_TAU = 8.0f;
 
 // w[i] for a run-time i < N (selects, no indexed register access)

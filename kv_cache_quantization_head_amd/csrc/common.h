@@ -129,6 +129,16 @@ __device__ __forceinline__ int chunk_of(const StreamHeader *hdr, int t) {
   return lo;
 }
 
+// chunk_of over a copy of the chunk table's first tokens in LDS
+__device__ __forceinline__ int chunk_of_lds(const int32_t *starts, int n_chunks, int t) {
+  int lo = 0, hi = n_chunks - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (starts[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 // ---------------------------------------------------------------- launch helpers
 
 static inline unsigned cdiv(int64_t a, int64_t b) { return unsigned((a + b - 1) / b); }

@@ -5,35 +5,55 @@ namespace qkv {
 
 // ----------------------------------------------------------------- decode
 
-// Rebuild one group (G channels) of token tt of head h in fp32:
-// xhat = fl32(...fl32(base + rhat_1)... + rhat_S).  xh holds the base on entry.
+// Codes and (sigma, z) of the stages of one group (G channels) of token tt
+// of head h, all loaded before any is used so that their loads are in
+// flight together (stages past L.S are left unset).
+constexpr int kStagesMax = 4;
+template <int G, int BITS>
+struct GroupStages {
+  static constexpr int WORDS = G * BITS / 32;
+  uint32_t w[kStagesMax][WORDS];
+  uint32_t m[kStagesMax];
+};
 template <int D, int G, int BITS>
-__device__ __forceinline__ void add_stages(const uint8_t *st, const DevLayout &L, int h, int64_t tt,
-                                           int g, float *xh) {
+__device__ __forceinline__ void load_stages(const uint8_t *st, const DevLayout &L, int h, int64_t tt, int g,
+                                            GroupStages<G, BITS> &gs) {
   constexpr int WORDS = G * BITS / 32;
-  for (int s = 0; s < L.S; ++s) {
+#pragma unroll
+  for (int s = 0; s < kStagesMax; ++s) {
+    if (s >= L.S) break;
     const uint8_t *cp = st + L.codes_off + uint64_t(s) * L.codes_stage + uint64_t(h) * L.codes_head +
                         uint64_t(tt) * L.codes_token + uint64_t(g) * (G * BITS / 8);
-    uint32_t w[WORDS];
     if constexpr (WORDS == 2) {
       const uint2 v = *(const uint2 *)cp;
-      w[0] = v.x; w[1] = v.y;
+      gs.w[s][0] = v.x; gs.w[s][1] = v.y;
     } else {
 #pragma unroll
       for (int i = 0; i < WORDS; i += 4) {
         const uint4 v = *(const uint4 *)(cp + 4 * i);
-        w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
+        gs.w[s][i] = v.x; gs.w[s][i + 1] = v.y; gs.w[s][i + 2] = v.z; gs.w[s][i + 3] = v.w;
       }
     }
-    const uint32_t m = *((const uint32_t *)(st + L.meta_off + uint64_t(s) * L.meta_stage +
-                                            uint64_t(h) * L.meta_head + uint64_t(tt) * L.meta_token) + g);
-    const float sf = f16_bits_to_f32(uint16_t(m & 0xffffu));
-    const float zf = f16_bits_to_f32(uint16_t(m >> 16));
+    gs.m[s] = *((const uint32_t *)(st + L.meta_off + uint64_t(s) * L.meta_stage + uint64_t(h) * L.meta_head +
+                                   uint64_t(tt) * L.meta_token) + g);
+  }
+}
+
+// Rebuild one group in fp32: xhat = fl32(...fl32(base + rhat_1)... + rhat_S).
+// xh holds the base on entry.
+template <int G, int BITS>
+__device__ __forceinline__ void add_stages(const GroupStages<G, BITS> &gs, int S, float *xh) {
+  constexpr int WORDS = G * BITS / 32;
+#pragma unroll
+  for (int s = 0; s < kStagesMax; ++s) {
+    if (s >= S) break;
+    const float sf = f16_bits_to_f32(uint16_t(gs.m[s] & 0xffffu));
+    const float zf = f16_bits_to_f32(uint16_t(gs.m[s] >> 16));
     float q[G];
 #pragma unroll
     for (int i = 0; i < WORDS; ++i) {
-      if constexpr (BITS == 2) widen_codes2(w[i], q + 16 * i);
-      else widen_codes4(w[i], q + 8 * i);
+      if constexpr (BITS == 2) widen_codes2(gs.w[s][i], q + 16 * i);
+      else widen_codes4(gs.w[s][i], q + 8 * i);
     }
 #pragma unroll
     for (int j = 0; j < G; ++j) xh[j] = xh[j] + fmaf(q[j], sf, zf);
@@ -84,10 +104,8 @@ __device__ __forceinline__ void add_stages_outl(const uint8_t *st, const DevLayo
 // Centroid base of token tt (snapshot of its chunk).
 template <int D, int G, bool CB_BF16>
 __device__ __forceinline__ void centroid_base(const uint8_t *st, const DevLayout &L, int h, int tt, int g,
-                                              float *xh) {
+                                              int slot, float *xh) {
   constexpr int EB = CB_BF16 ? 2 : 4;
-  const StreamHeader *hdr = (const StreamHeader *)(st + L.header_off);
-  const int slot = chunk_of(hdr, tt);
   const int id = load_id(st + L.ids_off + uint64_t(h) * L.ids_head, L.id_bytes, tt);
   const uint8_t *crow = st + L.cb_off + uint64_t(slot) * L.cb_chunk + uint64_t(h) * L.cb_head +
                         uint64_t(id) * D * EB + uint64_t(g) * G * EB;
@@ -144,20 +162,30 @@ __global__ __launch_bounds__(256) void k_reconstruct(ReconArgs a, int64_t out_to
   // items of this wave that exist (the run ends at the last token)
   const int wave_item0 = idx - lane;
   const int valid_lanes = int(min<int64_t>(64, int64_t(a.n) * NG - wave_item0));
-  if (valid_lanes <= 0) return;             // whole wave past the end
   const uint8_t *st = stream_ptr(a.arena, L, a.layer0 + lrel, a.kv);
+  // the chunk table (first token of each chunk) staged in LDS once per block
+  __shared__ int32_t starts_s[kMaxChunks + 1];
+  const StreamHeader *hdr = (const StreamHeader *)(st + L.header_off);
+  const int nch = hdr->n_chunks;
+  if (nch > 1 && (!a.pred || OUTL)) {
+    for (int i = threadIdx.x; i < nch; i += blockDim.x) starts_s[i] = hdr->start[i];
+    __syncthreads();
+  }
+  if (valid_lanes <= 0) return;             // whole wave past the end
   const int tt = a.t0 + min(t, a.n - 1);
+  const int slot = nch > 1 && (!a.pred || OUTL) ? chunk_of_lds(starts_s, nch, tt) : 0;
+  GroupStages<G, BITS> gs;
+  if constexpr (!OUTL) load_stages<D, G, BITS>(st, L, h, tt, g, gs);
   float xh[G];
   if (a.pred) {
     const float *p = a.pred + (uint64_t(h) * a.n + min(t, a.n - 1)) * D + g * G;
 #pragma unroll
     for (int j = 0; j < G; ++j) xh[j] = p[j];
   } else {
-    centroid_base<D, G, CB_BF16>(st, L, h, tt, g, xh);
+    centroid_base<D, G, CB_BF16>(st, L, h, tt, g, slot, xh);
   }
   if constexpr (OUTL) {
     constexpr int FW = (G + 31) / 32;
-    const int slot = chunk_of((const StreamHeader *)(st + L.header_off), tt);
     const uint32_t *mw = (const uint32_t *)(st + L.mask_off + uint64_t(slot) * L.mask_chunk +
                                             uint64_t(h) * L.mask_head);
     uint32_t fm[FW];
@@ -165,7 +193,7 @@ __global__ __launch_bounds__(256) void k_reconstruct(ReconArgs a, int64_t out_to
     for (int i = 0; i < FW; ++i) fm[i] = mw[g * FW + i];
     add_stages_outl<D, G, BITS>(st, L, h, tt, g, xh, fm);
   } else {
-    add_stages<D, G, BITS>(st, L, h, tt, g, xh);
+    add_stages<G, BITS>(gs, L.S, xh);
   }
   // first item of the wave: token t_w = wave_item0 / NG, group 0 (runs of a
   // wave start at a token boundary because 64 % NG == 0)
