@@ -19,7 +19,7 @@ namespace qkv {
 // time (transposed, fp32; outputs past r read zero columns).
 constexpr int XL_MC = 32;
 __host__ __device__ constexpr int xl_project_groups(int r) { return r <= 32 ? 4 : 8; }
-__global__ __launch_bounds__(256) void k_xl_project(XlArgs a, int kv0) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_xl_project(XlArgs a, int kv0) {
   __shared__ float ys[XL_MC][256 + 4];    // [m][token]
   __shared__ float vs[XL_MC][64 + 4];     // [m][k]
   const int KG = xl_project_groups(a.r), KP = 8 * KG, TG = 256 / KG, TT = 4 * TG;
@@ -34,18 +34,45 @@ __global__ __launch_bounds__(256) void k_xl_project(XlArgs a, int kv0) {
   for (int u = 0; u < 4; ++u)
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[u][c] = 0.0;
-  for (uint64_t m0 = 0; m0 < HD; m0 += XL_MC) {
+  // The next chunk's operands are loaded into registers while the current
+  // one is multiplied: y as 16-byte pieces (token, 8 channels), V as bf16.
+  constexpr int YP = XL_MC * 256 / 8 / 256;             // y pieces per thread (TT = 256)
+  constexpr int VP = XL_MC * 64 / 256;                  // V entries per thread (KP <= 64)
+  uint4 ypre[YP];
+  uint32_t vpre[VP];
+  auto fetch = [&](uint64_t m0) {
     const int hh = int(m0 / a.D), j0 = int(m0 % a.D);   // a chunk lies inside one head (D % 32 == 0)
-    __syncthreads();                                    // previous chunk consumed
-    for (int e = tid; e < TT * XL_MC; e += 256) {
-      const int tt = e / XL_MC, jj = e % XL_MC, t = min(t0 + tt, a.n - 1);
-      ys[jj][tt] = bf16_to_f32(y[(uint64_t(hh) * a.n + t) * a.D + j0 + jj]);
+#pragma unroll
+    for (int i = 0; i < YP; ++i) {
+      const int e8 = tid + 256 * i, tt = e8 / (XL_MC / 8), j8 = 8 * (e8 % (XL_MC / 8));
+      const int t = min(t0 + tt, a.n - 1);
+      if (tt < TT) ypre[i] = *(const uint4 *)(y + (uint64_t(hh) * a.n + t) * a.D + j0 + j8);
     }
-    for (int e = tid; e < XL_MC * KP; e += 256) {
-      const int jj = e / KP, kk = e % KP;
-      vs[jj][kk] = kk < a.r ? bf16_to_f32(Vw[(m0 + jj) * a.r + kk]) : 0.0f;
+#pragma unroll
+    for (int i = 0; i < VP; ++i) {
+      const int e = tid + 256 * i, jj = e / KP, kk = e % KP;
+      if (jj < XL_MC) vpre[i] = kk < a.r ? uint32_t(Vw[(m0 + jj) * a.r + kk]) : 0u;
+    }
+  };
+  fetch(0);
+  for (uint64_t m0 = 0; m0 < HD; m0 += XL_MC) {
+    __syncthreads();                                    // previous chunk consumed
+#pragma unroll
+    for (int i = 0; i < YP; ++i) {
+      const int e8 = tid + 256 * i, tt = e8 / (XL_MC / 8), j8 = 8 * (e8 % (XL_MC / 8));
+      if (tt < TT) {
+        const uint32_t w[4] = {ypre[i].x, ypre[i].y, ypre[i].z, ypre[i].w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ys[j8 + q][tt] = bf16_to_f32((w[q >> 1] >> (16 * (q & 1))) & 0xffffu);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VP; ++i) {
+      const int e = tid + 256 * i, jj = e / KP, kk = e % KP;
+      if (jj < XL_MC) vs[jj][kk] = bf16_to_f32(vpre[i]);
     }
     __syncthreads();
+    if (m0 + XL_MC < HD) fetch(m0 + XL_MC);
 #pragma unroll 4
     for (int jj = 0; jj < XL_MC; ++jj) {
       const float4 yv = *(const float4 *)&ys[jj][4 * tg];
@@ -73,13 +100,16 @@ __global__ __launch_bounds__(256) void k_xl_project(XlArgs a, int kv0) {
 
 // pred[h][t][i] = sum_j B_h[i][j] y[t][j] (order j), then + sum_k U[h*D+i][k]
 // w[t][k] (order k), fp64, rounded once to fp32.  Block = 256 threads =
-// (token groups of 4) x (output groups of 8) over token tiles of 4*256/(D/8)
-// tokens; B_h and U_h are staged once per block (transposed, as bf16: two
-// blocks fit a CU) and the block walks every gridDim.x-th token tile.
-__global__ __launch_bounds__(256) void k_xl_predict(XlArgs a, int kv0) {
+// (token groups of XL_PT) x (output groups of 8) over token tiles of
+// XL_PT*256/(D/8) tokens: a thread's 8 x 8 fp64 accumulators take 64 fmas per
+// 16 operands converted from bf16.  B_h and U_h are staged once per block
+// (transposed, as bf16: two blocks fit a CU) and the block walks every
+// gridDim.x-th token tile.
+constexpr int XL_PT = 8;                     // tokens per thread
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_xl_predict(XlArgs a, int kv0) {
   extern __shared__ uint16_t xs16[];
   const int D = a.D, RP = (a.r + 7) & ~7;
-  const int IG = D / 8, TG = 256 / IG, TT = 4 * TG;
+  const int IG = D / 8, TG = 256 / IG, TT = XL_PT * TG;
   uint16_t *bsT = xs16;                       // [D j][D i] bf16
   uint16_t *usT = bsT + D * D;                // [RP k][D i]
   uint16_t *ysT = usT + RP * D;               // [D j][TT]
@@ -114,22 +144,24 @@ __global__ __launch_bounds__(256) void k_xl_predict(XlArgs a, int kv0) {
       wsT[kk * TT + tt] = kk < a.r ? f32_to_bf16_bits(w[uint64_t(t) * a.r + kk]) : uint16_t(0);
     }
     __syncthreads();
-    double acc[4][8];
+    double acc[XL_PT][8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < XL_PT; ++u)
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[u][c] = 0.0;
     auto step = [&](const uint16_t *ycol, const uint16_t *bcol) {
-      const uint2 yv = *(const uint2 *)(ycol + 4 * tg);
+      const uint4 yv = *(const uint4 *)(ycol + XL_PT * tg);
       const uint4 bv = *(const uint4 *)(bcol + 8 * ig);
-      const double yd[4] = {double(__uint_as_float(yv.x << 16)), double(__uint_as_float(yv.x & 0xffff0000u)),
-                            double(__uint_as_float(yv.y << 16)), double(__uint_as_float(yv.y & 0xffff0000u))};
+      const double yd[XL_PT] = {double(__uint_as_float(yv.x << 16)), double(__uint_as_float(yv.x & 0xffff0000u)),
+                                double(__uint_as_float(yv.y << 16)), double(__uint_as_float(yv.y & 0xffff0000u)),
+                                double(__uint_as_float(yv.z << 16)), double(__uint_as_float(yv.z & 0xffff0000u)),
+                                double(__uint_as_float(yv.w << 16)), double(__uint_as_float(yv.w & 0xffff0000u))};
       const double bd[8] = {double(__uint_as_float(bv.x << 16)), double(__uint_as_float(bv.x & 0xffff0000u)),
                             double(__uint_as_float(bv.y << 16)), double(__uint_as_float(bv.y & 0xffff0000u)),
                             double(__uint_as_float(bv.z << 16)), double(__uint_as_float(bv.z & 0xffff0000u)),
                             double(__uint_as_float(bv.w << 16)), double(__uint_as_float(bv.w & 0xffff0000u))};
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < XL_PT; ++u)
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[u][c] = fma(bd[c], yd[u], acc[u][c]);
     };
@@ -139,8 +171,8 @@ __global__ __launch_bounds__(256) void k_xl_predict(XlArgs a, int kv0) {
     }
     for (int kk = 0; kk < a.r; ++kk) step(wsT + kk * TT, usT + kk * D);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = t0 + 4 * tg + u;
+    for (int u = 0; u < XL_PT; ++u) {
+      const int t = t0 + XL_PT * tg + u;
       if (t >= a.n) continue;
       float *pp = a.pred + (uint64_t(kv) * HD * a.n) + (uint64_t(h) * a.n + t) * D + 8 * ig;
       *(float4 *)pp = make_float4(float(acc[u][0]), float(acc[u][1]), float(acc[u][2]), float(acc[u][3]));
@@ -327,7 +359,7 @@ void launch_xl_predict(const XlArgs &a, int kv0, int n_kv, hipStream_t st) {
   const int TT = 4 * (256 / xl_project_groups(a.r));
   if (!a.skip_project) QKV_LAUNCH(k_xl_project, dim3(cdiv(a.n, TT), n_kv), dim3(256), 0, st, a, kv0);
   const int RP = (a.r + 7) & ~7;
-  const int IG = a.D / 8, TTp = 4 * (256 / IG);
+  const int IG = a.D / 8, TTp = XL_PT * (256 / IG);
   const size_t lds = size_t(a.D * a.D + RP * a.D + a.D * TTp + RP * TTp) * 2;
   (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_xl_predict),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
