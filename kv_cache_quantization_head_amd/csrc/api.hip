@@ -379,6 +379,8 @@ static void enqueue_attend(qkv_ctx *ctx, const AttnSplit &w, int32_t layer, cons
   a.n_qblocks = int32_t(w.n_qblocks);
   a.n_ktiles = int32_t(w.n_ktiles);
   a.units_per_block = int32_t(w.units_per_block);
+  a.head_blocks = int32_t(w.head_blocks);
+  a.main_tiles = int32_t(w.main_tiles);
   a.max_segments = int32_t(w.max_segments);
   a.xcd_remap = w.n_blocks % 8 == 0;
   a.out = d_out;
@@ -466,6 +468,8 @@ extern "C" int qkv_attend_with_chunk(qkv_ctx *ctx, int32_t layer, const void *d_
     a.n_qblocks = int32_t(w.n_qblocks);
     a.n_ktiles = int32_t(w.n_ktiles);
     a.units_per_block = int32_t(w.units_per_block);
+    a.head_blocks = int32_t(w.head_blocks);
+    a.main_tiles = int32_t(w.main_tiles);
     a.max_segments = int32_t(w.max_segments);
     a.xcd_remap = w.n_blocks % 8 == 0;
     a.part_o = part_o;

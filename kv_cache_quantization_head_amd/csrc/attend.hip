@@ -137,19 +137,58 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   // query block) for the merge kernel.  Blocks are numbered so that each XCD
   // (blocks are dealt to the 8 XCDs round robin) gets a consecutive range of
   // runs: the query blocks of one head then share that XCD's L2.
+  //
+  // Per-head split (head_blocks > 0): block j of head h takes, for j below
+  // the number of query blocks, key tiles [0, main_tiles) of query block j
+  // (partial slot 0), so a head's query blocks read the same tiles side by
+  // side; the other blocks take runs of the tails [main_tiles, T) of the
+  // head's query blocks in order (slot 1 + the run's index among the runs
+  // meeting that query block's tail).
   const int lb = a.xcd_remap ? (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8 : blockIdx.x;
   const int64_t T = a.n_ktiles, U = a.units_per_block;
   const int64_t total = T * a.n_qblocks * L.H;
-  int64_t u = int64_t(lb) * U;
-  const int64_t u_end = min(total, u + U);
+  const int HB = a.head_blocks;
+  const int hb = HB ? lb / HB : 0, jb = HB ? lb % HB : 0;
+  const int64_t TL = T - a.main_tiles;      // tail tiles of a query block (per-head split)
+  int64_t u, u_end;                          // stream-K units, or the block's tail units
+  if (!HB) {
+    u = int64_t(lb) * U;
+    u_end = min(total, u + U);
+  } else if (hb >= L.H) {
+    u = u_end = 0;
+  } else if (jb < a.n_qblocks) {
+    u = 0;
+    u_end = 1;                               // the one main segment
+  } else {
+    u = int64_t(jb - a.n_qblocks) * U;
+    u_end = min(TL * a.n_qblocks, u + U);
+  }
   __syncthreads();  // chunk table in LDS
   while (u < u_end) {
-    const int64_t seg = u / T;
-    const int h = int(seg / a.n_qblocks), qblk = int(seg % a.n_qblocks);
-    const int t0 = int(u % T);
-    const int t1 = int(min(T, t0 + (u_end - u)));
-    const int slot = (t0 == 0 && t1 == T) ? -1 : int(lb - (seg * T) / U);
-    u += t1 - t0;
+    int h, qblk, t0, t1, slot;
+    if (!HB) {
+      const int64_t seg = u / T;
+      h = int(seg / a.n_qblocks);
+      qblk = int(seg % a.n_qblocks);
+      t0 = int(u % T);
+      t1 = int(min(T, t0 + (u_end - u)));
+      slot = (t0 == 0 && t1 == T) ? -1 : int(lb - (seg * T) / U);
+      u += t1 - t0;
+    } else if (jb < a.n_qblocks) {
+      h = hb;
+      qblk = jb;
+      t0 = 0;
+      t1 = a.main_tiles;
+      slot = t1 == T ? -1 : 0;
+      u = u_end;
+    } else {
+      h = hb;
+      qblk = int(u / TL);
+      t0 = int(a.main_tiles + u % TL);
+      t1 = int(min(T, t0 + (u_end - u)));
+      slot = 1 + int((jb - a.n_qblocks) - (int64_t(qblk) * TL) / U);
+      u += t1 - t0;
+    }
     const uint8_t *ids_base = FRESH ? nullptr : st + L.ids_off;
     const int ks = t0 * AT_BK;
     const int ke = min(a.n_keys, t1 * AT_BK);
@@ -548,8 +587,15 @@ __global__ __launch_bounds__(256) void k_attend_merge(AttnArgs a) {
   if (idx >= int64_t(a.n_q) * D4) return;
   const int q = int(idx / D4), d4 = int(idx % D4), h = blockIdx.y;
   const int64_t T = a.n_ktiles, U = a.units_per_block;
-  const int64_t first = (int64_t(h) * a.n_qblocks + q / AT_BQ) * T;
-  const int nseg = int((first + T - 1) / U - first / U) + 1;
+  int nseg;
+  if (a.head_blocks) {
+    // the main segment, then the runs meeting the query block's tail
+    const int64_t TL = T - a.main_tiles, qb = q / AT_BQ;
+    nseg = TL == 0 ? 1 : 1 + int(((qb + 1) * TL - 1) / U - (qb * TL) / U) + 1;
+  } else {
+    const int64_t first = (int64_t(h) * a.n_qblocks + q / AT_BQ) * T;
+    nseg = int((first + T - 1) / U - first / U) + 1;
+  }
   if (nseg == 1) return;
   float ls[kMaxSplits];
   float mx = -INFINITY;
@@ -610,6 +656,15 @@ __global__ __launch_bounds__(256) void k_attend_merge2(MergeArgs m) {
 
 // ---------------------------------------------------------------- launchers
 
+// blocks of a launch: one per run of units (per-head split: head_blocks per
+// head), rounded up to a multiple of 8 when blocks are numbered XCD by XCD
+// (blocks past the last run find no work)
+static unsigned attend_grid(const AttnArgs &a) {
+  const int64_t total = int64_t(a.n_ktiles) * a.n_qblocks * a.L.H;
+  const unsigned g = a.head_blocks ? unsigned(a.head_blocks * a.L.H) : cdiv(total, a.units_per_block);
+  return a.xcd_remap ? (g + 7) / 8 * 8 : g;
+}
+
 template <int D, int G, int BITS, bool BF, int S, bool OUTL>
 static void launch_attend_s(const AttnArgs &a, const dim3 &grid, hipStream_t st) {
   QKV_LAUNCH((k_attend3<D, G, BITS, BF, S, false, OUTL>), grid, dim3(512), 0, st, a);
@@ -617,8 +672,7 @@ static void launch_attend_s(const AttnArgs &a, const dim3 &grid, hipStream_t st)
 
 template <int D, int G, int BITS, bool BF>
 static void launch_attend_t(const AttnArgs &a, hipStream_t st) {
-  const int64_t total = int64_t(a.n_ktiles) * a.n_qblocks * a.L.H;
-  const dim3 grid(unsigned(cdiv(total, a.units_per_block)));
+  const dim3 grid(attend_grid(a));
   if (a.L.mask_off) {
     switch (a.L.S) {
       case 1: launch_attend_s<D, G, BITS, BF, 1, true>(a, grid, st); break;
@@ -637,8 +691,7 @@ static void launch_attend_t(const AttnArgs &a, hipStream_t st) {
 }
 
 void launch_attend_fresh(const AttnArgs &a, hipStream_t st) {
-  const int64_t total = int64_t(a.n_ktiles) * a.n_qblocks * a.L.H;
-  const dim3 grid(unsigned(cdiv(total, a.units_per_block)));
+  const dim3 grid(attend_grid(a));
   if (a.L.D == 64)
     QKV_LAUNCH((k_attend3<64, 32, 2, true, 1, true>), grid, dim3(512), 0, st, a);
   else

@@ -83,6 +83,11 @@ struct AttnArgs {
   int32_t n_qblocks;                    // query blocks of 256
   int32_t n_ktiles;                     // key tiles of 64 (at least 1)
   int32_t units_per_block;              // consecutive units per block
+  // per-head split (0: plain stream-K): head_blocks blocks per head; the
+  // first n_qblocks each take key tiles [0, main_tiles) of one query block,
+  // the others the remaining tiles of all its query blocks in runs of
+  // units_per_block
+  int32_t head_blocks, main_tiles;
   int32_t max_segments;                 // most blocks sharing one query block
   int32_t xcd_remap;                    // number blocks XCD by XCD (grid % 8 == 0)
   void *out;                            // final [H][n_q][D]

@@ -229,6 +229,26 @@ AttnSplit attention_split(const Plan &p, int64_t n_keys, int64_t n_q, int n_cu, 
   // one run per compute unit, but no query block shared by more than
   // max_splits blocks (partial slots of the scratch region)
   const int64_t ms = std::max(2, std::min(max_splits, kMaxSplits));
+  // Per-head split when every query block of a head can have a block of its
+  // own: head h gets B = n_cu / H blocks; its n_qblocks query blocks sweep
+  // key tiles [0, M) side by side (they read the same tiles at about the same
+  // time, and consecutive blocks share an XCD's L2), and the other B -
+  // n_qblocks blocks take the tails [M, T) of all its query blocks.
+  const int64_t H = p.cfg.n_heads, B = cus / H;
+  if (H <= cus && B >= w.n_qblocks) {
+    const int64_t U = (w.n_qblocks * w.n_ktiles + B - 1) / B;
+    const int64_t M = std::min(U, w.n_ktiles), tail = w.n_ktiles - M;
+    // a tail of `tail` units meets at most ceil(tail / U) + 1 runs
+    const int64_t segs = M == w.n_ktiles ? 1 : 2 + (tail + U - 1) / U;
+    if (segs <= ms) {
+      w.head_blocks = B;
+      w.main_tiles = M;
+      w.units_per_block = U;
+      w.n_blocks = (H * B + 7) / 8 * 8;
+      w.max_segments = segs;
+      return w;
+    }
+  }
   w.units_per_block = std::max((total + cus - 1) / cus, (w.n_ktiles + ms - 2) / (ms - 1));
   w.n_blocks = (total + w.units_per_block - 1) / w.units_per_block;
   // blocks meeting one query block: at most ceil((T - 1) / U) + 1

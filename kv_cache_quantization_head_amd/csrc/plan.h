@@ -125,6 +125,7 @@ int check_attend_with_chunk(const qkv_ctx *ctx, int32_t layer, const void *q, in
 // consecutive units, one run per block, about one block per compute unit.
 struct AttnSplit {
   int64_t n_qblocks, n_ktiles, units_per_block, n_blocks, max_segments;
+  int64_t head_blocks, main_tiles;      // per-head split (head_blocks = 0: plain stream-K)
 };
 // max_splits bounds the blocks sharing one query block (partial slots used).
 AttnSplit attention_split(const Plan &p, int64_t n_keys, int64_t n_q, int n_cu, int max_splits = kMaxSplits);
