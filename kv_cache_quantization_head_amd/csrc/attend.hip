@@ -74,6 +74,16 @@ __device__ __forceinline__ uint32_t pick_word(const uint32_t *w, int i) {
   else return (i & 2) ? ((i & 1) ? w[3] : w[2]) : ((i & 1) ? w[1] : w[0]);
 }
 
+// Item registers of the outlier option: the item's mask word in its key's
+// chunk and, where it flags a channel, the outlier group's (sigma, z) of every
+// stage.
+template <int SMAX>
+struct OutlierRegs {
+  uint32_t fm;
+  uint32_t mo[SMAX];
+};
+struct NoOutlierRegs {};
+
 template <int D, int G, int BITS, bool CB_BF16, int SMAX, bool FRESH = false, bool OUTL = false>
 __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   // SMAX = the number of PRQ stages (a template parameter so that the staging
@@ -262,7 +272,7 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     auto id_of = [&](int tile, uint32_t w) -> int {
       return int((w >> (8 * uint32_t(id_off(tile) & 3))) & (L.id_bytes == 1 ? 0xffu : 0xffffu));
     };
-    struct Regs {
+    struct Regs : std::conditional_t<OUTL, OutlierRegs<SMAX>, NoOutlierRegs> {
       uint32_t codes[SMAX][KW];
       uint32_t meta[SMAX];
       uint4 cent[KC];
@@ -277,7 +287,6 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     // fresh rows: channels it_ch .. it_ch+31 of key t_first of head h
     const uint16_t *fresh_p = FRESH ? (it_kv ? a.v_new : a.k_new) + (uint64_t(h) * a.n_keys + t_first) * D + it_ch
                                     : nullptr;
-    const uint64_t tile_meta = uint64_t(AT_BK) * L.meta_token;
     // chunk (snapshot slot) of the item's key, advanced tile by tile: keys
     // only grow, and a tile's keys rarely cross more than one chunk start
     int c_cur = (FRESH || nch_s == 1) ? 0 : chunk_of_lds(starts_s, nch_s, t_first);
@@ -299,6 +308,7 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
         return;
       }
       while (c_cur + 1 < nch_s && starts_s[c_cur + 1] <= t) ++c_cur;
+      if constexpr (OUTL) R.fm = masks_s[it_kv][c_cur * (D / 32) + (it_ch >> 5)];
       const uint8_t *crow = cb_p + uint64_t(c_cur) * L.cb_chunk + uint64_t(id_of(tile, id_word)) * (D * EB);
   #pragma unroll
       for (int i = 0; i < KC; ++i) R.cent[i] = *(const uint4 *)(crow + 16 * i);
@@ -317,6 +327,13 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
           }
         }
         R.meta[s2] = *(const uint32_t *)(mp + uint64_t(s2) * L.meta_stage);
+      }
+      if constexpr (OUTL) {
+        if (R.fm) {
+  #pragma unroll
+          for (int s2 = 0; s2 < SMAX; ++s2)
+            R.mo[s2] = *(const uint32_t *)(mp + uint64_t(s2) * L.meta_stage + 4 * (D / G - it_g));
+        }
       }
     };
     // one PRQ stage folded into 16 channels: xh[c] = fmaf(q_c, sigma, xh[c]) (the
@@ -391,29 +408,19 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
         *(uint4 *)(dst + j) = make_uint4(pack_bf16x2(xh[j], xh[j + 1]), pack_bf16x2(xh[j + 2], xh[j + 3]),
                                          pack_bf16x2(xh[j + 4], xh[j + 5]), pack_bf16x2(xh[j + 6], xh[j + 7]));
       if constexpr (OUTL) {
-        // channels of the item flagged in the mask of the key's chunk (mask
-        // words in LDS): rebuilt again with the outlier group's (sigma, z) and
-        // the item's registers, stored over the first result; read only
-        // here, so that nothing of it is held during the rebuild
-        uint32_t fm = 0u;
-        uint32_t mo[SMAX];
-        const int t = ks + tile * AT_BK + it_key;
-        if (t < ke) {
-          const int cslot = nch_s > 1 ? chunk_of_lds(starts_s, nch_s, t) : 0;
-          fm = masks_s[it_kv][cslot * (D / 32) + (it_ch >> 5)];
-          if (fm) {
-            const uint8_t *mop = meta_p + uint64_t(tile) * tile_meta + 4 * (D / G - it_g);
-  #pragma unroll
-            for (int s2 = 0; s2 < SMAX; ++s2) mo[s2] = *(const uint32_t *)(mop + uint64_t(s2) * L.meta_stage);
-          }
-        }
+        // channels of the item flagged in the mask of the key's chunk (the
+        // mask word and the outlier group's (sigma, z), loaded with the rest
+        // of the item's data): rebuilt again with those and stored over the
+        // first result.  A key past the segment's end carries the last key's
+        // data, like the plain rebuild.
+        uint32_t fm = R.fm;
         if (fm) {
           float so[SMAX];
           float zso = 0.0f;
   #pragma unroll
           for (int s2 = 0; s2 < SMAX; ++s2) {
-            so[s2] = f16_bits_to_f32(uint16_t(mo[s2] & 0xffffu));
-            zso += f16_bits_to_f32(uint16_t(mo[s2] >> 16));
+            so[s2] = f16_bits_to_f32(uint16_t(R.mo[s2] & 0xffffu));
+            zso += f16_bits_to_f32(uint16_t(R.mo[s2] >> 16));
           }
           while (fm) {
             const int e = __builtin_ctz(fm);
