@@ -406,7 +406,9 @@ extern "C" int qkv_attend(qkv_ctx *ctx, int32_t layer, const void *d_q, int64_t 
   TraceScope trace(ctx);
   const Plan &p = ctx->plan;
   ensure_cu_count(ctx);
-  const AttnSplit w = attention_split(p, ctx->layers[layer].n_tokens, n_q, ctx->n_cu);
+  // a cross-layer coded layer is read as uncoded bf16 rows
+  const uint64_t kb = p.cfg.xlayer && layer >= 1 ? bf16_key_bytes(p) : packed_key_bytes(p);
+  const AttnSplit w = attention_split(p, ctx->layers[layer].n_tokens, n_q, ctx->n_cu, kb);
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   if (p.cfg.xlayer && (layer >= 1 || p.cfg.n_layers > 1)) sweep_to(ctx, layer, st);
@@ -425,7 +427,7 @@ extern "C" int qkv_attend_noalloc(qkv_ctx *ctx, int32_t layer, const void *d_q, 
   if (!ctx->noalloc_scratch || ctx->plan.cfg.xlayer) return QKV_E_UNSUPPORTED;
   const Plan &p = ctx->plan;
   ensure_cu_count(ctx);
-  const AttnSplit w = attention_split(p, ctx->layers[layer].n_tokens, n_q, ctx->n_cu);
+  const AttnSplit w = attention_split(p, ctx->layers[layer].n_tokens, n_q, ctx->n_cu, packed_key_bytes(p));
   // partials of the slots this call can use, in the fixed array
   const uint64_t rows = uint64_t(w.max_segments) * p.cfg.n_heads * uint64_t(n_q);
   const uint64_t lse_off = align_up(rows * p.cfg.head_dim * 4);
@@ -457,8 +459,8 @@ extern "C" int qkv_attend_with_chunk(qkv_ctx *ctx, int32_t layer, const void *d_
   float *part_lse = reinterpret_cast<float *>(scratch(ctx, p.attn_part_lse_off));
   float *o_part[2] = {part_o + (kMaxSplits - 2) * HQ * c.head_dim, part_o + (kMaxSplits - 1) * HQ * c.head_dim};
   float *l_part[2] = {part_lse + (kMaxSplits - 2) * HQ, part_lse + (kMaxSplits - 1) * HQ};
-  auto args_for = [&](int64_t n_keys) {
-    const AttnSplit w = attention_split(p, n_keys, n_q, ctx->n_cu, kMaxSplits - 2);
+  auto args_for = [&](int64_t n_keys, uint64_t key_bytes) {
+    const AttnSplit w = attention_split(p, n_keys, n_q, ctx->n_cu, key_bytes, kMaxSplits - 2);
     AttnArgs a{};
     a.L = dev_layout(p);
     a.q = d_q;
@@ -478,7 +480,7 @@ extern "C" int qkv_attend_with_chunk(qkv_ctx *ctx, int32_t layer, const void *d_
   };
   (void)hipGetLastError();
   // fresh part: straight into the output when the cache holds nothing
-  AttnArgs f = args_for(n_new);
+  AttnArgs f = args_for(n_new, bf16_key_bytes(p));
   f.k_new = static_cast<const uint16_t *>(d_k_new);
   f.v_new = static_cast<const uint16_t *>(d_v_new);
   if (n_cache == 0) {
@@ -490,7 +492,7 @@ extern "C" int qkv_attend_with_chunk(qkv_ctx *ctx, int32_t layer, const void *d_
     return hip_status(ctx);
   }
   if (c.xlayer && (layer >= 1 || c.n_layers > 1)) sweep_to(ctx, layer, st);
-  AttnArgs a = args_for(n_cache);
+  AttnArgs a = args_for(n_cache, c.xlayer && layer >= 1 ? bf16_key_bytes(p) : packed_key_bytes(p));
   a.out = o_part[0];
   a.out_bf16 = 0;
   a.lse = l_part[0];

@@ -220,7 +220,14 @@ int check_rewind(const qkv_ctx *ctx, int32_t layer0, int32_t n_layers, int64_t n
   return QKV_OK;
 }
 
-AttnSplit attention_split(const Plan &p, int64_t n_keys, int64_t n_q, int n_cu, int max_splits) {
+uint64_t packed_key_bytes(const Plan &p) {
+  const uint64_t S = p.cfg.n_stages;
+  return 2 * uint64_t(p.cfg.n_heads) * (S * p.s.codes_token + S * p.s.meta_token + p.s.id_bytes);
+}
+uint64_t bf16_key_bytes(const Plan &p) { return 2 * uint64_t(p.cfg.n_heads) * p.cfg.head_dim * 2; }
+
+AttnSplit attention_split(const Plan &p, int64_t n_keys, int64_t n_q, int n_cu, uint64_t key_bytes,
+                          int max_splits) {
   AttnSplit w{};
   w.n_qblocks = (n_q + 255) / 256;
   w.n_ktiles = std::max<int64_t>(1, (n_keys + 63) / 64);
@@ -229,13 +236,14 @@ AttnSplit attention_split(const Plan &p, int64_t n_keys, int64_t n_q, int n_cu, 
   // one run per compute unit, but no query block shared by more than
   // max_splits blocks (partial slots of the scratch region)
   const int64_t ms = std::max(2, std::min(max_splits, kMaxSplits));
-  // Per-head split when every query block of a head can have a block of its
-  // own: head h gets B = n_cu / H blocks; its n_qblocks query blocks sweep
-  // key tiles [0, M) side by side (they read the same tiles at about the same
-  // time, and consecutive blocks share an XCD's L2), and the other B -
-  // n_qblocks blocks take the tails [M, T) of all its query blocks.
+  // Per-head split when the keys do not stay in the MALL and every query
+  // block of a head can have a block of its own: head h gets B = n_cu / H
+  // blocks; its n_qblocks query blocks sweep key tiles [0, M) side by side
+  // (they read the same tiles at about the same time, and consecutive blocks
+  // share an XCD's L2), and the other B - n_qblocks blocks take the tails
+  // [M, T) of all its query blocks.
   const int64_t H = p.cfg.n_heads, B = cus / H;
-  if (H <= cus && B >= w.n_qblocks) {
+  if (uint64_t(n_keys) * key_bytes > kHeadSplitMinBytes && H <= cus && B >= w.n_qblocks) {
     const int64_t U = (w.n_qblocks * w.n_ktiles + B - 1) / B;
     const int64_t M = std::min(U, w.n_ktiles), tail = w.n_ktiles - M;
     // a tail of `tail` units meets at most ceil(tail / U) + 1 runs

@@ -127,8 +127,16 @@ struct AttnSplit {
   int64_t n_qblocks, n_ktiles, units_per_block, n_blocks, max_segments;
   int64_t head_blocks, main_tiles;      // per-head split (head_blocks = 0: plain stream-K)
 };
-// max_splits bounds the blocks sharing one query block (partial slots used).
-AttnSplit attention_split(const Plan &p, int64_t n_keys, int64_t n_q, int n_cu, int max_splits = kMaxSplits);
+// key_bytes: bytes one key costs the read over all heads, K and V (packed:
+// packed_key_bytes; uncoded bf16 rows: bf16_key_bytes).  max_splits bounds the
+// blocks sharing one query block (partial slots used).
+AttnSplit attention_split(const Plan &p, int64_t n_keys, int64_t n_q, int n_cu, uint64_t key_bytes,
+                          int max_splits = kMaxSplits);
+uint64_t packed_key_bytes(const Plan &p);
+uint64_t bf16_key_bytes(const Plan &p);
+// The per-head split pays when the keys read by one call do not stay in the
+// device's last-level (MALL, 256 MiB) cache.
+constexpr uint64_t kHeadSplitMinBytes = uint64_t(256) << 20;
 
 // Byte offset of stream (layer, kv) from the arena base.
 inline uint64_t stream_offset(const Plan &p, int layer, int kv) {
