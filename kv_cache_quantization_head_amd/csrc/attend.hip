@@ -67,11 +67,20 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 constexpr float AT3_TAU = 8.0f;
 
-// w[i] for a run-time i < N (selects, no indexed register access)
+// b where bit k of i is set, else a: a bitwise select of two values.  A
+// conditional expression over two register words lets the compiler merge
+// them into one load at a run-time offset, which forces the words into
+// memory.
+template <int K>
+__device__ __forceinline__ uint32_t bit_sel(int i, uint32_t a, uint32_t b) {
+  const uint32_t m = 0u - ((uint32_t(i) >> K) & 1u);
+  return (b & m) | (a & ~m);
+}
+// w[i] for a run-time i < N (bitwise selects, no indexed register access)
 template <int N>
 __device__ __forceinline__ uint32_t pick_word(const uint32_t *w, int i) {
-  if constexpr (N == 2) return i ? w[1] : w[0];
-  else return (i & 2) ? ((i & 1) ? w[3] : w[2]) : ((i & 1) ? w[1] : w[0]);
+  if constexpr (N == 2) return bit_sel<0>(i, w[0], w[1]);
+  else return bit_sel<1>(i, bit_sel<0>(i, w[0], w[1]), bit_sel<0>(i, w[2], w[3]));
 }
 
 // Item registers of the outlier option: the item's mask word in its key's
@@ -361,20 +370,26 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
         return __uint_as_float(w);
       }
     };
-    // centroid channel e of the item for a run-time e (a select tree over the
-    // item's registers)
+    // centroid channel e of the item for a run-time e: a select tree over the
+    // item's register values (selecting whole uint4 values would select their
+    // addresses, which keeps the item's registers in memory)
     auto cent_pick = [&](int e) -> float {
+      auto comp = [](const uint4 &v, int i) -> uint32_t {
+        return bit_sel<1>(i, bit_sel<0>(i, v.x, v.y), bit_sel<0>(i, v.z, v.w));
+      };
       if constexpr (CB_BF16) {
-        const int wi = e >> 1;
-        const uint4 a = (wi & 8) ? ((wi & 4) ? R.cent[3] : R.cent[2]) : ((wi & 4) ? R.cent[1] : R.cent[0]);
-        const uint32_t w = (wi & 2) ? ((wi & 1) ? a.w : a.z) : ((wi & 1) ? a.y : a.x);
+        const int wi = e >> 1;   // word of the item: component wi % 4 of R.cent[wi / 4]
+        const uint32_t w0 = comp(R.cent[0], wi), w1 = comp(R.cent[1], wi);
+        const uint32_t w2 = comp(R.cent[2], wi), w3 = comp(R.cent[3], wi);
+        const uint32_t w = bit_sel<3>(wi, bit_sel<2>(wi, w0, w1), bit_sel<2>(wi, w2, w3));
         return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
       } else {
-        const int vi = e >> 2;
-        const uint4 a0 = (vi & 2) ? ((vi & 1) ? R.cent[3] : R.cent[2]) : ((vi & 1) ? R.cent[1] : R.cent[0]);
-        const uint4 a1 = (vi & 2) ? ((vi & 1) ? R.cent[7] : R.cent[6]) : ((vi & 1) ? R.cent[5] : R.cent[4]);
-        const uint4 a = (vi & 4) ? a1 : a0;
-        return __uint_as_float((e & 2) ? ((e & 1) ? a.w : a.z) : ((e & 1) ? a.y : a.x));
+        uint32_t w[8];
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = comp(R.cent[i], e);
+        const uint32_t lo = bit_sel<3>(e, bit_sel<2>(e, w[0], w[1]), bit_sel<2>(e, w[2], w[3]));
+        const uint32_t hi = bit_sel<3>(e, bit_sel<2>(e, w[4], w[5]), bit_sel<2>(e, w[6], w[7]));
+        return __uint_as_float(bit_sel<4>(e, lo, hi));
       }
     };
     // Rebuild the item for the products: xh = fmaf(q_S, sigma_S, ... fmaf(q_1,
@@ -386,8 +401,12 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
       if (!has_item) return;
       if constexpr (FRESH) {
         uint16_t *dst = it_kv ? &Vs[buf][it_key * VP + it_ch] : &Ks[buf][it_key * KP + it_ch];
-  #pragma unroll
-        for (int i = 0; i < KC; ++i) *(uint4 *)(dst + 8 * i) = R.cent[i];
+        static_assert(KC == 4, "a fresh item is 32 bf16 channels");
+        const uint4 c0 = R.cent[0], c1 = R.cent[1], c2 = R.cent[2], c3 = R.cent[3];
+        *(uint4 *)(dst) = c0;
+        *(uint4 *)(dst + 8) = c1;
+        *(uint4 *)(dst + 16) = c2;
+        *(uint4 *)(dst + 24) = c3;
         return;
       }
       float xh[IC];
