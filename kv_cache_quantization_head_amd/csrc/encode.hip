@@ -1014,7 +1014,11 @@ __global__ __launch_bounds__(256) void k_quantize(EncodeArgs a) {
       const float zfo = f16_bits_to_f32(zbo);
       const uint16_t sbo = ho ? f32_to_f16_bits((omx - zfo) / LEVELS) : uint16_t(0);
       const float sfo = f16_bits_to_f32(sbo);
-      const float inv = 1.0f / sf, invo = 1.0f / sfo;
+      // reciprocals of the two sigmas (0 for a degenerate group, which makes
+      // every code 0 with r^ = z); opaque, so that the per-channel select
+      // below is not turned into a division per channel
+      float inv = sf != 0.0f ? 1.0f / sf : 0.0f, invo = sfo != 0.0f ? 1.0f / sfo : 0.0f;
+      asm volatile("" : "+v"(inv), "+v"(invo));
       constexpr int PER_BYTE = 8 / BITS;
       uint32_t w[WORDS];
 #pragma unroll
@@ -1027,9 +1031,7 @@ __global__ __launch_bounds__(256) void k_quantize(EncodeArgs a) {
           const int j = j0 + e;
           const bool f = (fm[j >> 5] >> (j & 31)) & 1u;
           const float zj = f ? zfo : zf, sj = f ? sfo : sf, ij = f ? invo : inv;
-          // sigma 0 (degenerate group): code 0, r^ = z
-          const float qq = fminf(fmaxf(rintf((r[j] - zj) * ij), 0.0f), LEVELS);
-          q[e] = sj != 0.0f ? qq : 0.0f;
+          q[e] = fminf(fmaxf(rintf((r[j] - zj) * ij), 0.0f), LEVELS);
           const float rh = fmaf(q[e], sj, zj);
           r[j] = r[j] - rh;
           if constexpr (CHAIN) xh[j] = xh[j] + rh;
