@@ -118,6 +118,8 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   __shared__ int32_t nch_s;
   // OUTL: the segment head's mask words of every chunk, per tensor
   __shared__ uint32_t masks_s[2][OUTL ? kMaxChunks * (D / 32) : 1];
+  // OUTL: a thread's centroid slice, [uint4 i][thread], read back per flagged channel
+  __shared__ uint4 cent_s[OUTL ? KC * 512 : 1];
 
   const DevLayout &L = a.L;
   const int tid = threadIdx.x;
@@ -370,28 +372,6 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
         return __uint_as_float(w);
       }
     };
-    // centroid channel e of the item for a run-time e: a select tree over the
-    // item's register values (selecting whole uint4 values would select their
-    // addresses, which keeps the item's registers in memory)
-    auto cent_pick = [&](int e) -> float {
-      auto comp = [](const uint4 &v, int i) -> uint32_t {
-        return bit_sel<1>(i, bit_sel<0>(i, v.x, v.y), bit_sel<0>(i, v.z, v.w));
-      };
-      if constexpr (CB_BF16) {
-        const int wi = e >> 1;   // word of the item: component wi % 4 of R.cent[wi / 4]
-        const uint32_t w0 = comp(R.cent[0], wi), w1 = comp(R.cent[1], wi);
-        const uint32_t w2 = comp(R.cent[2], wi), w3 = comp(R.cent[3], wi);
-        const uint32_t w = bit_sel<3>(wi, bit_sel<2>(wi, w0, w1), bit_sel<2>(wi, w2, w3));
-        return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
-      } else {
-        uint32_t w[8];
-  #pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = comp(R.cent[i], e);
-        const uint32_t lo = bit_sel<3>(e, bit_sel<2>(e, w[0], w[1]), bit_sel<2>(e, w[2], w[3]));
-        const uint32_t hi = bit_sel<3>(e, bit_sel<2>(e, w[4], w[5]), bit_sel<2>(e, w[6], w[7]));
-        return __uint_as_float(bit_sel<4>(e, lo, hi));
-      }
-    };
     // Rebuild the item for the products: xh = fmaf(q_S, sigma_S, ... fmaf(q_1,
     // sigma_1, c + (z_1 + ... + z_S))), then nearest-even bf16.  This differs
     // from the stage-by-stage reconstruction (c + rhat_1) + rhat_2 ... by a few
@@ -430,10 +410,13 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
         // channels of the item flagged in the mask of the key's chunk (the
         // mask word and the outlier group's (sigma, z), loaded with the rest
         // of the item's data): rebuilt again with those and stored over the
-        // first result.  A key past the segment's end carries the last key's
-        // data, like the plain rebuild.
+        // first result (the channel's centroid value read back from the
+        // thread's copy of its slice in LDS).  A key past the segment's end
+        // carries the last key's data, like the plain rebuild.
         uint32_t fm = R.fm;
         if (fm) {
+  #pragma unroll
+          for (int i = 0; i < KC; ++i) cent_s[i * 512 + tid] = R.cent[i];
           float so[SMAX];
           float zso = 0.0f;
   #pragma unroll
@@ -444,7 +427,9 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
           while (fm) {
             const int e = __builtin_ctz(fm);
             fm &= fm - 1u;
-            float v = cent_pick(e) + zso;
+            constexpr int EPV = 16 / EB;   // centroid elements per uint4
+            const uint8_t *cw = (const uint8_t *)&cent_s[(e / EPV) * 512 + tid] + (e % EPV) * EB;
+            float v = (CB_BF16 ? bf16_to_f32(*(const uint16_t *)cw) : *(const float *)cw) + zso;
   #pragma unroll
             for (int s2 = 0; s2 < SMAX; ++s2) {
               const uint32_t w = pick_word<KW>(R.codes[s2], (e * BITS) >> 5);
