@@ -99,84 +99,121 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 }
 
 // pred[h][t][i] = sum_j B_h[i][j] y[t][j] (order j), then + sum_k U[h*D+i][k]
-// w[t][k] (order k), fp64, rounded once to fp32.  Block = 256 threads =
-// (token groups of XL_PT) x (output groups of 8) over token tiles of
-// XL_PT*256/(D/8) tokens: a thread's 8 x 8 fp64 accumulators take 64 fmas per
-// 16 operands converted from bf16.  B_h and U_h are staged once per block
-// (transposed, as bf16: two blocks fit a CU) and the block walks every
-// gridDim.x-th token tile.
-constexpr int XL_PT = 8;                     // tokens per thread
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_xl_predict(XlArgs a, int kv0) {
+// w[t][k] (order k), fp64, rounded once to fp32, on the fp64 matrix
+// instruction v_mfma_f64_16x16x4_f64.  That instruction adds its four
+// products to the accumulator one after another in k order, each sum
+// rounded to fp64 (checked on the device against a sequential fp64
+// reference: identical bits for 1M outputs whose operands span +-2^44, where
+// the reverse, pairwise and single-rounding orders each differ in about 3.5 %
+// of them), so a chain of them over ascending k is the same sequence of fp64
+// additions as the definition.  Operand layouts of the 16x16x4 shape: A[m][k]
+// in lane m + 16 k, B[k][n] in lane n + 16 k, D[m][n] in lane n + 16 (m % 4),
+// register m / 4.  Here m = token, n = output channel, k = input channel j
+// (then rank k).  Block = 4 waves over a tile of 64 tokens, wave w taking
+// tokens 16 w .. 16 w + 15 and all D outputs (D/16 accumulator tiles).  B_h
+// and U_h are staged once per block and the block walks every gridDim.x-th
+// token tile.  In LDS every operand row keeps its k index permuted inside
+// each run of 16 (k = 16 q + 4 s + g stored at 16 q + 4 g + s), so that the
+// lane of k-group g reads the values of four consecutive k-steps s in one
+// 8-byte load.
+constexpr int XP_TT = 64;                    // tokens per tile
+__device__ __forceinline__ int xp_perm(int k) { return (k & ~15) | ((k & 3) << 2) | ((k >> 2) & 3); }
+__device__ __forceinline__ double xp_bf16(uint2 v, int s) {
+  const uint32_t w = (s & 2) ? v.y : v.x;
+  return double(__uint_as_float((s & 1) ? (w & 0xffff0000u) : (w << 16)));
+}
+typedef double xp_double4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_xl_predict(XlArgs a, int kv0) {
+  constexpr int NI = D / 16, BP = D + 4;     // accumulator tiles; B / y row stride (bf16)
   extern __shared__ uint16_t xs16[];
-  const int D = a.D, RP = (a.r + 7) & ~7;
-  const int IG = D / 8, TG = 256 / IG, TT = XL_PT * TG;
-  uint16_t *bsT = xs16;                       // [D j][D i] bf16
-  uint16_t *usT = bsT + D * D;                // [RP k][D i]
-  uint16_t *ysT = usT + RP * D;               // [D j][TT]
-  uint16_t *wsT = ysT + D * TT;               // [RP k][TT]
-  const int tid = threadIdx.x, h = blockIdx.y, kv = kv0 + blockIdx.z;
-  const int ig = tid % IG, tg = tid / IG;
+  const int RP = (a.r + 15) & ~15, UP = RP + 4;
+  uint16_t *Bs = xs16;                       // [D i][BP]: B_h[i][j] at xp_perm(j)
+  uint16_t *Us = Bs + D * BP;                // [D i][UP]: U[h*D+i][k] at xp_perm(k), 0 past r
+  uint16_t *Ys = Us + D * UP;                // [XP_TT t][BP]: y[t][j] at xp_perm(j)
+  uint16_t *Ws = Ys + XP_TT * BP;            // [XP_TT t][UP]: w[t][k] at xp_perm(k), 0 past r
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m = lane & 15, g = lane >> 4;
+  const int h = blockIdx.y, kv = kv0 + blockIdx.z;
   const uint64_t HD = uint64_t(a.H) * D;
   const uint16_t *W = a.weights + uint64_t(kv) * a.kv_weight_stride;
   const uint16_t *B = a.b_weights ? a.b_weights + (uint64_t(kv) * a.H + h) * D * D : W + uint64_t(h) * D * D;
   const uint16_t *U = W + HD * D + uint64_t(h) * D * a.r;
   const uint16_t *y = a.chain + uint64_t(kv) * HD * a.n + uint64_t(h) * a.n * D;
   const float *w = a.proj + uint64_t(kv) * a.n * a.r;
-  for (int e = tid; e < D * D; e += 256) {
-    const int i = e / D, j = e % D;
-    bsT[j * D + i] = B[e];
-  }
+  float *pred = a.pred + uint64_t(kv) * HD * a.n + uint64_t(h) * a.n * D;
+  for (int e = tid; e < D * D; e += 256) Bs[(e / D) * BP + xp_perm(e % D)] = B[e];
   for (int e = tid; e < D * RP; e += 256) {
-    const int i = e / RP, kk = e % RP;
-    usT[kk * D + i] = kk < a.r ? U[uint64_t(i) * a.r + kk] : uint16_t(0);
+    const int i = e / RP, k = e % RP;
+    Us[i * UP + xp_perm(k)] = k < a.r ? U[uint64_t(i) * a.r + k] : uint16_t(0);
   }
-  const int n_tiles = (a.n + TT - 1) / TT;
-  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    const int t0 = tile * TT;
-    __syncthreads();                          // weights staged / previous tile consumed
-    for (int e = tid; e < TT * D; e += 256) {
-      const int tt = e / D, j = e % D, t = min(t0 + tt, a.n - 1);
-      ysT[j * TT + tt] = y[uint64_t(t) * D + j];
+  // the next tile's y rows and w values are loaded into registers while the
+  // current tile is multiplied (16-byte pieces of y; w as bf16 bits)
+  constexpr int YPT = XP_TT * D / 8 / 256;   // y pieces per thread
+  constexpr int WPT = XP_TT * 64 / 256;      // w values per thread (r <= 64)
+  uint4 ypre[YPT];
+  uint16_t wpre[WPT];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < YPT; ++i) {
+      const int e8 = tid + 256 * i, tt = e8 / (D / 8), j8 = 8 * (e8 % (D / 8)), t = min(t0 + tt, a.n - 1);
+      ypre[i] = *(const uint4 *)(y + uint64_t(t) * D + j8);
     }
-    for (int e = tid; e < TT * RP; e += 256) {
-      const int tt = e / RP, kk = e % RP, t = min(t0 + tt, a.n - 1);
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int e = tid + 256 * i, tt = e / RP, k = e % RP, t = min(t0 + tt, a.n - 1);
       // w holds bf16 values (rounded in the projection): exact in bf16
-      wsT[kk * TT + tt] = kk < a.r ? f32_to_bf16_bits(w[uint64_t(t) * a.r + kk]) : uint16_t(0);
+      wpre[i] = e < XP_TT * RP && k < a.r ? f32_to_bf16_bits(w[uint64_t(t) * a.r + k]) : uint16_t(0);
+    }
+  };
+  const int n_tiles = (a.n + XP_TT - 1) / XP_TT;
+  if (blockIdx.x < n_tiles) fetch(blockIdx.x * XP_TT);
+  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const int t0 = tile * XP_TT;
+    __syncthreads();                         // weights staged / previous tile consumed
+#pragma unroll
+    for (int i = 0; i < YPT; ++i) {
+      const int e8 = tid + 256 * i, tt = e8 / (D / 8), j8 = 8 * (e8 % (D / 8));
+      const uint32_t v4[4] = {ypre[i].x, ypre[i].y, ypre[i].z, ypre[i].w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) Ys[tt * BP + xp_perm(j8 + q)] = uint16_t(v4[q >> 1] >> (16 * (q & 1)));
+    }
+#pragma unroll
+    for (int i = 0; i < WPT; ++i) {
+      const int e = tid + 256 * i, tt = e / RP, k = e % RP;
+      if (e < XP_TT * RP) Ws[tt * UP + xp_perm(k)] = wpre[i];
     }
     __syncthreads();
-    double acc[XL_PT][8];
+    if (tile + int(gridDim.x) < n_tiles) fetch((tile + gridDim.x) * XP_TT);
+    xp_double4 acc[NI];
 #pragma unroll
-    for (int u = 0; u < XL_PT; ++u)
+    for (int it = 0; it < NI; ++it) acc[it] = xp_double4{0.0, 0.0, 0.0, 0.0};
+    // 16 k values (four k-steps) per round: A from the token rows, B from the
+    // weight rows of every accumulator tile
+    auto rounds = [&](const uint16_t *arow, const uint16_t *brows, int stride, int nq) {
+      for (int q = 0; q < nq; ++q) {
+        const uint2 av = *(const uint2 *)(arow + 16 * q);
+        uint2 bv[NI];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[u][c] = 0.0;
-    auto step = [&](const uint16_t *ycol, const uint16_t *bcol) {
-      const uint4 yv = *(const uint4 *)(ycol + XL_PT * tg);
-      const uint4 bv = *(const uint4 *)(bcol + 8 * ig);
-      const double yd[XL_PT] = {double(__uint_as_float(yv.x << 16)), double(__uint_as_float(yv.x & 0xffff0000u)),
-                                double(__uint_as_float(yv.y << 16)), double(__uint_as_float(yv.y & 0xffff0000u)),
-                                double(__uint_as_float(yv.z << 16)), double(__uint_as_float(yv.z & 0xffff0000u)),
-                                double(__uint_as_float(yv.w << 16)), double(__uint_as_float(yv.w & 0xffff0000u))};
-      const double bd[8] = {double(__uint_as_float(bv.x << 16)), double(__uint_as_float(bv.x & 0xffff0000u)),
-                            double(__uint_as_float(bv.y << 16)), double(__uint_as_float(bv.y & 0xffff0000u)),
-                            double(__uint_as_float(bv.z << 16)), double(__uint_as_float(bv.z & 0xffff0000u)),
-                            double(__uint_as_float(bv.w << 16)), double(__uint_as_float(bv.w & 0xffff0000u))};
+        for (int it = 0; it < NI; ++it) bv[it] = *(const uint2 *)(brows + (16 * it) * stride + 16 * q);
 #pragma unroll
-      for (int u = 0; u < XL_PT; ++u)
+        for (int s = 0; s < 4; ++s) {
+          const double ad = xp_bf16(av, s);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[u][c] = fma(bd[c], yd[u], acc[u][c]);
+          for (int it = 0; it < NI; ++it)
+            acc[it] = __builtin_amdgcn_mfma_f64_16x16x4f64(ad, xp_bf16(bv[it], s), acc[it], 0, 0, 0);
+        }
+      }
     };
-    if (!a.lowrank_only) {
-#pragma unroll 4
-      for (int j = 0; j < D; ++j) step(ysT + j * TT, bsT + j * D);
-    }
-    for (int kk = 0; kk < a.r; ++kk) step(wsT + kk * TT, usT + kk * D);
+    if (!a.lowrank_only) rounds(Ys + (16 * wave + m) * BP + 4 * g, Bs + m * BP + 4 * g, BP, D / 16);
+    rounds(Ws + (16 * wave + m) * UP + 4 * g, Us + m * UP + 4 * g, UP, RP / 16);
 #pragma unroll
-    for (int u = 0; u < XL_PT; ++u) {
-      const int t = t0 + XL_PT * tg + u;
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + 16 * wave + 4 * r + g;
       if (t >= a.n) continue;
-      float *pp = a.pred + (uint64_t(kv) * HD * a.n) + (uint64_t(h) * a.n + t) * D + 8 * ig;
-      *(float4 *)pp = make_float4(float(acc[u][0]), float(acc[u][1]), float(acc[u][2]), float(acc[u][3]));
-      *(float4 *)(pp + 4) = make_float4(float(acc[u][4]), float(acc[u][5]), float(acc[u][6]), float(acc[u][7]));
+#pragma unroll
+      for (int it = 0; it < NI; ++it) pred[uint64_t(t) * D + 16 * it + m] = float(acc[it][r]);
     }
   }
 }
@@ -358,16 +395,22 @@ void launch_xl_predict(const XlArgs &a, int kv0, int n_kv, hipStream_t st) {
   // tiled kernels (fp32 LDS staging of the bf16 operands)
   const int TT = 4 * (256 / xl_project_groups(a.r));
   if (!a.skip_project) QKV_LAUNCH(k_xl_project, dim3(cdiv(a.n, TT), n_kv), dim3(256), 0, st, a, kv0);
-  const int RP = (a.r + 7) & ~7;
-  const int IG = a.D / 8, TTp = XL_PT * (256 / IG);
-  const size_t lds = size_t(a.D * a.D + RP * a.D + a.D * TTp + RP * TTp) * 2;
-  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_xl_predict),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-  // two blocks per CU fit (the staged weights); about 512 blocks in all,
-  // each walking every gx-th token tile of its (head, kv)
-  const int64_t n_tiles = cdiv(a.n, TTp);
+  const int RP = (a.r + 15) & ~15;
+  const size_t lds = size_t((a.D + XP_TT) * (a.D + 4) + (a.D + XP_TT) * (RP + 4)) * 2;
+  // two blocks per CU (staged weights + one token tile); at most 512 blocks
+  // in all, so that they run in one round, each walking every gx-th token
+  // tile of its (head, kv)
+  const int64_t n_tiles = cdiv(a.n, XP_TT);
   const int64_t hk = int64_t(a.H) * n_kv;
-  const unsigned gx = unsigned(std::max<int64_t>(1, std::min<int64_t>(n_tiles, (512 + hk - 1) / hk)));
-  QKV_LAUNCH(k_xl_predict, dim3(gx, a.H, n_kv), dim3(256), lds, st, a, kv0);
+  const unsigned gx = unsigned(std::max<int64_t>(1, std::min<int64_t>(n_tiles, 512 / hk)));
+  if (a.D == 64) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_xl_predict<64>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    QKV_LAUNCH(k_xl_predict<64>, dim3(gx, a.H, n_kv), dim3(256), lds, st, a, kv0);
+  } else {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_xl_predict<128>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    QKV_LAUNCH(k_xl_predict<128>, dim3(gx, a.H, n_kv), dim3(256), lds, st, a, kv0);
+  }
 }
 }  // namespace qkv
