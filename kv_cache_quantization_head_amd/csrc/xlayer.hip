@@ -13,87 +13,99 @@ namespace qkv {
 // fma(p, q, acc) equals acc + p*q rounded once: each output is exactly that
 // sequence of fp64 additions, however the work is tiled.
 
-// proj[t][k] = bf16(sum over m = 0 .. H*D-1 of y[t][m] V[m][k]).  Block = 256
-// threads = (token groups of 4) x (output groups of 8: 4 groups for r <= 32,
-// else 8), i.e. 256 or 128 tokens; the m axis is staged through LDS 32 at a
-// time (transposed, fp32; outputs past r read zero columns).
-constexpr int XL_MC = 32;
-__host__ __device__ constexpr int xl_project_groups(int r) { return r <= 32 ? 4 : 8; }
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_xl_project(XlArgs a, int kv0) {
-  __shared__ float ys[XL_MC][256 + 4];    // [m][token]
-  __shared__ float vs[XL_MC][64 + 4];     // [m][k]
-  const int KG = xl_project_groups(a.r), KP = 8 * KG, TG = 256 / KG, TT = 4 * TG;
-  const int tid = threadIdx.x, kv = kv0 + blockIdx.y;
-  const int kg = tid % KG, tg = tid / KG;
-  const int t0 = blockIdx.x * TT;
-  const uint64_t HD = uint64_t(a.H) * a.D;
-  const uint16_t *Vw = a.weights + uint64_t(kv) * a.kv_weight_stride + HD * a.D + HD * a.r;
+constexpr int XP_TT = 64;                    // tokens per tile
+__device__ __forceinline__ int xp_perm(int k) { return (k & ~15) | ((k & 3) << 2) | ((k >> 2) & 3); }
+__device__ __forceinline__ double xp_bf16(uint2 v, int s) {
+  const uint32_t w = (s & 2) ? v.y : v.x;
+  return double(__uint_as_float((s & 1) ? (w & 0xffff0000u) : (w << 16)));
+}
+typedef double xp_double4 __attribute__((ext_vector_type(4)));
+
+// proj[t][k] = bf16(sum over m = 0 .. H*D-1 of y[t][m] V[m][k]) on the fp64
+// matrix instruction, m ascending (see the prediction below for its order
+// and operand layouts; here m = token, n = output k, k-index = input m).
+// Block = 4 waves over 64 tokens (16 per wave, all r outputs: r/16
+// accumulator tiles); the m axis is staged through LDS 64 at a time (a chunk
+// lies inside one head), the next chunk's y and V loaded into registers
+// while the current one is multiplied.
+constexpr int XJ_MC = 64;                    // inputs m per chunk
+constexpr int XJ_TT = 64;                    // tokens per block
+template <int NT>   // accumulator tiles: outputs k < 16 NT (r <= 16 NT)
+__global__ __launch_bounds__(256, 2) void k_xl_project(XlArgs a, int kv0) {
+  constexpr int SP = XJ_MC + 4;              // LDS row stride (bf16)
+  constexpr int RP = 16 * NT;
+  __shared__ __attribute__((aligned(16))) uint16_t ys[XJ_TT * SP];  // [token][m'] (m permuted in runs of 16)
+  __shared__ __attribute__((aligned(16))) uint16_t vs[64 * SP];     // [k][m']
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, kv = kv0 + blockIdx.y;
+  const int ln = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * XJ_TT;
+  const int D = a.D;
+  const uint64_t HD = uint64_t(a.H) * D;
+  const uint16_t *Vw = a.weights + uint64_t(kv) * a.kv_weight_stride + HD * D + HD * a.r;
   const uint16_t *y = a.chain + uint64_t(kv) * HD * a.n;
-  double acc[4][8];
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[u][c] = 0.0;
-  // The next chunk's operands are loaded into registers while the current
-  // one is multiplied: y as 16-byte pieces (token, 8 channels), V as bf16.
-  constexpr int YP = XL_MC * 256 / 8 / 256;             // y pieces per thread (TT = 256)
-  constexpr int VP = XL_MC * 64 / 256;                  // V entries per thread (KP <= 64)
-  uint4 ypre[YP];
-  uint32_t vpre[VP];
+  constexpr int YPT = XJ_TT * XJ_MC / 8 / 256;   // 16-byte y pieces per thread
+  constexpr int VPT = XJ_MC * RP / 256;          // V values per thread
+  uint4 ypre[YPT];
+  uint16_t vpre[VPT];
   auto fetch = [&](uint64_t m0) {
-    const int hh = int(m0 / a.D), j0 = int(m0 % a.D);   // a chunk lies inside one head (D % 32 == 0)
+    const int hh = int(m0 / D), j0 = int(m0 % D);
 #pragma unroll
-    for (int i = 0; i < YP; ++i) {
-      const int e8 = tid + 256 * i, tt = e8 / (XL_MC / 8), j8 = 8 * (e8 % (XL_MC / 8));
+    for (int i = 0; i < YPT; ++i) {
+      const int e8 = tid + 256 * i, tt = e8 / (XJ_MC / 8), j8 = 8 * (e8 % (XJ_MC / 8));
       const int t = min(t0 + tt, a.n - 1);
-      if (tt < TT) ypre[i] = *(const uint4 *)(y + (uint64_t(hh) * a.n + t) * a.D + j0 + j8);
+      ypre[i] = *(const uint4 *)(y + (uint64_t(hh) * a.n + t) * D + j0 + j8);
     }
 #pragma unroll
-    for (int i = 0; i < VP; ++i) {
-      const int e = tid + 256 * i, jj = e / KP, kk = e % KP;
-      if (jj < XL_MC) vpre[i] = kk < a.r ? uint32_t(Vw[(m0 + jj) * a.r + kk]) : 0u;
+    for (int i = 0; i < VPT; ++i) {
+      const int e = tid + 256 * i, jj = e / RP, k = e % RP;
+      vpre[i] = k < a.r ? Vw[(m0 + jj) * a.r + k] : uint16_t(0);
     }
   };
+  xp_double4 acc[NT];
+#pragma unroll
+  for (int it = 0; it < NT; ++it) acc[it] = xp_double4{0.0, 0.0, 0.0, 0.0};
   fetch(0);
-  for (uint64_t m0 = 0; m0 < HD; m0 += XL_MC) {
-    __syncthreads();                                    // previous chunk consumed
+  for (uint64_t m0 = 0; m0 < HD; m0 += XJ_MC) {
+    __syncthreads();                         // previous chunk consumed
 #pragma unroll
-    for (int i = 0; i < YP; ++i) {
-      const int e8 = tid + 256 * i, tt = e8 / (XL_MC / 8), j8 = 8 * (e8 % (XL_MC / 8));
-      if (tt < TT) {
-        const uint32_t w[4] = {ypre[i].x, ypre[i].y, ypre[i].z, ypre[i].w};
+    for (int i = 0; i < YPT; ++i) {
+      const int e8 = tid + 256 * i, tt = e8 / (XJ_MC / 8), j8 = 8 * (e8 % (XJ_MC / 8));
+      const uint32_t v4[4] = {ypre[i].x, ypre[i].y, ypre[i].z, ypre[i].w};
 #pragma unroll
-        for (int q = 0; q < 8; ++q) ys[j8 + q][tt] = bf16_to_f32((w[q >> 1] >> (16 * (q & 1))) & 0xffffu);
-      }
+      for (int q = 0; q < 8; ++q) ys[tt * SP + xp_perm(j8 + q)] = uint16_t(v4[q >> 1] >> (16 * (q & 1)));
     }
 #pragma unroll
-    for (int i = 0; i < VP; ++i) {
-      const int e = tid + 256 * i, jj = e / KP, kk = e % KP;
-      if (jj < XL_MC) vs[jj][kk] = bf16_to_f32(vpre[i]);
+    for (int i = 0; i < VPT; ++i) {
+      const int e = tid + 256 * i, jj = e / RP, k = e % RP;
+      vs[k * SP + xp_perm(jj)] = vpre[i];
     }
     __syncthreads();
-    if (m0 + XL_MC < HD) fetch(m0 + XL_MC);
-#pragma unroll 4
-    for (int jj = 0; jj < XL_MC; ++jj) {
-      const float4 yv = *(const float4 *)&ys[jj][4 * tg];
-      const float4 v0 = *(const float4 *)&vs[jj][8 * kg], v1 = *(const float4 *)&vs[jj][8 * kg + 4];
-      const double yd[4] = {double(yv.x), double(yv.y), double(yv.z), double(yv.w)};
-      const double vd[8] = {double(v0.x), double(v0.y), double(v0.z), double(v0.w),
-                            double(v1.x), double(v1.y), double(v1.z), double(v1.w)};
+    if (m0 + XJ_MC < HD) fetch(m0 + XJ_MC);
+    const uint16_t *arow = ys + (16 * wave + ln) * SP + 4 * g;
+    const uint16_t *brow = vs + ln * SP + 4 * g;
+#pragma unroll 1
+    for (int q = 0; q < XJ_MC / 16; ++q) {
+      const uint2 av = *(const uint2 *)(arow + 16 * q);
+      uint2 bv[NT];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int it = 0; it < NT; ++it) bv[it] = *(const uint2 *)(brow + (16 * it) * SP + 16 * q);
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc[u][c] = fma(yd[u], vd[c], acc[u][c]);
+      for (int s = 0; s < 4; ++s) {
+        const double ad = xp_bf16(av, s);
+#pragma unroll
+        for (int it = 0; it < NT; ++it)
+          acc[it] = __builtin_amdgcn_mfma_f64_16x16x4f64(ad, xp_bf16(bv[it], s), acc[it], 0, 0, 0);
+      }
     }
   }
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int t = t0 + 4 * tg + u;
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + 16 * wave + 4 * i + g;
     if (t >= a.n) continue;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int kk = 8 * kg + c;
-      if (kk < a.r) a.proj[(uint64_t(kv) * a.n + t) * a.r + kk] = bf16_to_f32(f64_to_bf16_bits(acc[u][c]));
+    for (int it = 0; it < NT; ++it) {
+      const int k = 16 * it + ln;
+      if (k < a.r) a.proj[(uint64_t(kv) * a.n + t) * a.r + k] = bf16_to_f32(f64_to_bf16_bits(acc[it][i]));
     }
   }
 }
@@ -116,19 +128,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 // each run of 16 (k = 16 q + 4 s + g stored at 16 q + 4 g + s), so that the
 // lane of k-group g reads the values of four consecutive k-steps s in one
 // 8-byte load.
-constexpr int XP_TT = 64;                    // tokens per tile
-__device__ __forceinline__ int xp_perm(int k) { return (k & ~15) | ((k & 3) << 2) | ((k >> 2) & 3); }
-__device__ __forceinline__ double xp_bf16(uint2 v, int s) {
-  const uint32_t w = (s & 2) ? v.y : v.x;
-  return double(__uint_as_float((s & 1) ? (w & 0xffff0000u) : (w << 16)));
-}
-typedef double xp_double4 __attribute__((ext_vector_type(4)));
-
-template <int D>
+template <int D, int NT>   // NT: runs of 16 ranks (r <= 16 NT)
 __global__ __launch_bounds__(256, 2) void k_xl_predict(XlArgs a, int kv0) {
   constexpr int NI = D / 16, BP = D + 4;     // accumulator tiles; B / y row stride (bf16)
+  constexpr int RP = 16 * NT, UP = RP + 4;   // padded rank; U / w row stride (bf16)
   extern __shared__ uint16_t xs16[];
-  const int RP = (a.r + 15) & ~15, UP = RP + 4;
   uint16_t *Bs = xs16;                       // [D i][BP]: B_h[i][j] at xp_perm(j)
   uint16_t *Us = Bs + D * BP;                // [D i][UP]: U[h*D+i][k] at xp_perm(k), 0 past r
   uint16_t *Ys = Us + D * UP;                // [XP_TT t][BP]: y[t][j] at xp_perm(j)
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(256, 2) void k_xl_predict(XlArgs a, int kv0) {
   // the next tile's y rows and w values are loaded into registers while the
   // current tile is multiplied (16-byte pieces of y; w as bf16 bits)
   constexpr int YPT = XP_TT * D / 8 / 256;   // y pieces per thread
-  constexpr int WPT = XP_TT * 64 / 256;      // w values per thread (r <= 64)
+  constexpr int WPT = XP_TT * RP / 256;      // w values per thread
   uint4 ypre[YPT];
   uint16_t wpre[WPT];
   auto fetch = [&](int t0) {
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(256, 2) void k_xl_predict(XlArgs a, int kv0) {
     for (int i = 0; i < WPT; ++i) {
       const int e = tid + 256 * i, tt = e / RP, k = e % RP, t = min(t0 + tt, a.n - 1);
       // w holds bf16 values (rounded in the projection): exact in bf16
-      wpre[i] = e < XP_TT * RP && k < a.r ? f32_to_bf16_bits(w[uint64_t(t) * a.r + k]) : uint16_t(0);
+      wpre[i] = k < a.r ? f32_to_bf16_bits(w[uint64_t(t) * a.r + k]) : uint16_t(0);
     }
   };
   const int n_tiles = (a.n + XP_TT - 1) / XP_TT;
@@ -182,7 +186,7 @@ __global__ __launch_bounds__(256, 2) void k_xl_predict(XlArgs a, int kv0) {
 #pragma unroll
     for (int i = 0; i < WPT; ++i) {
       const int e = tid + 256 * i, tt = e / RP, k = e % RP;
-      if (e < XP_TT * RP) Ws[tt * UP + xp_perm(k)] = wpre[i];
+      Ws[tt * UP + xp_perm(k)] = wpre[i];
     }
     __syncthreads();
     if (tile + int(gridDim.x) < n_tiles) fetch((tile + gridDim.x) * XP_TT);
@@ -391,10 +395,20 @@ void launch_xl_refit(const RefitArgs &a, hipStream_t st) {
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
   QKV_LAUNCH(k_xl_solve, dim3(a.H, 2), dim3(256), lds, st, a);
 }
+template <int D, int NT>
+static void xl_predict_launch(const XlArgs &a, int kv0, const dim3 &grid, size_t lds, hipStream_t st) {
+  (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_xl_predict<D, NT>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  QKV_LAUNCH((k_xl_predict<D, NT>), grid, dim3(256), lds, st, a, kv0);
+}
 void launch_xl_predict(const XlArgs &a, int kv0, int n_kv, hipStream_t st) {
-  // tiled kernels (fp32 LDS staging of the bf16 operands)
-  const int TT = 4 * (256 / xl_project_groups(a.r));
-  if (!a.skip_project) QKV_LAUNCH(k_xl_project, dim3(cdiv(a.n, TT), n_kv), dim3(256), 0, st, a, kv0);
+  if (!a.skip_project) {
+    const dim3 grid(cdiv(a.n, XJ_TT), n_kv);
+    if (a.r <= 16) QKV_LAUNCH(k_xl_project<1>, grid, dim3(256), 0, st, a, kv0);
+    else if (a.r <= 32) QKV_LAUNCH(k_xl_project<2>, grid, dim3(256), 0, st, a, kv0);
+    else if (a.r <= 48) QKV_LAUNCH(k_xl_project<3>, grid, dim3(256), 0, st, a, kv0);
+    else QKV_LAUNCH(k_xl_project<4>, grid, dim3(256), 0, st, a, kv0);
+  }
   const int RP = (a.r + 15) & ~15;
   const size_t lds = size_t((a.D + XP_TT) * (a.D + 4) + (a.D + XP_TT) * (RP + 4)) * 2;
   // two blocks per CU (staged weights + one token tile); at most 512 blocks
@@ -403,14 +417,21 @@ void launch_xl_predict(const XlArgs &a, int kv0, int n_kv, hipStream_t st) {
   const int64_t n_tiles = cdiv(a.n, XP_TT);
   const int64_t hk = int64_t(a.H) * n_kv;
   const unsigned gx = unsigned(std::max<int64_t>(1, std::min<int64_t>(n_tiles, 512 / hk)));
+  const dim3 grid(gx, a.H, n_kv);
   if (a.D == 64) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_xl_predict<64>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    QKV_LAUNCH(k_xl_predict<64>, dim3(gx, a.H, n_kv), dim3(256), lds, st, a, kv0);
+    switch (RP / 16) {
+      case 1: xl_predict_launch<64, 1>(a, kv0, grid, lds, st); break;
+      case 2: xl_predict_launch<64, 2>(a, kv0, grid, lds, st); break;
+      case 3: xl_predict_launch<64, 3>(a, kv0, grid, lds, st); break;
+      default: xl_predict_launch<64, 4>(a, kv0, grid, lds, st); break;
+    }
   } else {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_xl_predict<128>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    QKV_LAUNCH(k_xl_predict<128>, dim3(gx, a.H, n_kv), dim3(256), lds, st, a, kv0);
+    switch (RP / 16) {
+      case 1: xl_predict_launch<128, 1>(a, kv0, grid, lds, st); break;
+      case 2: xl_predict_launch<128, 2>(a, kv0, grid, lds, st); break;
+      case 3: xl_predict_launch<128, 3>(a, kv0, grid, lds, st); break;
+      default: xl_predict_launch<128, 4>(a, kv0, grid, lds, st); break;
+    }
   }
 }
 }  // namespace qkv
