@@ -122,14 +122,13 @@ __global__ __launch_bounds__(256, 2) void k_xl_project(XlArgs a, int kv0) {
 // in lane m + 16 k, B[k][n] in lane n + 16 k, D[m][n] in lane n + 16 (m % 4),
 // register m / 4.  Here m = token, n = output channel, k = input channel j
 // (then rank k).  Block = 4 waves over a tile of 64 tokens, wave w taking
-// tokens 16 w .. 16 w + 15 and all D outputs (D/16 accumulator tiles).  B_h
-// and U_h are staged once per block and the block walks every gridDim.x-th
-// token tile.  In LDS every operand row keeps its k index permuted inside
+// tokens 16 w .. 16 w + 15 and all D outputs (D/16 accumulator tiles); a
+// block walks a consecutive range of (tensor, head, token tile) units.  In LDS every operand row keeps its k index permuted inside
 // each run of 16 (k = 16 q + 4 s + g stored at 16 q + 4 g + s), so that the
 // lane of k-group g reads the values of four consecutive k-steps s in one
 // 8-byte load.
 template <int D, int NT>   // NT: runs of 16 ranks (r <= 16 NT)
-__global__ __launch_bounds__(256, 2) void k_xl_predict(XlArgs a, int kv0) {
+__global__ __launch_bounds__(256, 2) void k_xl_predict(XlArgs a, int kv0, int n_kv) {
   constexpr int NI = D / 16, BP = D + 4;     // accumulator tiles; B / y row stride (bf16)
   constexpr int RP = 16 * NT, UP = RP + 4;   // padded rank; U / w row stride (bf16)
   extern __shared__ uint16_t xs16[];
@@ -139,26 +138,27 @@ __global__ __launch_bounds__(256, 2) void k_xl_predict(XlArgs a, int kv0) {
   uint16_t *Ws = Ys + XP_TT * BP;            // [XP_TT t][UP]: w[t][k] at xp_perm(k), 0 past r
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int m = lane & 15, g = lane >> 4;
-  const int h = blockIdx.y, kv = kv0 + blockIdx.z;
   const uint64_t HD = uint64_t(a.H) * D;
-  const uint16_t *W = a.weights + uint64_t(kv) * a.kv_weight_stride;
-  const uint16_t *B = a.b_weights ? a.b_weights + (uint64_t(kv) * a.H + h) * D * D : W + uint64_t(h) * D * D;
-  const uint16_t *U = W + HD * D + uint64_t(h) * D * a.r;
-  const uint16_t *y = a.chain + uint64_t(kv) * HD * a.n + uint64_t(h) * a.n * D;
-  const float *w = a.proj + uint64_t(kv) * a.n * a.r;
-  float *pred = a.pred + uint64_t(kv) * HD * a.n + uint64_t(h) * a.n * D;
-  for (int e = tid; e < D * D; e += 256) Bs[(e / D) * BP + xp_perm(e % D)] = B[e];
-  for (int e = tid; e < D * RP; e += 256) {
-    const int i = e / RP, k = e % RP;
-    Us[i * UP + xp_perm(k)] = k < a.r ? U[uint64_t(i) * a.r + k] : uint16_t(0);
-  }
-  // the next tile's y rows and w values are loaded into registers while the
-  // current tile is multiplied (16-byte pieces of y; w as bf16 bits)
+  // The (head, tensor, token tile) units, tensor-major then head, are split
+  // into equal consecutive ranges, one per block; B_h and U_h are staged
+  // again where a block's range moves to another head.
+  const int n_tiles = (a.n + XP_TT - 1) / XP_TT;
+  const int64_t n_units = int64_t(n_tiles) * a.H * n_kv;
+  const int64_t u0 = n_units * blockIdx.x / gridDim.x, u1 = n_units * (blockIdx.x + 1) / gridDim.x;
+  auto chain_of = [&](int hk) {              // hk = kv_rel * H + h
+    return a.chain + uint64_t(kv0 + hk / a.H) * HD * a.n + uint64_t(hk % a.H) * a.n * D;
+  };
+  auto proj_of = [&](int hk) { return a.proj + uint64_t(kv0 + hk / a.H) * a.n * a.r; };
+  // the next unit's y rows and w values are loaded into registers while the
+  // current one is multiplied (16-byte pieces of y; w as bf16 bits)
   constexpr int YPT = XP_TT * D / 8 / 256;   // y pieces per thread
   constexpr int WPT = XP_TT * RP / 256;      // w values per thread
   uint4 ypre[YPT];
   uint16_t wpre[WPT];
-  auto fetch = [&](int t0) {
+  auto fetch = [&](int64_t u) {
+    const int hk = int(u / n_tiles), t0 = int(u % n_tiles) * XP_TT;
+    const uint16_t *y = chain_of(hk);
+    const float *w = proj_of(hk);
 #pragma unroll
     for (int i = 0; i < YPT; ++i) {
       const int e8 = tid + 256 * i, tt = e8 / (D / 8), j8 = 8 * (e8 % (D / 8)), t = min(t0 + tt, a.n - 1);
@@ -171,11 +171,23 @@ __global__ __launch_bounds__(256, 2) void k_xl_predict(XlArgs a, int kv0) {
       wpre[i] = k < a.r ? f32_to_bf16_bits(w[uint64_t(t) * a.r + k]) : uint16_t(0);
     }
   };
-  const int n_tiles = (a.n + XP_TT - 1) / XP_TT;
-  if (blockIdx.x < n_tiles) fetch(blockIdx.x * XP_TT);
-  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    const int t0 = tile * XP_TT;
-    __syncthreads();                         // weights staged / previous tile consumed
+  int staged = -1;                           // head whose B_h and U_h are in LDS
+  if (u0 < u1) fetch(u0);
+  for (int64_t u = u0; u < u1; ++u) {
+    const int hk = int(u / n_tiles), t0 = int(u % n_tiles) * XP_TT;
+    __syncthreads();                         // previous unit consumed
+    if (hk != staged) {                      // block-uniform
+      const int kv = kv0 + hk / a.H, h = hk % a.H;
+      const uint16_t *W = a.weights + uint64_t(kv) * a.kv_weight_stride;
+      const uint16_t *B = a.b_weights ? a.b_weights + (uint64_t(kv) * a.H + h) * D * D : W + uint64_t(h) * D * D;
+      const uint16_t *U = W + HD * D + uint64_t(h) * D * a.r;
+      for (int e = tid; e < D * D; e += 256) Bs[(e / D) * BP + xp_perm(e % D)] = B[e];
+      for (int e = tid; e < D * RP; e += 256) {
+        const int i = e / RP, k = e % RP;
+        Us[i * UP + xp_perm(k)] = k < a.r ? U[uint64_t(i) * a.r + k] : uint16_t(0);
+      }
+      staged = hk;
+    }
 #pragma unroll
     for (int i = 0; i < YPT; ++i) {
       const int e8 = tid + 256 * i, tt = e8 / (D / 8), j8 = 8 * (e8 % (D / 8));
@@ -189,7 +201,8 @@ __global__ __launch_bounds__(256, 2) void k_xl_predict(XlArgs a, int kv0) {
       Ws[tt * UP + xp_perm(k)] = wpre[i];
     }
     __syncthreads();
-    if (tile + int(gridDim.x) < n_tiles) fetch((tile + gridDim.x) * XP_TT);
+    if (u + 1 < u1) fetch(u + 1);
+    float *pred = a.pred + uint64_t(kv0 + hk / a.H) * HD * a.n + uint64_t(hk % a.H) * a.n * D;
     xp_double4 acc[NI];
 #pragma unroll
     for (int it = 0; it < NI; ++it) acc[it] = xp_double4{0.0, 0.0, 0.0, 0.0};
@@ -396,10 +409,10 @@ void launch_xl_refit(const RefitArgs &a, hipStream_t st) {
   QKV_LAUNCH(k_xl_solve, dim3(a.H, 2), dim3(256), lds, st, a);
 }
 template <int D, int NT>
-static void xl_predict_launch(const XlArgs &a, int kv0, const dim3 &grid, size_t lds, hipStream_t st) {
+static void xl_predict_launch(const XlArgs &a, int kv0, int n_kv, const dim3 &grid, size_t lds, hipStream_t st) {
   (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_xl_predict<D, NT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-  QKV_LAUNCH((k_xl_predict<D, NT>), grid, dim3(256), lds, st, a, kv0);
+  QKV_LAUNCH((k_xl_predict<D, NT>), grid, dim3(256), lds, st, a, kv0, n_kv);
 }
 void launch_xl_predict(const XlArgs &a, int kv0, int n_kv, hipStream_t st) {
   if (!a.skip_project) {
@@ -414,23 +427,23 @@ void launch_xl_predict(const XlArgs &a, int kv0, int n_kv, hipStream_t st) {
   // two blocks per CU (staged weights + one token tile); at most 512 blocks
   // in all, so that they run in one round, each walking every gx-th token
   // tile of its (head, kv)
-  const int64_t n_tiles = cdiv(a.n, XP_TT);
-  const int64_t hk = int64_t(a.H) * n_kv;
-  const unsigned gx = unsigned(std::max<int64_t>(1, std::min<int64_t>(n_tiles, 512 / hk)));
-  const dim3 grid(gx, a.H, n_kv);
+  // two blocks per CU (staged weights + one token tile), at most 512 in all
+  // so that they run in one round
+  const int64_t n_units = cdiv(a.n, XP_TT) * int64_t(a.H) * n_kv;
+  const dim3 grid(unsigned(std::min<int64_t>(n_units, 512)));
   if (a.D == 64) {
     switch (RP / 16) {
-      case 1: xl_predict_launch<64, 1>(a, kv0, grid, lds, st); break;
-      case 2: xl_predict_launch<64, 2>(a, kv0, grid, lds, st); break;
-      case 3: xl_predict_launch<64, 3>(a, kv0, grid, lds, st); break;
-      default: xl_predict_launch<64, 4>(a, kv0, grid, lds, st); break;
+      case 1: xl_predict_launch<64, 1>(a, kv0, n_kv, grid, lds, st); break;
+      case 2: xl_predict_launch<64, 2>(a, kv0, n_kv, grid, lds, st); break;
+      case 3: xl_predict_launch<64, 3>(a, kv0, n_kv, grid, lds, st); break;
+      default: xl_predict_launch<64, 4>(a, kv0, n_kv, grid, lds, st); break;
     }
   } else {
     switch (RP / 16) {
-      case 1: xl_predict_launch<128, 1>(a, kv0, grid, lds, st); break;
-      case 2: xl_predict_launch<128, 2>(a, kv0, grid, lds, st); break;
-      case 3: xl_predict_launch<128, 3>(a, kv0, grid, lds, st); break;
-      default: xl_predict_launch<128, 4>(a, kv0, grid, lds, st); break;
+      case 1: xl_predict_launch<128, 1>(a, kv0, n_kv, grid, lds, st); break;
+      case 2: xl_predict_launch<128, 2>(a, kv0, n_kv, grid, lds, st); break;
+      case 3: xl_predict_launch<128, 3>(a, kv0, n_kv, grid, lds, st); break;
+      default: xl_predict_launch<128, 4>(a, kv0, n_kv, grid, lds, st); break;
     }
   }
 }
