@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqkv.so")
+SELFCHECK = os.path.join(HERE, "selfcheck_mfma_f64")
 ARCH = os.environ.get("QKV_OFFLOAD_ARCH", "gfx950")
 
 # -ffp-contract=off: the codec's fp32 arithmetic is specified operation by
@@ -75,6 +76,15 @@ def build(verbose=False):
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed linking libqkv.so")
     os.replace(tmp, LIB)
+    # the self-check of the fp64 matrix instruction's summation order (run by
+    # the GPU tests; the cross-layer kernels rely on it)
+    cmd = [hipcc()] + COMMON + ["-o", SELFCHECK, os.path.join(CSRC, "selfcheck_mfma_f64.hip")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building selfcheck_mfma_f64")
     return LIB
 
 
