@@ -172,6 +172,16 @@ def xlayer_main(args):
     kt = codec.trace_read()
     codec.trace(False)
     sweep_bytes = 2 * H * T * d * 2
+    # the prediction of layer 1's K and V in the read (one launch): per token,
+    # head and tensor d*(d + r) fp64 fmas, on the fp64 matrix instruction
+    xl_roofline = None
+    if "k_xl_predict" in kt and kt["k_xl_predict"][0]:
+        n_pred, tot_pred = kt["k_xl_predict"]
+        flops = 2.0 * 2 * H * T * d * (d + r)
+        tf = flops / (tot_pred / n_pred * 1e-3) / 1e12
+        xl_roofline = {"kernel": "k_xl_predict", "bound": "fp64 matrix", "achieved": round(tf, 2),
+                       "peak": 78.6, "unit": "TFLOP/s", "frac": round(tf / 78.6, 4),
+                       "flops_per_launch": flops, "launch_ms": round(tot_pred / n_pred, 4)}
 
     def layer1_error(c):
         err = []
@@ -193,6 +203,7 @@ def xlayer_main(args):
         "read_q_tokens": Tq,
         "read_layer0_ms": round(r0, 4), "read_layer1_ms": round(r1, 4),
         "read_kernels": {k: {"launches": n, "avg_ms": round(tot / max(n, 1), 4)} for k, (n, tot) in kt.items()},
+        "roofline": xl_roofline,
         "read_rolling_copy_bytes": sweep_bytes,
         "read_note": "layer 0: packed read + its reconstruction into the rolling bf16 copy; layer 1: "
                      "prediction from the copy (fp64), reconstruction over it, bf16 read"}), flush=True)
