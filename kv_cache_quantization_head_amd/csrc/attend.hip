@@ -28,13 +28,15 @@ namespace qkv {
 //    past the segment's end is rebuilt from the segment's last key (its
 //    logit is masked, so it weighs 0): the loads have no data-dependent
 //    path, and only a segment's last tile runs the masking code.
-//  * Loads are software-pipelined: ids of tile i+2 and the packed data
-//    (codes, scale/zero, centroid rows) of tile i+1 are in flight while tile
-//    i is rebuilt and multiplied; half of the waves multiply before they
-//    rebuild and half after, so that the MFMA work of one wave of a SIMD
-//    overlaps the VALU work of the other.  The chunk table is cached in LDS;
-//    each item follows its key's chunk with a cursor that only moves
-//    forward.
+//  * Loads are software-pipelined: ids of tile i+3 and the packed data
+//    (codes, scale/zero, centroid rows) of tile i+2 are in flight while tile
+//    i+1 is rebuilt and tile i multiplied.  The rebuild's arithmetic is
+//    spread between the S^T products of the wave's own tile: measured on
+//    the device, a wave's back-to-back products and the vector work of the
+//    other wave of its SIMD overlap little, vector instructions placed
+//    between a wave's own products largely do.  The chunk table is cached in
+//    LDS; each item follows its key's chunk with a cursor that only moves
+//    forward, the next chunk start and the chunk's codebook in registers.
 //  * The softmax scale is folded into the exponent's fma; the running max is
 //    only raised (and O, l rescaled) when a tile's max exceeds it by more
 //    than 8 (log2 units), so exponentials stay <= 256; row sums of P are
@@ -137,7 +139,7 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   // threads of one key read one centroid row.  K and V tiles are
   // both stored [key][d]; the PV step reads V with transposing LDS loads.
   const int it_kv = tid & 1, it_rem = tid >> 1;
-  const bool has_item = it_rem < 64 * NI;
+  const bool has_item = 2 * 64 * NI == 512 || it_rem < 64 * NI;   // every thread for D = 128
   const int it_key = it_rem / NI;
   const int it_ch = (it_rem % NI) * IC, it_g = it_ch / G;
   const uint8_t *st = it_kv ? a.stream_v : a.stream_k;
@@ -186,6 +188,7 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     u_end = min(TL * a.n_qblocks, u + U);
   }
   __syncthreads();  // chunk table in LDS
+  const int nch = nch_s;
   while (u < u_end) {
     int h, qblk, t0, t1, slot;
     if (!HB) {
@@ -220,7 +223,7 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
       // written after the previous segment's last tile barrier, read after
       // the barrier before this segment's first rebuild
       constexpr int MW = D / 32;
-      const int per = nch_s * MW;
+      const int per = nch * MW;
       for (int i = tid; i < 2 * per; i += blockDim.x) {
         const int kv = i / per, c = (i % per) / MW, w = i % MW;
         masks_s[kv][c * MW + w] = *(const uint32_t *)((kv ? a.stream_v : a.stream_k) + L.mask_off +
@@ -288,9 +291,12 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
       uint32_t codes[SMAX][KW];
       uint32_t meta[SMAX];
       uint4 cent[KC];
-    } R;
+    } R{};   // zero for threads without an item (rebuilt, never stored)
     // per-item pointers of the segment (key t = ks + AT_BK * tile + it_key)
-    const int t_first = ks + it_key;
+    // clamped like item_key, so that every key the item reads lies at or
+    // after t_first (the offsets below are unsigned): an item past the end of
+    // a segment shorter than a tile reads the segment's last key throughout
+    const int t_first = max(ks, min(ks + it_key, ke - 1));
     const uint8_t *code_p = FRESH ? nullptr : st + L.codes_off + uint64_t(h) * L.codes_head +
                                               uint64_t(t_first) * L.codes_token + it_ch * BITS / 8;
     const uint8_t *meta_p = FRESH ? nullptr : st + L.meta_off + uint64_t(h) * L.meta_head +
@@ -300,8 +306,12 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     const uint16_t *fresh_p = FRESH ? (it_kv ? a.v_new : a.k_new) + (uint64_t(h) * a.n_keys + t_first) * D + it_ch
                                     : nullptr;
     // chunk (snapshot slot) of the item's key, advanced tile by tile: keys
-    // only grow, and a tile's keys rarely cross more than one chunk start
-    int c_cur = (FRESH || nch_s == 1) ? 0 : chunk_of_lds(starts_s, nch_s, t_first);
+    // only grow, and a tile's keys rarely cross more than one chunk start.
+    // The next chunk's first token and the chunk's codebook are kept in
+    // registers, so a tile that stays in its chunk reads nothing from LDS.
+    int c_cur = (FRESH || nch == 1) ? 0 : chunk_of_lds(starts_s, nch, t_first);
+    int c_next = (FRESH || c_cur + 1 >= nch) ? INT_MAX : starts_s[c_cur + 1];
+    const uint8_t *cb_cur = FRESH ? nullptr : cb_p + uint64_t(c_cur) * L.cb_chunk;
     // packed data of the item's key: centroid slice, codes, (sigma, z)
     auto load_data = [&](int tile, uint32_t id_word) {
       if (!has_item || tile >= n_tiles) return;   // wave-uniform
@@ -319,13 +329,20 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
         for (int i = 0; i < KC; ++i) R.cent[i] = *(const uint4 *)(row + 8 * i);
         return;
       }
-      while (c_cur + 1 < nch_s && starts_s[c_cur + 1] <= t) ++c_cur;
+      while (t >= c_next) {
+        ++c_cur;
+        c_next = c_cur + 1 < nch ? starts_s[c_cur + 1] : INT_MAX;
+        cb_cur += L.cb_chunk;
+      }
       if constexpr (OUTL) R.fm = masks_s[it_kv][c_cur * (D / 32) + (it_ch >> 5)];
-      const uint8_t *crow = cb_p + uint64_t(c_cur) * L.cb_chunk + uint64_t(id_of(tile, id_word)) * (D * EB);
+      const uint8_t *crow = cb_cur + uint32_t(id_of(tile, id_word)) * uint32_t(D * EB);
   #pragma unroll
       for (int i = 0; i < KC; ++i) R.cent[i] = *(const uint4 *)(crow + 16 * i);
-      const uint8_t *cp = code_p + uint64_t(t - t_first) * L.codes_token;
-      const uint8_t *mp = meta_p + uint64_t(t - t_first) * L.meta_token;
+      // offsets inside one head's codes and (sigma, z) of a stage: below 2^32
+      // (the layout refuses larger heads)
+      const uint32_t dt = uint32_t(t - t_first);
+      const uint8_t *cp = code_p + dt * uint32_t(L.codes_token);
+      const uint8_t *mp = meta_p + dt * uint32_t(L.meta_token);
   #pragma unroll
       for (int s2 = 0; s2 < SMAX; ++s2) {
         if constexpr (KW == 2) {
@@ -377,43 +394,62 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     // sigma_1, c + (z_1 + ... + z_S))), then nearest-even bf16.  This differs
     // from the stage-by-stage reconstruction (c + rhat_1) + rhat_2 ... by a few
     // fp32 ulps, which changes the bf16 operand only for values within those
-    // ulps of a bf16 rounding boundary.
-    auto dequant_store = [&](int buf, int tile) {
+    // ulps of a bf16 rounding boundary.  Registers only (no memory access), so
+    // that it can share a basic block with the matrix products.
+    // The rebuild in steps, so that it can be spread between the S^T
+    // products of a tile: per half of the item (16 channels) one step for
+    // c + (z_1 + ... + z_S), one per stage, one that packs the half to bf16
+    // and stores it into LDS tile buf.
+    constexpr int RB_STEPS = FRESH ? 0 : 2 * (SMAX + 2);
+    // Spread between the products where the registers allow it (packed
+    // tiles, bf16 codebook, D = 128, no outlier fix-up, at most 3 INT4
+    // stages); else the whole rebuild runs before the tile's products, while
+    // no S^T accumulator is live (spreading it spilled registers there).
+    constexpr bool RB_SPREAD = !FRESH && D == 128 && CB_BF16 && !OUTL && (BITS == 2 || SMAX <= 3);
+    float xh[16];
+    float zs = 0.0f;
+    auto rebuild_step = [&](int c, int buf) {
+      if constexpr (!FRESH) {
+        const int half = c / (SMAX + 2), j = c % (SMAX + 2);
+        if (j == 0) {
+          if (half == 0) {
+            zs = 0.0f;
+  #pragma unroll
+            for (int s2 = 0; s2 < SMAX; ++s2) zs += f16_bits_to_f32(uint16_t(R.meta[s2] >> 16));
+          }
+  #pragma unroll
+          for (int e = 0; e < 16; ++e) xh[e] = cent_f32(16 * half + e) + zs;
+        } else if (j <= SMAX) {
+          stage16(&R.codes[j - 1][half * (BITS / 2)], f16_bits_to_f32(uint16_t(R.meta[j - 1] & 0xffffu)), xh);
+        } else if (has_item) {
+          uint16_t *dst = (it_kv ? &Vs[buf][it_key * VP + it_ch] : &Ks[buf][it_key * KP + it_ch]) + 16 * half;
+          *(uint4 *)(dst) = make_uint4(pack_bf16x2(xh[0], xh[1]), pack_bf16x2(xh[2], xh[3]),
+                                       pack_bf16x2(xh[4], xh[5]), pack_bf16x2(xh[6], xh[7]));
+          *(uint4 *)(dst + 8) = make_uint4(pack_bf16x2(xh[8], xh[9]), pack_bf16x2(xh[10], xh[11]),
+                                           pack_bf16x2(xh[12], xh[13]), pack_bf16x2(xh[14], xh[15]));
+        }
+      }
+    };
+    // Finish an item in LDS tile buf: the uncoded rows of a fresh tile are
+    // copied as read (four explicit stores: a copy loop kept the item in
+    // scratch); with the outlier option, the item's flagged channels (mask
+    // word of the key's chunk, the outlier group's (sigma, z), both loaded
+    // with the rest of the item's data) are rebuilt again with those and
+    // stored over the plain result, the channel's centroid value read back
+    // from the thread's copy of its slice in LDS.  A key past the segment's
+    // end carries the last key's data, like the plain rebuild.
+    auto finish_item = [&](int buf) {
       if (!has_item) return;
+      uint16_t *dst = it_kv ? &Vs[buf][it_key * VP + it_ch] : &Ks[buf][it_key * KP + it_ch];
       if constexpr (FRESH) {
-        uint16_t *dst = it_kv ? &Vs[buf][it_key * VP + it_ch] : &Ks[buf][it_key * KP + it_ch];
         static_assert(KC == 4, "a fresh item is 32 bf16 channels");
         const uint4 c0 = R.cent[0], c1 = R.cent[1], c2 = R.cent[2], c3 = R.cent[3];
         *(uint4 *)(dst) = c0;
         *(uint4 *)(dst + 8) = c1;
         *(uint4 *)(dst + 16) = c2;
         *(uint4 *)(dst + 24) = c3;
-        return;
       }
-      float xh[IC];
-      float zs = 0.0f;
-  #pragma unroll
-      for (int s2 = 0; s2 < SMAX; ++s2) zs += f16_bits_to_f32(uint16_t(R.meta[s2] >> 16));
-  #pragma unroll
-      for (int e = 0; e < IC; ++e) xh[e] = cent_f32(e) + zs;
-  #pragma unroll
-      for (int s2 = 0; s2 < SMAX; ++s2) {
-        const float sf = f16_bits_to_f32(uint16_t(R.meta[s2] & 0xffffu));
-  #pragma unroll
-        for (int b16 = 0; b16 < IC / 16; ++b16) stage16(&R.codes[s2][b16 * (BITS / 2)], sf, &xh[16 * b16]);
-      }
-      uint16_t *dst = it_kv ? &Vs[buf][it_key * VP + it_ch] : &Ks[buf][it_key * KP + it_ch];
-  #pragma unroll
-      for (int j = 0; j < IC; j += 8)
-        *(uint4 *)(dst + j) = make_uint4(pack_bf16x2(xh[j], xh[j + 1]), pack_bf16x2(xh[j + 2], xh[j + 3]),
-                                         pack_bf16x2(xh[j + 4], xh[j + 5]), pack_bf16x2(xh[j + 6], xh[j + 7]));
       if constexpr (OUTL) {
-        // channels of the item flagged in the mask of the key's chunk (the
-        // mask word and the outlier group's (sigma, z), loaded with the rest
-        // of the item's data): rebuilt again with those and stored over the
-        // first result (the channel's centroid value read back from the
-        // thread's copy of its slice in LDS).  A key past the segment's end
-        // carries the last key's data, like the plain rebuild.
         uint32_t fm = R.fm;
         if (fm) {
   #pragma unroll
@@ -445,6 +481,13 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
 
     // a tile that reaches past the segment's last key (its last tile only)
     auto partial_tile = [&](int tile) { return ks + (tile + 1) * AT_BK > ke; };
+    // One tile: S^T = K Q^T, the rebuild of the next tile (its registers are
+    // ready: loaded during the previous tile), the online softmax and O^T +=
+    // V^T P^T.  Each wave mixes its own vector work between its products:
+    // the rebuild's arithmetic between the S^T products, the exponentials
+    // beside the P V products.  On a segment's last tile the rebuild works on
+    // the last data loaded; its result lands in the idle buffer and is never
+    // read.
     auto compute_tile = [&](int tile) {
       const int buf = tile & 1;
       const int kt0 = ks + tile * AT_BK;
@@ -453,13 +496,29 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
   #pragma unroll
       for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
       const uint16_t *kp = &Ks[buf][c32 * KP + 8 * hh];
+      // k-step s issues its two products, then rebuild steps
+      // [RB_STEPS s / NS, RB_STEPS (s+1) / NS) of the next tile; the K
+      // fragments of step s+1 are loaded a step ahead.  Scheduling barriers
+      // keep this order (the compiler would otherwise issue the 16 products
+      // back to back).
+      bf16x8 k0 = *(const bf16x8 *)(kp), k1 = *(const bf16x8 *)(kp + 32 * KP);
   #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const bf16x8 k0 = *(const bf16x8 *)(kp + 16 * s);
-        const bf16x8 k1 = *(const bf16x8 *)(kp + 32 * KP + 16 * s);
+        bf16x8 n0, n1;
+        if (s + 1 < NS) {
+          n0 = *(const bf16x8 *)(kp + 16 * (s + 1));
+          n1 = *(const bf16x8 *)(kp + 32 * KP + 16 * (s + 1));
+        }
         s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], s1, 0, 0, 0);
+        if constexpr (RB_SPREAD) {
+  #pragma unroll
+          for (int c = RB_STEPS * s / NS; c < RB_STEPS * (s + 1) / NS; ++c) rebuild_step(c, buf ^ 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < NS) { k0 = n0; k1 = n1; }
       }
+      if constexpr (RB_SPREAD) finish_item(buf ^ 1);
       if (partial_tile(tile)) {
         // an empty volatile asm keeps this a branch taken on the last tile
         // only (speculated, its selects would run on every tile)
@@ -529,28 +588,28 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
         }
     };
 
-    // Pipeline: at iteration i every wave rebuilds tile i+1 from data loaded
-    // during iteration i-1 and issues the loads of tile i+2 (ids of tile i+3);
-    // one barrier per tile.  Two waves share each SIMD; half of the waves
-    // multiply tile i before rebuilding and half after, so one wave's MFMA work
-    // overlaps its partner's VALU work.  The split flips between waves w and
-    // w+4 and between waves 2k and 2k+1, whichever way waves sit on SIMDs.
-    const bool mfma_first = ((wave >> 2) ^ wave) & 1;
+    // Pipeline: at iteration i every wave multiplies tile i, rebuilds tile
+    // i+1 from the data loaded during iteration i-1 and issues the loads of
+    // tile i+2 (ids of tile i+3); one barrier per tile.
     __syncthreads();  // previous segment's tiles no longer read
     uint32_t id_next;   // id word of the item's key in tile+2
     load_data(0, load_id_word(0));
-    dequant_store(0, 0);
+  #pragma unroll
+    for (int c = 0; c < RB_STEPS; ++c) rebuild_step(c, 0);
+    finish_item(0);
     load_data(1, load_id_word(1));
     id_next = load_id_word(2);
     __syncthreads();
 
     for (int tile = 0; tile < n_tiles; ++tile) {
-      const int buf = tile & 1;
-      if (mfma_first) compute_tile(tile);
-      if (tile + 1 < n_tiles) dequant_store(buf ^ 1, tile + 1);   // data of tile+1 already in R
+      if constexpr (!RB_SPREAD) {
+  #pragma unroll
+        for (int c = 0; c < RB_STEPS; ++c) rebuild_step(c, (tile & 1) ^ 1);
+        finish_item((tile & 1) ^ 1);
+      }
+      compute_tile(tile);
       load_data(tile + 2, id_next);
       id_next = load_id_word(tile + 3);
-      if (!mfma_first) compute_tile(tile);
       __syncthreads();
     }
 

@@ -62,6 +62,9 @@ int make_plan(const qkv_config *cfg, Plan *plan) {
   s.meta_stage = H * s.meta_head;
   s.meta_off = off;
   off = align_up(off + S * s.meta_stage);
+  // the fused read addresses one head's codes and (sigma, z) of one stage
+  // with 32-bit offsets
+  if (s.codes_head >= (uint64_t(1) << 32) || s.meta_head >= (uint64_t(1) << 32)) return QKV_E_INVAL;
   s.id_bytes = C <= 256 ? 1 : 2;
   s.ids_head = T * s.id_bytes;
   s.ids_off = off;
