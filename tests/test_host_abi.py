@@ -286,3 +286,16 @@ def test_adapted_mode_layout_and_readback():
     rc, c = _init(plain, predictor=FAKE)
     assert L.qkv_adapted_blocks(c, 1, ctypes.byref(off1)) == B.QKV_E_INVAL
     L.qkv_destroy(c)
+
+
+def test_head_codes_addressable_with_32_bit_offsets():
+    # the fused read addresses one head's codes of one stage with 32-bit
+    # offsets: 2^26 tokens of INT4 codes at d = 128 (64 bytes per token) is
+    # the first size refused; one token fewer is accepted
+    T = 1 << 26
+    ok = _cfg(n_layers=1, n_heads=1, bits=4, max_tokens=T - 1, max_chunk_tokens=4680, max_query_tokens=0)
+    big = _cfg(n_layers=1, n_heads=1, bits=4, max_tokens=T, max_chunk_tokens=4680, max_query_tokens=0)
+    assert qkv.workspace_bytes(ok) > 0
+    assert qkv.workspace_bytes(big) == 0
+    rc, ctx = _init(big, nbytes=1, arena=1)
+    assert rc == B.QKV_E_INVAL and not ctx.value
