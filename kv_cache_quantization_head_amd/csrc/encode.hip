@@ -317,34 +317,61 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     uint32_t m1[2], m2[2], m3[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) m1[nt] = m2[nt] = m3[nt] = 0xffffffffu;
-    for (int k0 = 0; k0 < C16; k0 += 16) {
+    // The scores of a 16-cluster block are ranked while the products of the
+    // next block run: each wave mixes the ranking's vector work between its
+    // own products (measured on the device, a wave's back-to-back products
+    // and the vector work of other waves on its SIMD overlap little).
+    // Scheduling barriers keep the order.
+    auto rank4 = [&](const floatx4 *acc, int k0, int r) {
+      // with m1 <= m2 <= m3: new third = med3(m2, m3, key), new second =
+      // med3(m1, m2, key), new first = min(m1, key)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const uint32_t key = (__float_as_uint(acc[nt][r]) & ~0x1ffu) | uint32_t(k0 + g4 * 4 + r);
+        const uint32_t n3 = umed3(m2[nt], m3[nt], key);
+        const uint32_t n2 = umed3(m1[nt], m2[nt], key);
+        m1[nt] = min(m1[nt], key);
+        m2[nt] = n2;
+        m3[nt] = n3;
+      }
+    };
+    // products of block k0 into acc; between its k-steps, ranking steps
+    // [0, 4) of the previous block's scores (prev; none for the first block)
+    auto block = [&](int k0, floatx4 *acc, const floatx4 *prev) {
       bf16x8 ca[STEPS];
 #pragma unroll
       for (int step = 0; step < STEPS; ++step)
         ca[step] = *(const bf16x8 *)(cbs + (k0 + c16) * KP + step * 32 + g4 * 8);
       const float4 ch = *(const float4 *)(cnh + k0 + g4 * 4);
-      uint32_t kidx[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) kidx[r] = uint32_t(k0 + g4 * 4 + r);
+      if (prev) rank4(prev, k0 - 16, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        floatx4 acc = {ch.x + xnh[nt], ch.y + xnh[nt], ch.z + xnh[nt], ch.w + xnh[nt]};
-#pragma unroll
-        for (int step = 0; step < STEPS; ++step)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[step], xf[nt][step], acc, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          // with m1 <= m2 <= m3: new third = med3(m2, m3, key), new second =
-          // med3(m1, m2, key), new first = min(m1, key)
-          const uint32_t key = (__float_as_uint(acc[r]) & ~0x1ffu) | kidx[r];
-          const uint32_t n3 = umed3(m2[nt], m3[nt], key);
-          const uint32_t n2 = umed3(m1[nt], m2[nt], key);
-          m1[nt] = min(m1[nt], key);
-          m2[nt] = n2;
-          m3[nt] = n3;
-        }
+        acc[nt] = floatx4{ch.x + xnh[nt], ch.y + xnh[nt], ch.z + xnh[nt], ch.w + xnh[nt]};
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[0], xf[nt][0], acc[nt], 0, 0, 0);
       }
+#pragma unroll
+      for (int step = 1; step < STEPS; ++step) {
+        if (prev && step < 4) rank4(prev, k0 - 16, step);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ca[step], xf[nt][step], acc[nt], 0, 0, 0);
+      }
+      if (prev)
+#pragma unroll
+        for (int r = STEPS; r < 4; ++r) rank4(prev, k0 - 16, r);
+    };
+    floatx4 accp[2];
+    block(0, accp, nullptr);
+    for (int k0 = 16; k0 < C16; k0 += 16) {
+      floatx4 accn[2];
+      block(k0, accn, accp);
+      accp[0] = accn[0];
+      accp[1] = accn[1];
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rank4(accp, C16 - 16, r);
     // merge the sorted triples of the four lanes that share a token column
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
