@@ -601,15 +601,21 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     id_next = load_id_word(2);
     __syncthreads();
 
+    // Where the rebuild is not spread between the products, half of the
+    // waves multiply before they rebuild and half after (the split flips
+    // between waves w and w+4 and between waves 2k and 2k+1, whichever way
+    // waves sit on SIMDs).
+    const bool mfma_first = ((wave >> 2) ^ wave) & 1;
     for (int tile = 0; tile < n_tiles; ++tile) {
+      if (RB_SPREAD || mfma_first) compute_tile(tile);
       if constexpr (!RB_SPREAD) {
   #pragma unroll
         for (int c = 0; c < RB_STEPS; ++c) rebuild_step(c, (tile & 1) ^ 1);
         finish_item((tile & 1) ^ 1);
       }
-      compute_tile(tile);
       load_data(tile + 2, id_next);
       id_next = load_id_word(tile + 3);
+      if (!RB_SPREAD && !mfma_first) compute_tile(tile);
       __syncthreads();
     }
 
