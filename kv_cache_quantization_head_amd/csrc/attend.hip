@@ -394,12 +394,10 @@ __global__ __launch_bounds__(512, 1) void k_attend3(AttnArgs a) {
     // sigma_1, c + (z_1 + ... + z_S))), then nearest-even bf16.  This differs
     // from the stage-by-stage reconstruction (c + rhat_1) + rhat_2 ... by a few
     // fp32 ulps, which changes the bf16 operand only for values within those
-    // ulps of a bf16 rounding boundary.  Registers only (no memory access), so
-    // that it can share a basic block with the matrix products.
-    // The rebuild in steps, so that it can be spread between the S^T
-    // products of a tile: per half of the item (16 channels) one step for
-    // c + (z_1 + ... + z_S), one per stage, one that packs the half to bf16
-    // and stores it into LDS tile buf.
+    // ulps of a bf16 rounding boundary.  It runs in steps, so that it can be
+    // spread between the S^T products of a tile: per half of the item (16
+    // channels) one step for c + (z_1 + ... + z_S), one per stage, one that
+    // packs the half to bf16 and stores it into LDS tile buf.
     constexpr int RB_STEPS = FRESH ? 0 : 2 * (SMAX + 2);
     // Spread between the products where the registers allow it (packed
     // tiles, bf16 codebook, D = 128, no outlier fix-up, at most 3 INT4
