@@ -31,6 +31,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+# one fp32 vector operation per lane per clock: 256 CUs x 64 lanes x 2.4 GHz (the packed
+# two-operation fp32 instructions behind the 157.3 TFLOP/s figure are not used)
+ALU_PEAK_TOPS = 39.32
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 
 
@@ -744,6 +747,15 @@ def main():
                                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                                "launch_ms": round(t_att, 4), "launches": n_att, "flops_per_launch": att_flops}
     rooflines["quantize"] = hbm("quantize", quant_bytes, "k_quantize")
+    if rooflines["quantize"]:
+        # the quantizer's own arithmetic: per element the base subtraction and,
+        # per stage, the group's min and max search, subtract z, scale by 1/sigma,
+        # round, clamp, multiply-add back, subtract (separately rounded fp32)
+        ops = enc_tokens * d * (1 + 8 * S)
+        tops = ops / (rooflines["quantize"]["launch_ms"] * 1e-3) / 1e12
+        rooflines["quantize"]["alu"] = {"bound": "alu", "achieved": round(tops, 2), "peak": ALU_PEAK_TOPS,
+                                        "unit": "Top/s (fp32 vector operations)",
+                                        "frac": round(tops / ALU_PEAK_TOPS, 4), "ops_per_launch": ops}
     rooflines["reconstruct"] = hbm("reconstruct", recon_bytes, "k_reconstruct")
     rooflines["update"] = hbm("update", update_bytes, "k_update_sorted")
     t_as, n_as = kernel_ms("k_assign_mfma")
