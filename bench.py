@@ -702,6 +702,10 @@ def main():
     print(f"# timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
     ms = {n: _avg_ms(p) for n, p in ev.items()}
     ms_attend_call = _avg_ms(att_calls)
+    att_sorted = sorted(x.elapsed_time(y) for x, y in att_calls)
+
+    def pct(q):
+        return round(att_sorted[min(len(att_sorted) - 1, int(q * len(att_sorted)))], 4)
     ms_step = wall * 1e3 / args.steps
 
     # traced leg (not timed): per-kernel HIP events of two more steps
@@ -784,7 +788,9 @@ def main():
                                "into all layers, every layer reconstructed (bf16)",
                    "layers": L, "heads": H, "tokens": T, "head_dim": d, "clusters": C, "stages": S, "bits": b,
                    "group": G, "q_tokens": Tq, "chunk_tokens": n_call},
-        "calls_ms": {"attend_per_layer": round(ms_attend_call, 4), "attend_all_layers": round(ms["attend"], 4),
+        "calls_ms": {"attend_per_layer": round(ms_attend_call, 4),
+                     "attend_per_layer_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+                     "attend_all_layers": round(ms["attend"], 4),
                      "encode_chunk_all_layers": round(ms["encode"], 4),
                      "reconstruct_all_layers_k_and_v": round(ms["reconstruct"], 4),
                      "rewind": round(ms["rewind"], 4)},
