@@ -183,6 +183,22 @@ def test_encode_is_deterministic():
     assert torch.equal(arenas[0], arenas[1])
 
 
+def test_attend_is_deterministic():
+    # the split partials are merged in a fixed order and every key tile is
+    # walked in one order: repeated reads of one cache give the same bytes,
+    # with the query blocks split across blocks (1000 queries over 6000 keys
+    # of 4 heads) and without
+    cfgs = synth.scaled(synth.WAN_LAYER, n_heads=4, tokens=6000)
+    codec = make_codec(4, 128, 256, 2, 2, 32, max_tokens=6000, max_chunks=1, max_q=1000)
+    codec.encode_chunk(synth.kv_tokens(cfgs, 0, 0, 0, 6000).to(DEV), synth.kv_tokens(cfgs, 0, 1, 0, 6000).to(DEV))
+    for n_q in (1000, 64):
+        q = synth.queries(cfgs, 0, n_q).to(DEV)
+        runs = [codec.attend(0, q) for _ in range(3)]
+        torch.cuda.synchronize()
+        for out, lse in runs[1:]:
+            assert torch.equal(out, runs[0][0]) and torch.equal(lse, runs[0][1])
+
+
 def _near_tie_tokens(H, T, d, seed):
     """bf16-exact tokens built so that most are near-ties for the nearest
     centroid.  With no k-means iteration the codebook is the strided initial
